@@ -1,0 +1,269 @@
+/*
+ * pagedkv.h - C ABI of a paged KV-cache decode-attention library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed (the pages this library follows):
+ *
+ *  - Page "KV cache & continuous batching" (docs.masst.dev), section "The core
+ *    insight": a decode step computes the query of the new token only and
+ *    attends over the cached keys and values of every earlier token.  Section
+ *    "KV cache memory math": the cache holds K and V per layer, per KV head and
+ *    per token; grouped-query attention lets several query heads share one KV
+ *    head.  Section "Visual: the lifecycle of a request in continuous
+ *    batching": the cache is handed out in blocks of 16 tokens.  Section
+ *    "2. PagedAttention (vLLM)": each request has a block table mapping its
+ *    logical blocks to physical blocks that need not be contiguous, and the
+ *    attention kernel gathers K and V through that list of blocks.  Section
+ *    "5. Speculative decoding": the target model checks K drafted tokens in one
+ *    forward pass at length current + K.
+ *  - Page "LLM Serving - KV Cache, Batching, Speculative Decoding"
+ *    (dineshblog.com), section "KV memory, paging and prefix identity": logical
+ *    blocks map to physical blocks, which several sequences may share.
+ *  - Page "LLM Inference Optimization: KV Cache, Batching, and Speculative
+ *    Decoding" (adaptiverecall.com), section "Memory Bandwidth Optimization":
+ *    decode reads the entire cache for each new token, and storing the cache in
+ *    one byte per element halves those reads.
+ *
+ * Conventions shared by every call
+ *  - Device pointers ("dev_") point to memory the caller allocated on the GPU
+ *    the call runs on; host pointers ("host_") to ordinary host memory read
+ *    only during the call.  The library never allocates device memory.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    Work is enqueued asynchronously on it; order between calls is the
+ *    caller's, by using one stream.
+ *  - Every call returns a pkv_status: 0 on success, a negative code on error.
+ *    On an error nothing has been enqueued (except PKV_ERR_HIP, which reports
+ *    a failure of the HIP runtime while enqueuing).  No call throws.
+ *  - Handles (pkv_pool, pkv_table) are immutable after creation and hold
+ *    non-owning pointers; destroying a handle frees only the handle.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_BLOCK_SIZE 16
+#define PKV_ABI_VERSION 1
+
+typedef int32_t pkv_status;
+#define PKV_OK               0
+#define PKV_ERR_INVALID     (-1) /* null pointer, bad count or size, bad layer  */
+#define PKV_ERR_UNSUPPORTED (-2) /* dtype combination, head_dim, block size    */
+#define PKV_ERR_BLOCK_RANGE (-3) /* a used block-table entry outside the pool  */
+#define PKV_ERR_SEQ_LEN     (-4) /* seq_len < 1, > table capacity, or < rows   */
+#define PKV_ERR_WORKSPACE   (-5) /* device buffer or workspace too small       */
+#define PKV_ERR_HIP         (-6) /* the HIP runtime reported an error          */
+
+/* Element types. */
+#define PKV_F32      0  /* IEEE binary32                                        */
+#define PKV_BF16     1  /* bfloat16 (upper half of a binary32)                  */
+#define PKV_FP8_E4M3 2  /* OCP FP8 E4M3 ("e4m3fn": bias 7, max 448, NaN S.1111.111,
+                           no infinities) times a float32 scale per (layer, KV head) */
+
+/*
+ * Pool geometry.
+ *
+ * The pool is one caller-owned device buffer of kv_pool_bytes(desc) bytes,
+ * i.e. num_blocks * 16 token slots times the per-token size
+ * 2 * num_layers * num_kv_heads * head_dim * b (b = 4, 2, 1 bytes), which is
+ * the page-1 formula of section "KV cache memory math" applied to the pool's
+ * capacity.
+ *
+ * Byte layout.  The buffer is an array of tiles, one per
+ * (layer l, physical block p, KV head h, kv in {K = 0, V = 1}); tile
+ * (l, p, h, kv) starts at byte
+ *        ((((l * num_blocks + p) * num_kv_heads + h) * 2 + kv) * TILE,
+ *        TILE = 16 * head_dim * b.
+ * Inside a K tile, element (token offset o in [0,16), dim i) is element number
+ *        ((i / X) * 16 + o) * X + (i % X),   X = 16 / b,
+ * i.e. 16-byte chunks of X consecutive dims, chunk-major then token.  Inside a
+ * V tile, element (o, i) is element number  i * 16 + o  (V stored transposed).
+ * Token position t of a sequence with block table row `bt` lives at block
+ * bt[t / 16], offset t % 16; its flat slot is bt[t / 16] * 16 + t % 16.
+ * For PKV_FP8_E4M3 the stored code c of head h in layer l stands for the value
+ * decode(c) * scale[l][h], with separate K and V scale arrays.
+ */
+typedef struct pkv_pool_desc {
+    int32_t num_layers;    /* >= 1                                    */
+    int32_t num_blocks;    /* >= 1 physical blocks per layer          */
+    int32_t num_kv_heads;  /* >= 1                                    */
+    int32_t head_dim;      /* 64 or 128                               */
+    int32_t block_size;    /* must be PKV_BLOCK_SIZE (16)             */
+    int32_t kv_dtype;      /* PKV_F32, PKV_BF16 or PKV_FP8_E4M3       */
+} pkv_pool_desc;
+
+typedef struct pkv_pool pkv_pool;
+typedef struct pkv_table pkv_table;
+
+/* ABI version (PKV_ABI_VERSION of the built library). */
+int32_t pkv_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* pkv_status_string(pkv_status status);
+
+/*
+ * Bytes one token adds to the cache across all layers: 2 * L * H_kv * d * b
+ * (page "KV cache & continuous batching", section "KV cache memory math";
+ * page "LLM Serving - KV Cache, Batching, Speculative Decoding", section "KV
+ * memory, paging and prefix identity").  Returns -1 for invalid arguments.
+ */
+int64_t kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t kv_dtype);
+
+/* Bytes of the pool described by desc (layout above); -1 if desc is invalid. */
+int64_t kv_pool_bytes(const pkv_pool_desc* desc);
+
+/*
+ * Wrap a caller-allocated pool buffer in a handle.
+ *   dev_base   device buffer of at least kv_pool_bytes(desc) bytes, 256-byte aligned.
+ *   dev_k_scale, dev_v_scale  float32 [num_layers][num_kv_heads] device arrays;
+ *              required (non-NULL) for PKV_FP8_E4M3, ignored otherwise.
+ * Errors: PKV_ERR_INVALID (null, short or misaligned buffer, bad counts),
+ *         PKV_ERR_UNSUPPORTED (block_size != 16, head_dim not 64/128, dtype).
+ * The buffer contents are not touched.
+ */
+pkv_status kv_pool_create(const pkv_pool_desc* desc, void* dev_base, size_t dev_bytes,
+                          const float* dev_k_scale, const float* dev_v_scale,
+                          pkv_pool** out);
+pkv_status kv_pool_destroy(pkv_pool* pool);
+
+/*
+ * Device bytes block_table_upload needs for num_seqs sequences with
+ * max_blocks_per_seq table entries each, split into partition_tokens-token
+ * partitions (0 = one partition per sequence).  0 for invalid arguments.
+ */
+size_t block_table_device_bytes(int32_t num_seqs, int32_t max_blocks_per_seq,
+                                int32_t partition_tokens);
+
+/*
+ * Validate a batch of block tables, plan its split-KV partitions and copy
+ * both to the device (page "KV cache & continuous batching", section
+ * "2. PagedAttention (vLLM)": one table per request, logical block -> physical
+ * block).
+ *   host_block_table  int32 [num_seqs][max_blocks_per_seq], row-major.  Entry
+ *                     j of row s is used iff j < ceil(seq_len[s] / 16); every
+ *                     used entry must lie in [0, pool num_blocks).  Unused
+ *                     entries are ignored (any value).  Rows may share entries.
+ *   host_seq_lens     int32 [num_seqs]: positions visible to the last query row
+ *                     of each sequence, counting tokens appended this step;
+ *                     1 <= seq_len <= max_blocks_per_seq * 16.
+ *   partition_tokens  split-KV partition length, a multiple of 16 (0 = none).
+ *                     A sequence with more than one partition is attended as
+ *                     independent partitions whose partial results a second
+ *                     kernel merges.
+ *   dev_buffer        device buffer of >= block_table_device_bytes(...) bytes;
+ *                     it must stay valid and unmodified while the table is in use.
+ * The host arrays are copied into the handle before returning; the copy to
+ * dev_buffer is enqueued on `stream`.  Destroying the handle waits for that
+ * copy.  Errors: PKV_ERR_INVALID, PKV_ERR_BLOCK_RANGE, PKV_ERR_SEQ_LEN,
+ * PKV_ERR_WORKSPACE (dev_buffer too small), PKV_ERR_HIP.
+ */
+pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_table,
+                              int32_t num_seqs, int32_t max_blocks_per_seq,
+                              const int32_t* host_seq_lens, int32_t partition_tokens,
+                              void* dev_buffer, size_t dev_buffer_bytes, void* stream,
+                              pkv_table** out);
+pkv_status block_table_destroy(pkv_table* table);
+
+/*
+ * Facts of an uploaded table (any output pointer may be NULL):
+ * number of (sequence, partition) work units, partial-result slots of split
+ * sequences, and the longest and shortest sequence.
+ */
+pkv_status block_table_info(const pkv_table* table, int32_t* num_units,
+                            int32_t* num_split_slots, int32_t* max_seq_len,
+                            int32_t* min_seq_len);
+
+/*
+ * Slot of each (sequence, position) pair through the uploaded tables:
+ *   slot = table[seq][pos / 16] * 16 + pos % 16
+ * (page "KV cache & continuous batching", section "2. PagedAttention (vLLM)").
+ *   dev_seq_ids, dev_positions  int32 [num_tokens]; dev_slot_mapping int64 [num_tokens] out.
+ * A pair whose sequence is outside the batch, whose position is negative or
+ * beyond the row's capacity (max_blocks_per_seq * 16), or whose table entry is
+ * outside the pool gets slot -1.  num_tokens == 0 enqueues nothing.
+ */
+pkv_status slot_mapping_compute(const pkv_table* table, const int32_t* dev_seq_ids,
+                                const int32_t* dev_positions, int32_t num_tokens,
+                                int64_t* dev_slot_mapping, void* stream);
+
+/*
+ * Append new tokens' K and V to the pool through a slot mapping (the decode
+ * step extends the cache before attending: page "KV cache & continuous
+ * batching", section "The core insight"; page "LLM Serving - KV Cache,
+ * Batching, Speculative Decoding", section "Hands-on: cache equivalence and
+ * scheduling oracles").
+ *   dev_k_new, dev_v_new  [num_tokens][num_kv_heads][head_dim], element type in_dtype.
+ *   in_dtype     PKV_F32 for an F32 pool, PKV_BF16 for a BF16 pool, PKV_F32 or
+ *                PKV_BF16 for an FP8 pool.
+ *   dev_slot_mapping  int64 [num_tokens]; a slot outside [0, num_blocks * 16)
+ *                (e.g. -1) skips its token.  Two tokens with the same slot race.
+ * F32 and BF16 pools store the input bits unchanged.  FP8 pools store
+ *   e4m3( sat448( f32(x) * f32(1 / scale[layer][h]) ) )
+ * with round-to-nearest-even, saturation to +-448 and NaN kept NaN.
+ */
+pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, const void* dev_k_new,
+                             const void* dev_v_new, int32_t in_dtype,
+                             const int64_t* dev_slot_mapping, int32_t num_tokens,
+                             void* stream);
+
+/*
+ * Workspace bytes paged_attention_decode (query_rows = 1) or
+ * paged_attention_verify needs with this pool and table: the split-KV partial
+ * results (float32 output, max and sum per partition, query row and KV head).
+ * 0 when no sequence is split.  Returns 0 for invalid arguments as well.
+ */
+size_t paged_attention_workspace_bytes(const pkv_pool* pool, const pkv_table* table,
+                                       int32_t num_q_heads, int32_t query_rows);
+
+/*
+ * Decode attention, one query token per sequence:
+ *   out[s][g] = softmax( scale * q[s][g] . K_s[t][h]^T, t < seq_len[s] ) V_s[t][h],
+ *   h = g / (num_q_heads / num_kv_heads)          (grouped-query sharing)
+ * with K_s, V_s read from `layer` of the pool through the table's block list.
+ *   dev_q    [num_seqs][num_q_heads][head_dim], q_dtype.
+ *   dev_out  [num_seqs][num_q_heads][head_dim], out_dtype.
+ *   q_dtype  PKV_F32 with an F32 pool; PKV_BF16 with BF16 and FP8 pools.
+ *   out_dtype  PKV_F32 or PKV_BF16 (round to nearest even).
+ *   scale    softmax scale (typically 1/sqrt(head_dim)).
+ *   dev_workspace  >= paged_attention_workspace_bytes(pool, table, num_q_heads, 1)
+ *            bytes (may be NULL when that is 0); no initial contents needed.
+ * num_q_heads must be a multiple of num_kv_heads with at most 64 query heads
+ * per KV head.  Accumulation is float32; bf16/fp8 operands go through the
+ * matrix cores with float32 accumulation, probabilities rounded to bfloat16.
+ * Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_BLOCK_RANGE (the table's
+ * entries do not fit this pool), PKV_ERR_WORKSPACE, PKV_ERR_HIP.
+ */
+pkv_status paged_attention_decode(const pkv_pool* pool, int32_t layer, const pkv_table* table,
+                                  const void* dev_q, int32_t q_dtype, int32_t num_q_heads,
+                                  float scale, void* dev_workspace, size_t workspace_bytes,
+                                  void* dev_out, int32_t out_dtype, void* stream);
+
+/*
+ * Speculative verify attention, query_rows (= k) query tokens per sequence
+ * (page "KV cache & continuous batching", section "5. Speculative decoding";
+ * page "LLM Inference Optimization: KV Cache, Batching, and Speculative
+ * Decoding", section "Speculative Decoding").  The k rows of sequence s are
+ * positions n-k .. n-1 (n = seq_len[s]) whose K/V were appended beforehand;
+ * row j attends causally to positions t <= n - k + j.
+ *   dev_q, dev_out  [num_seqs][k][num_q_heads][head_dim].
+ * (query rows per KV head) = k * num_q_heads / num_kv_heads must be <= 64,
+ * and every seq_len >= k (else PKV_ERR_SEQ_LEN).  Otherwise as decode, which is
+ * this call with k = 1.
+ */
+pkv_status paged_attention_verify(const pkv_pool* pool, int32_t layer, const pkv_table* table,
+                                  const void* dev_q, int32_t q_dtype, int32_t query_rows,
+                                  int32_t num_q_heads, float scale, void* dev_workspace,
+                                  size_t workspace_bytes, void* dev_out, int32_t out_dtype,
+                                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,208 @@
+"""torch-facing wrappers with the C ABI's names.
+
+Each wrapper checks tensor shapes/dtypes/devices, takes raw pointers and the
+current HIP stream, and calls the library; a non-zero status raises
+``PagedKVError``.  Allocation of outputs and workspaces that the caller did
+not pass is done with torch (the library itself never allocates).
+"""
+
+import ctypes
+import math
+
+import numpy as np
+import torch
+
+from ._lib import BF16, BLOCK_SIZE, F32, FP8_E4M3, PagedKVError, PoolDesc, lib
+
+_KV_DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, F32: F32, BF16: BF16, FP8_E4M3: FP8_E4M3}
+_TORCH_CODE = {torch.float32: F32, torch.bfloat16: BF16}
+_CODE_TORCH = {F32: torch.float32, BF16: torch.bfloat16}
+
+
+def _check(call, status):
+    if status != 0:
+        raise PagedKVError(call, status)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _desc(num_layers, num_blocks, num_kv_heads, head_dim, kv_dtype):
+    return PoolDesc(int(num_layers), int(num_blocks), int(num_kv_heads), int(head_dim),
+                    BLOCK_SIZE, _KV_DTYPES[kv_dtype])
+
+
+def kv_bytes_per_token(num_layers, num_kv_heads, head_dim, kv_dtype):
+    """2 * L * H_kv * d * b (int); -1 if the arguments are invalid."""
+    return int(lib.kv_bytes_per_token(int(num_layers), int(num_kv_heads), int(head_dim),
+                                      _KV_DTYPES[kv_dtype]))
+
+
+def kv_pool_bytes(num_layers, num_blocks, num_kv_heads, head_dim, kv_dtype):
+    d = _desc(num_layers, num_blocks, num_kv_heads, head_dim, kv_dtype)
+    return int(lib.kv_pool_bytes(ctypes.byref(d)))
+
+
+class KVPool:
+    """A pool handle plus the tensors it points into (kept alive here)."""
+
+    def __init__(self, handle, storage, k_scale, v_scale, desc):
+        self._handle = handle
+        self.storage = storage
+        self.k_scale = k_scale
+        self.v_scale = v_scale
+        self.num_layers = desc.num_layers
+        self.num_blocks = desc.num_blocks
+        self.num_kv_heads = desc.num_kv_heads
+        self.head_dim = desc.head_dim
+        self.kv_dtype = desc.kv_dtype
+
+    @property
+    def handle(self):
+        return self._handle
+
+    def __del__(self):
+        h = getattr(self, "_handle", None)
+        if h:
+            lib.kv_pool_destroy(h)
+            self._handle = None
+
+
+def kv_pool_create(num_layers, num_blocks, num_kv_heads, head_dim, kv_dtype, storage=None,
+                   k_scale=None, v_scale=None, device="cuda"):
+    """Wrap (or allocate, when storage is None) a device pool buffer.
+
+    storage: uint8 CUDA tensor of at least kv_pool_bytes(...) bytes.
+    k_scale, v_scale: float32 CUDA tensors [num_layers][num_kv_heads] (fp8 only).
+    """
+    desc = _desc(num_layers, num_blocks, num_kv_heads, head_dim, kv_dtype)
+    nbytes = int(lib.kv_pool_bytes(ctypes.byref(desc)))
+    if nbytes < 0:
+        _check("kv_pool_bytes", -2)
+    if storage is None:
+        storage = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    assert storage.dtype == torch.uint8 and storage.is_cuda and storage.is_contiguous()
+    for s in (k_scale, v_scale):
+        if s is not None:
+            assert s.dtype == torch.float32 and s.is_cuda and s.is_contiguous()
+            assert s.numel() == num_layers * num_kv_heads
+    out = ctypes.c_void_p()
+    _check("kv_pool_create", lib.kv_pool_create(ctypes.byref(desc), _ptr(storage), storage.numel(),
+                                                _ptr(k_scale), _ptr(v_scale), ctypes.byref(out)))
+    return KVPool(out.value, storage, k_scale, v_scale, desc)
+
+
+class BlockTable:
+    """An uploaded, validated block table and its device buffer."""
+
+    def __init__(self, handle, buffer, num_seqs, max_blocks):
+        self._handle = handle
+        self.buffer = buffer
+        self.num_seqs = num_seqs
+        self.max_blocks = max_blocks
+
+    @property
+    def handle(self):
+        return self._handle
+
+    def info(self):
+        vals = [ctypes.c_int32() for _ in range(4)]
+        _check("block_table_info", lib.block_table_info(self._handle, *[ctypes.byref(v) for v in vals]))
+        keys = ("num_units", "num_split_slots", "max_seq_len", "min_seq_len")
+        return dict(zip(keys, (v.value for v in vals)))
+
+    def __del__(self):
+        h = getattr(self, "_handle", None)
+        if h:
+            lib.block_table_destroy(h)
+            self._handle = None
+
+
+def block_table_upload(pool, block_tables, seq_lens, partition_tokens=512, device="cuda"):
+    """Validate and upload host block tables ([B][max_blocks] int32) and lengths ([B])."""
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    assert bt.ndim == 2 and sl.ndim == 1 and sl.shape[0] == bt.shape[0]
+    B, mb = bt.shape
+    nbytes = int(lib.block_table_device_bytes(B, mb, int(partition_tokens)))
+    if nbytes == 0:
+        _check("block_table_device_bytes", -1)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    out = ctypes.c_void_p()
+    _check("block_table_upload", lib.block_table_upload(
+        pool.handle, bt.ctypes.data_as(ctypes.c_void_p), B, mb, sl.ctypes.data_as(ctypes.c_void_p),
+        int(partition_tokens), _ptr(buf), nbytes, _stream(buf.device), ctypes.byref(out)))
+    return BlockTable(out.value, buf, B, mb)
+
+
+def slot_mapping_compute(table, seq_ids, positions, out=None):
+    """int64 slots of (sequence, position) pairs; -1 where invalid."""
+    assert seq_ids.dtype == torch.int32 and positions.dtype == torch.int32
+    assert seq_ids.is_cuda and seq_ids.shape == positions.shape and seq_ids.dim() == 1
+    T = seq_ids.numel()
+    if out is None:
+        out = torch.empty(T, dtype=torch.int64, device=seq_ids.device)
+    assert out.dtype == torch.int64 and out.numel() == T
+    _check("slot_mapping_compute", lib.slot_mapping_compute(
+        table.handle, _ptr(seq_ids.contiguous()), _ptr(positions.contiguous()), T, _ptr(out),
+        _stream(seq_ids.device)))
+    return out
+
+
+def reshape_and_cache(pool, layer, k_new, v_new, slot_mapping):
+    """Write new tokens' K/V ([T][H_kv][d], float32 or bfloat16) at their slots."""
+    assert k_new.shape == v_new.shape and k_new.dtype == v_new.dtype
+    assert k_new.dim() == 3 and k_new.shape[1:] == (pool.num_kv_heads, pool.head_dim)
+    assert k_new.is_contiguous() and v_new.is_contiguous() and k_new.is_cuda
+    assert slot_mapping.dtype == torch.int64 and slot_mapping.numel() == k_new.shape[0]
+    _check("reshape_and_cache", lib.reshape_and_cache(
+        pool.handle, int(layer), _ptr(k_new), _ptr(v_new), _TORCH_CODE[k_new.dtype],
+        _ptr(slot_mapping.contiguous()), int(k_new.shape[0]), _stream(k_new.device)))
+
+
+def paged_attention_workspace_bytes(pool, table, num_q_heads, query_rows=1):
+    return int(lib.paged_attention_workspace_bytes(pool.handle, table.handle, int(num_q_heads),
+                                                   int(query_rows)))
+
+
+def _attention(pool, layer, table, q, query_rows, scale, workspace, out, out_dtype):
+    assert q.is_cuda and q.is_contiguous() and q.dtype in _TORCH_CODE
+    Hq = q.shape[-2]
+    if out_dtype is None:
+        out_dtype = torch.float32 if pool.kv_dtype == F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    assert out.shape == q.shape and out.is_contiguous() and out.dtype in _TORCH_CODE
+    need = paged_attention_workspace_bytes(pool, table, Hq, query_rows)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = 1.0 / math.sqrt(pool.head_dim)
+    return out, workspace, ws_bytes, float(scale), Hq
+
+
+def paged_attention_decode(pool, layer, table, q, scale=None, workspace=None, out=None, out_dtype=None):
+    """Decode attention: q [B][H_q][d] -> out [B][H_q][d]."""
+    assert q.dim() == 3 and q.shape[0] == table.num_seqs
+    out, workspace, ws_bytes, scale, Hq = _attention(pool, layer, table, q, 1, scale, workspace, out, out_dtype)
+    _check("paged_attention_decode", lib.paged_attention_decode(
+        pool.handle, int(layer), table.handle, _ptr(q), _TORCH_CODE[q.dtype], Hq, scale,
+        _ptr(workspace), ws_bytes, _ptr(out), _TORCH_CODE[out.dtype], _stream(q.device)))
+    return out
+
+
+def paged_attention_verify(pool, layer, table, q, scale=None, workspace=None, out=None, out_dtype=None):
+    """k-row verify attention: q [B][k][H_q][d] -> out [B][k][H_q][d]."""
+    assert q.dim() == 4 and q.shape[0] == table.num_seqs
+    k = q.shape[1]
+    out, workspace, ws_bytes, scale, Hq = _attention(pool, layer, table, q, k, scale, workspace, out, out_dtype)
+    _check("paged_attention_verify", lib.paged_attention_verify(
+        pool.handle, int(layer), table.handle, _ptr(q), _TORCH_CODE[q.dtype], int(k), Hq, scale,
+        _ptr(workspace), ws_bytes, _ptr(out), _TORCH_CODE[out.dtype], _stream(q.device)))
+    return out

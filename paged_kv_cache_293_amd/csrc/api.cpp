@@ -1,0 +1,402 @@
+// Host side of the C ABI declared in include/pagedkv.h: argument validation,
+// the pool and block-table handles, the split-KV plan and kernel launches.
+// Nothing here allocates device memory; every device buffer is the caller's.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/pagedkv.h"
+#include "pkv_internal.h"
+
+struct pkv_pool {
+    pkv_pool_desc desc;
+    uint8_t* base;
+    size_t bytes;
+    const float* k_scale;
+    const float* v_scale;
+    int64_t tile_bytes;
+};
+
+struct pkv_table {
+    int32_t num_seqs;
+    int32_t max_blocks;
+    int32_t partition_tokens;
+    int32_t part_blocks;
+    int32_t num_units;
+    int32_t num_split_slots;
+    int32_t max_seq_len;
+    int32_t min_seq_len;
+    int32_t max_block_id;
+    int32_t pool_blocks;            // block count of the pool validated against
+    int32_t* d_table;
+    int32_t* d_seq_lens;
+    int32_t* d_split_base;
+    int32_t* d_units;
+    std::vector<int32_t> staging;   // source of the asynchronous upload
+    hipEvent_t uploaded;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(int32_t dtype) {
+    switch (dtype) {
+        case PKV_F32: return 4;
+        case PKV_BF16: return 2;
+        case PKV_FP8_E4M3: return 1;
+        default: return 0;
+    }
+}
+
+pkv_status check_desc(const pkv_pool_desc* d) {
+    if (!d) return PKV_ERR_INVALID;
+    if (d->num_layers < 1 || d->num_blocks < 1 || d->num_kv_heads < 1) return PKV_ERR_INVALID;
+    if (d->block_size != PKV_BLOCK_SIZE) return PKV_ERR_UNSUPPORTED;
+    if (d->head_dim != 64 && d->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (elem_bytes(d->kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
+    return PKV_OK;
+}
+
+// Device sub-buffers of an uploaded table, in this order, each 256-byte aligned.
+struct TableLayout {
+    size_t table, seq_lens, split_base, units, total;
+    int64_t max_units;
+};
+
+bool table_layout(int32_t num_seqs, int32_t max_blocks, int32_t partition_tokens, TableLayout* L) {
+    if (num_seqs < 1 || max_blocks < 1 || partition_tokens < 0 || partition_tokens % PKV_BLOCK_SIZE)
+        return false;
+    const int64_t part_blocks = partition_tokens == 0 ? max_blocks : partition_tokens / PKV_BLOCK_SIZE;
+    const int64_t parts_per_seq = (max_blocks + part_blocks - 1) / part_blocks;
+    L->max_units = static_cast<int64_t>(num_seqs) * parts_per_seq;
+    size_t off = 0;
+    L->table = off;
+    off = align_up(off + sizeof(int32_t) * static_cast<size_t>(num_seqs) * max_blocks);
+    L->seq_lens = off;
+    off = align_up(off + sizeof(int32_t) * num_seqs);
+    L->split_base = off;
+    off = align_up(off + sizeof(int32_t) * num_seqs);
+    L->units = off;
+    off = align_up(off + sizeof(int32_t) * 2 * static_cast<size_t>(L->max_units));
+    L->total = off;
+    return true;
+}
+
+pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_status_string(pkv_status s) {
+    switch (s) {
+        case PKV_OK: return "ok";
+        case PKV_ERR_INVALID: return "invalid argument";
+        case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+        case PKV_ERR_BLOCK_RANGE: return "block-table entry outside the pool";
+        case PKV_ERR_SEQ_LEN: return "sequence length out of range";
+        case PKV_ERR_WORKSPACE: return "device buffer or workspace too small";
+        case PKV_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int64_t kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim, int32_t kv_dtype) {
+    const int b = elem_bytes(kv_dtype);
+    if (num_layers < 1 || num_kv_heads < 1 || head_dim < 1 || b == 0) return -1;
+    return 2LL * num_layers * num_kv_heads * head_dim * b;
+}
+
+int64_t kv_pool_bytes(const pkv_pool_desc* desc) {
+    if (check_desc(desc) != PKV_OK) return -1;
+    return static_cast<int64_t>(desc->num_blocks) * PKV_BLOCK_SIZE *
+           kv_bytes_per_token(desc->num_layers, desc->num_kv_heads, desc->head_dim, desc->kv_dtype);
+}
+
+pkv_status kv_pool_create(const pkv_pool_desc* desc, void* dev_base, size_t dev_bytes,
+                          const float* dev_k_scale, const float* dev_v_scale, pkv_pool** out) {
+    try {
+        if (!out) return PKV_ERR_INVALID;
+        *out = nullptr;
+        const pkv_status st = check_desc(desc);
+        if (st != PKV_OK) return st;
+        if (!dev_base || reinterpret_cast<uintptr_t>(dev_base) % kAlign) return PKV_ERR_INVALID;
+        if (dev_bytes < static_cast<size_t>(kv_pool_bytes(desc))) return PKV_ERR_INVALID;
+        if (desc->kv_dtype == PKV_FP8_E4M3 && (!dev_k_scale || !dev_v_scale)) return PKV_ERR_INVALID;
+        pkv_pool* p = new pkv_pool;
+        p->desc = *desc;
+        p->base = static_cast<uint8_t*>(dev_base);
+        p->bytes = dev_bytes;
+        p->k_scale = desc->kv_dtype == PKV_FP8_E4M3 ? dev_k_scale : nullptr;
+        p->v_scale = desc->kv_dtype == PKV_FP8_E4M3 ? dev_v_scale : nullptr;
+        p->tile_bytes = static_cast<int64_t>(PKV_BLOCK_SIZE) * desc->head_dim * elem_bytes(desc->kv_dtype);
+        *out = p;
+        return PKV_OK;
+    } catch (...) {
+        return PKV_ERR_INVALID;
+    }
+}
+
+pkv_status kv_pool_destroy(pkv_pool* pool) {
+    delete pool;
+    return PKV_OK;
+}
+
+size_t block_table_device_bytes(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t partition_tokens) {
+    TableLayout L;
+    if (!table_layout(num_seqs, max_blocks_per_seq, partition_tokens, &L)) return 0;
+    return L.total;
+}
+
+pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_table, int32_t num_seqs,
+                              int32_t max_blocks_per_seq, const int32_t* host_seq_lens,
+                              int32_t partition_tokens, void* dev_buffer, size_t dev_buffer_bytes,
+                              void* stream, pkv_table** out) {
+    try {
+        if (!out) return PKV_ERR_INVALID;
+        *out = nullptr;
+        if (!pool || !host_block_table || !host_seq_lens || !dev_buffer) return PKV_ERR_INVALID;
+        if (reinterpret_cast<uintptr_t>(dev_buffer) % kAlign) return PKV_ERR_INVALID;
+        TableLayout L;
+        if (!table_layout(num_seqs, max_blocks_per_seq, partition_tokens, &L)) return PKV_ERR_INVALID;
+        if (dev_buffer_bytes < L.total) return PKV_ERR_WORKSPACE;
+        const int32_t nb_pool = pool->desc.num_blocks;
+        const int64_t cap = static_cast<int64_t>(max_blocks_per_seq) * PKV_BLOCK_SIZE;
+        const int32_t part_blocks = partition_tokens == 0 ? max_blocks_per_seq : partition_tokens / PKV_BLOCK_SIZE;
+
+        int32_t max_len = 0, min_len = INT32_MAX, max_id = -1;
+        for (int32_t s = 0; s < num_seqs; ++s) {
+            const int32_t n = host_seq_lens[s];
+            if (n < 1 || n > cap) return PKV_ERR_SEQ_LEN;
+            max_len = std::max(max_len, n);
+            min_len = std::min(min_len, n);
+            const int32_t used = (n + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
+            const int32_t* row = host_block_table + static_cast<int64_t>(s) * max_blocks_per_seq;
+            for (int32_t j = 0; j < used; ++j) {
+                if (row[j] < 0 || row[j] >= nb_pool) return PKV_ERR_BLOCK_RANGE;
+                max_id = std::max(max_id, row[j]);
+            }
+        }
+
+        // Plan: every (sequence, partition) is a work unit; longest units first
+        // so the tail of the grid holds the short ones.  Split sequences get
+        // consecutive partial-result slots.
+        struct Unit { int32_t tokens, seq, part; };
+        std::vector<Unit> units;
+        units.reserve(static_cast<size_t>(L.max_units));
+        std::vector<int32_t> split_base(num_seqs, -1);
+        int32_t slots = 0;
+        const int64_t part_tokens = static_cast<int64_t>(part_blocks) * PKV_BLOCK_SIZE;
+        for (int32_t s = 0; s < num_seqs; ++s) {
+            const int32_t n = host_seq_lens[s];
+            const int32_t nblk = (n + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
+            const int32_t parts = (nblk + part_blocks - 1) / part_blocks;
+            if (parts > 1) {
+                split_base[s] = slots;
+                slots += parts;
+            }
+            for (int32_t p = 0; p < parts; ++p) {
+                const int64_t left = n - p * part_tokens;
+                units.push_back({static_cast<int32_t>(std::min<int64_t>(left, part_tokens)), s, p});
+            }
+        }
+        std::stable_sort(units.begin(), units.end(),
+                         [](const Unit& x, const Unit& y) { return x.tokens > y.tokens; });
+
+        pkv_table* t = new pkv_table;
+        t->num_seqs = num_seqs;
+        t->max_blocks = max_blocks_per_seq;
+        t->partition_tokens = partition_tokens;
+        t->part_blocks = part_blocks;
+        t->num_units = static_cast<int32_t>(units.size());
+        t->num_split_slots = slots;
+        t->max_seq_len = max_len;
+        t->min_seq_len = min_len;
+        t->max_block_id = max_id;
+        t->pool_blocks = nb_pool;
+        uint8_t* base = static_cast<uint8_t*>(dev_buffer);
+        t->d_table = reinterpret_cast<int32_t*>(base + L.table);
+        t->d_seq_lens = reinterpret_cast<int32_t*>(base + L.seq_lens);
+        t->d_split_base = reinterpret_cast<int32_t*>(base + L.split_base);
+        t->d_units = reinterpret_cast<int32_t*>(base + L.units);
+
+        t->staging.assign(L.total / sizeof(int32_t), 0);
+        int32_t* hs = t->staging.data();
+        std::memcpy(hs + L.table / 4, host_block_table,
+                    sizeof(int32_t) * static_cast<size_t>(num_seqs) * max_blocks_per_seq);
+        std::memcpy(hs + L.seq_lens / 4, host_seq_lens, sizeof(int32_t) * num_seqs);
+        std::memcpy(hs + L.split_base / 4, split_base.data(), sizeof(int32_t) * num_seqs);
+        for (size_t u = 0; u < units.size(); ++u) {
+            hs[L.units / 4 + 2 * u] = units[u].seq;
+            hs[L.units / 4 + 2 * u + 1] = units[u].part;
+        }
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        hipError_t e = hipEventCreateWithFlags(&t->uploaded, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            delete t;
+            return PKV_ERR_HIP;
+        }
+        e = hipMemcpyAsync(dev_buffer, hs, L.total, hipMemcpyHostToDevice, st);
+        if (e == hipSuccess) e = hipEventRecord(t->uploaded, st);
+        if (e != hipSuccess) {
+            (void)hipEventDestroy(t->uploaded);
+            delete t;
+            return PKV_ERR_HIP;
+        }
+        *out = t;
+        return PKV_OK;
+    } catch (...) {
+        return PKV_ERR_INVALID;
+    }
+}
+
+pkv_status block_table_destroy(pkv_table* table) {
+    if (!table) return PKV_OK;
+    pkv_status st = hip_status(hipEventSynchronize(table->uploaded));
+    (void)hipEventDestroy(table->uploaded);
+    delete table;
+    return st;
+}
+
+pkv_status block_table_info(const pkv_table* table, int32_t* num_units, int32_t* num_split_slots,
+                            int32_t* max_seq_len, int32_t* min_seq_len) {
+    if (!table) return PKV_ERR_INVALID;
+    if (num_units) *num_units = table->num_units;
+    if (num_split_slots) *num_split_slots = table->num_split_slots;
+    if (max_seq_len) *max_seq_len = table->max_seq_len;
+    if (min_seq_len) *min_seq_len = table->min_seq_len;
+    return PKV_OK;
+}
+
+pkv_status slot_mapping_compute(const pkv_table* table, const int32_t* dev_seq_ids, const int32_t* dev_positions,
+                                int32_t num_tokens, int64_t* dev_slot_mapping, void* stream) {
+    if (!table || num_tokens < 0) return PKV_ERR_INVALID;
+    if (num_tokens == 0) return PKV_OK;
+    if (!dev_seq_ids || !dev_positions || !dev_slot_mapping) return PKV_ERR_INVALID;
+    pkv::SlotArgs a;
+    a.block_table = table->d_table;
+    a.seq_ids = dev_seq_ids;
+    a.positions = dev_positions;
+    a.slots = dev_slot_mapping;
+    a.num_seqs = table->num_seqs;
+    a.max_blocks = table->max_blocks;
+    a.num_blocks = table->pool_blocks;
+    a.num_tokens = num_tokens;
+    return hip_status(pkv::launch_slot_mapping(a, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, const void* dev_k_new, const void* dev_v_new,
+                             int32_t in_dtype, const int64_t* dev_slot_mapping, int32_t num_tokens, void* stream) {
+    if (!pool || num_tokens < 0) return PKV_ERR_INVALID;
+    if (layer < 0 || layer >= pool->desc.num_layers) return PKV_ERR_INVALID;
+    const int32_t kv = pool->desc.kv_dtype;
+    const bool ok = (kv == PKV_F32 && in_dtype == PKV_F32) || (kv == PKV_BF16 && in_dtype == PKV_BF16) ||
+                    (kv == PKV_FP8_E4M3 && (in_dtype == PKV_F32 || in_dtype == PKV_BF16));
+    if (!ok) return PKV_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return PKV_OK;
+    if (!dev_k_new || !dev_v_new || !dev_slot_mapping) return PKV_ERR_INVALID;
+    pkv::CacheArgs a;
+    a.pool = pool->base;
+    a.k_scale = pool->k_scale;
+    a.v_scale = pool->v_scale;
+    a.k_new = dev_k_new;
+    a.v_new = dev_v_new;
+    a.slots = dev_slot_mapping;
+    a.tile_bytes = pool->tile_bytes;
+    a.num_slots = static_cast<int64_t>(pool->desc.num_blocks) * PKV_BLOCK_SIZE;
+    a.layer = layer;
+    a.num_blocks = pool->desc.num_blocks;
+    a.num_kv_heads = pool->desc.num_kv_heads;
+    a.head_dim = pool->desc.head_dim;
+    a.num_tokens = num_tokens;
+    return hip_status(pkv::launch_reshape_and_cache(a, kv, in_dtype, static_cast<hipStream_t>(stream)));
+}
+
+size_t paged_attention_workspace_bytes(const pkv_pool* pool, const pkv_table* table, int32_t num_q_heads,
+                                       int32_t query_rows) {
+    if (!pool || !table || num_q_heads < 1 || query_rows < 1) return 0;
+    const int32_t hkv = pool->desc.num_kv_heads;
+    if (num_q_heads % hkv) return 0;
+    const int64_t rows = static_cast<int64_t>(num_q_heads / hkv) * query_rows;
+    const int64_t entries = static_cast<int64_t>(hkv) * table->num_split_slots * rows;
+    if (entries == 0) return 0;
+    const size_t o_bytes = align_up(sizeof(float) * static_cast<size_t>(entries) * pool->desc.head_dim);
+    const size_t ml_bytes = align_up(sizeof(float) * static_cast<size_t>(entries));
+    return o_bytes + 2 * ml_bytes;
+}
+
+pkv_status paged_attention_verify(const pkv_pool* pool, int32_t layer, const pkv_table* table, const void* dev_q,
+                                  int32_t q_dtype, int32_t query_rows, int32_t num_q_heads, float scale,
+                                  void* dev_workspace, size_t workspace_bytes, void* dev_out, int32_t out_dtype,
+                                  void* stream) {
+    if (!pool || !table || !dev_q || !dev_out) return PKV_ERR_INVALID;
+    if (layer < 0 || layer >= pool->desc.num_layers) return PKV_ERR_INVALID;
+    if (query_rows < 1 || num_q_heads < 1) return PKV_ERR_INVALID;
+    if (!std::isfinite(scale)) return PKV_ERR_INVALID;
+    const int32_t hkv = pool->desc.num_kv_heads;
+    if (num_q_heads % hkv) return PKV_ERR_INVALID;
+    const int32_t group = num_q_heads / hkv;
+    if (static_cast<int64_t>(group) * query_rows > pkv::kMaxRows) return PKV_ERR_UNSUPPORTED;
+    const int32_t kv = pool->desc.kv_dtype;
+    const int32_t want_q = kv == PKV_F32 ? PKV_F32 : PKV_BF16;
+    if (q_dtype != want_q) return PKV_ERR_UNSUPPORTED;
+    if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (table->min_seq_len < query_rows) return PKV_ERR_SEQ_LEN;
+    if (table->max_block_id >= pool->desc.num_blocks) return PKV_ERR_BLOCK_RANGE;
+    const size_t need = paged_attention_workspace_bytes(pool, table, num_q_heads, query_rows);
+    if (need > 0 && (!dev_workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+    if (need > 0 && reinterpret_cast<uintptr_t>(dev_workspace) % kAlign) return PKV_ERR_INVALID;
+
+    pkv::AttnArgs a;
+    a.pool = pool->base;
+    a.k_scale = pool->k_scale;
+    a.v_scale = pool->v_scale;
+    a.block_table = table->d_table;
+    a.seq_lens = table->d_seq_lens;
+    a.units = table->d_units;
+    a.split_base = table->d_split_base;
+    a.q = dev_q;
+    a.out = dev_out;
+    const int64_t entries = static_cast<int64_t>(hkv) * table->num_split_slots * group * query_rows;
+    uint8_t* ws = static_cast<uint8_t*>(dev_workspace);
+    const size_t o_bytes = align_up(sizeof(float) * static_cast<size_t>(entries) * pool->desc.head_dim);
+    const size_t ml_bytes = align_up(sizeof(float) * static_cast<size_t>(entries));
+    a.part_o = need ? reinterpret_cast<float*>(ws) : nullptr;
+    a.part_m = need ? reinterpret_cast<float*>(ws + o_bytes) : nullptr;
+    a.part_l = need ? reinterpret_cast<float*>(ws + o_bytes + ml_bytes) : nullptr;
+    a.tile_bytes = pool->tile_bytes;
+    a.layer = layer;
+    a.num_blocks = pool->desc.num_blocks;
+    a.num_seqs = table->num_seqs;
+    a.num_kv_heads = hkv;
+    a.num_q_heads = num_q_heads;
+    a.group = group;
+    a.rows = group * query_rows;
+    a.k_rows = query_rows;
+    a.max_blocks = table->max_blocks;
+    a.part_blocks = table->part_blocks;
+    a.num_split_slots = table->num_split_slots;
+    a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
+    a.score_scale = scale * 1.4426950408889634f;
+    return hip_status(pkv::launch_attention(a, kv, pool->desc.head_dim, table->num_units,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+pkv_status paged_attention_decode(const pkv_pool* pool, int32_t layer, const pkv_table* table, const void* dev_q,
+                                  int32_t q_dtype, int32_t num_q_heads, float scale, void* dev_workspace,
+                                  size_t workspace_bytes, void* dev_out, int32_t out_dtype, void* stream) {
+    return paged_attention_verify(pool, layer, table, dev_q, q_dtype, 1, num_q_heads, scale, dev_workspace,
+                                  workspace_bytes, dev_out, out_dtype, stream);
+}
+
+}  // extern "C"
