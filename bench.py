@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Paged decode-attention benchmark on one MI355X.
+
+One step is the whole hot path over one batch: the slot mapping of each
+sequence's new token, the append of its K and V (reshape_and_cache), and paged
+decode attention over every sequence (partition kernel plus, for split
+sequences, the split-KV merge).  The default workload is the Llama-3-8B-shaped
+decode layer: 32 query / 8 KV heads, head_dim 128, bf16 KV, 16-token blocks,
+64 sequences with lengths uniform in [512, 4096], a seeded random block
+placement over a pool of 1.25x the blocks in use, N(0, 1) values.
+
+Inputs are resident in HBM before timing.  Steps rotate over several
+independently filled pools (default 3, ~0.8 GB each) so that no step finds the
+previous step's KV in the 256 MB Infinity Cache; the block tables, queries and
+new tokens are shared.
+
+Printed: one JSON line.  ``value`` is KV bytes attended per second over the
+whole step (GB/s = 1e9 B/s); ``seqs_per_s`` is sequences decoded per second;
+``roofline`` rates the attention call alone (algorithmic KV bytes / its
+average duration, measured with events on the stream it runs on) against the
+8 TB/s HBM peak; ``cpu_baseline`` is the float64 oracle on a bounded sample.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attention KV GB/s (% HBM peak) + seqs/s, Llama-3-8B GQA shapes"
+WORKLOAD_NAMES = {
+    "c2": "llama3-8b-decode-layer bf16 kv, 32q/8kv heads, d128, block16, batch64, ctx U[512,4096]",
+    "c3": "llama3-70b-decode-layer bf16 kv, 64q/8kv heads, d128, block16, batch256, ctx 179xU[128,1024]+77xU[4096,32768]",
+    "c4": "long-context split-kv bf16 kv, 32q/8kv heads, d128, block16, batch4, ctx 131072, 512-token partitions",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--partition", type=int, default=None, help="split-KV partition tokens")
+    ap.add_argument("--rotate", type=int, default=3, help="independent pools cycled through")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kv_bytes(w):
+    elem = {"f32": 4, "bf16": 2, "fp8": 1}[w.kv_dtype]
+    return int(w.seq_lens.astype("int64").sum()) * 2 * w.num_kv_heads * w.head_dim * elem
+
+
+def cpu_baseline(w, pool_image, budget_s):
+    """The float64 oracle, single-threaded, on as many sequences as fit the budget."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as oatt
+    from oracle import pool as opool
+
+    desc = opool.PoolDesc(w.num_layers, w.num_blocks, w.num_kv_heads, w.head_dim, w.kv_dtype)
+    q = opool.bf16_bits_to_float(w.q[:, 0]) if w.q_dtype == "bf16" else w.q[:, 0].astype(np.float64)
+    done, tokens = 0, 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for s in range(w.batch):
+            oatt.decode(desc, pool_image, w.layer, w.block_tables, w.seq_lens, q, w.scale,
+                        w.k_scale, w.v_scale, seqs=[s])
+            done += 1
+            tokens += int(w.seq_lens[s])
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+    elem = {"f32": 4, "bf16": 2, "fp8": 1}[w.kv_dtype]
+    nbytes = tokens * 2 * w.num_kv_heads * w.head_dim * elem
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seqs_per_s": round(done / dt, 3),
+            "sample": f"float64 numpy oracle decode of the first {done} of {w.batch} sequences "
+                      f"({tokens} tokens, {dt:.1f} s, one thread)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence or KV head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_293_amd as pk
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = workloads.make(args.workload, materialize=False)
+    P = w.partition_tokens if args.partition is None else args.partition
+
+    ks = vs = None
+    if w.kv_dtype == "fp8":
+        ks = torch.from_numpy(w.k_scale).to(dev)
+        vs = torch.from_numpy(w.v_scale).to(dev)
+    pools = []
+    for r in range(max(1, args.rotate)):
+        nbytes = pk.kv_pool_bytes(w.num_layers, w.num_blocks, w.num_kv_heads, w.head_dim, w.kv_dtype)
+        storage = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        workloads.fill_pool_random(storage, w.kv_dtype, w.seed + 7919 * r)
+        pools.append(pk.kv_pool_create(w.num_layers, w.num_blocks, w.num_kv_heads, w.head_dim,
+                                       w.kv_dtype, storage=storage, k_scale=ks, v_scale=vs))
+    table = pk.block_table_upload(pools[0], w.block_tables, w.seq_lens, P)
+
+    def dev_raw(x, dt):
+        if dt == "f32":
+            return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q = dev_raw(w.q[:, 0], w.q_dtype)
+    k_new = dev_raw(w.k_new, w.in_dtype)
+    v_new = dev_raw(w.v_new, w.in_dtype)
+    sid = torch.from_numpy(w.new_seq_ids).to(dev)
+    pos = torch.from_numpy(w.new_positions).to(dev)
+    slots = torch.empty(sid.numel(), dtype=torch.int64, device=dev)
+    out = torch.empty(q.shape, dtype=torch.bfloat16 if w.kv_dtype != "f32" else torch.float32, device=dev)
+    ws_bytes = pk.paged_attention_workspace_bytes(pools[0], table, w.num_q_heads, 1)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    scale = w.scale
+
+    K, W = args.steps, args.warmup
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+
+    def step(i, timed):
+        pool = pools[i % len(pools)]
+        pk.slot_mapping_compute(table, sid, pos, out=slots)
+        pk.reshape_and_cache(pool, w.layer, k_new, v_new, slots)
+        if timed:
+            ev[i][0].record()
+        pk.paged_attention_decode(pool, w.layer, table, q, scale, workspace=ws, out=out)
+        if timed:
+            ev[i][1].record()
+
+    for i in range(W):
+        step(i, False)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(K):
+        step(i, True)
+    t_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_stop)
+    ms_step = ms_total / K
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    attn_avg = sum(attn_ms) / len(attn_ms)
+
+    nbytes = kv_bytes(w)
+    value = nbytes / (ms_step * 1e-3) / 1e9
+    achieved = nbytes / (attn_avg * 1e-3) / 1e9
+    info = table.info()
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_digest") == _kernel_digest():
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype,
+        "data": "synthetic (seeded N(0,1) KV, random block placement)",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "batch": w.batch,
+                   "tokens": int(w.seq_lens.sum()), "partition_tokens": P,
+                   "pools_rotated": len(pools), "work_units": info["num_units"]},
+        "seqs_per_s": round(w.batch / (ms_step * 1e-3), 1),
+        "pct_hbm_peak_step": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "attention_ms": round(attn_avg, 5),
+        "attention_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 5),
+                                 round(float(np.percentile(attn_ms, 90)), 5)],
+        "kv_bytes_per_step": nbytes,
+        "wall_s": round(wall, 3),
+        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode (partition + split-KV merge)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        image = pools[0].storage.cpu().numpy()
+        result["cpu_baseline"] = cpu_baseline(w, image, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def _kernel_digest():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_293_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()
