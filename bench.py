@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_NAMES))
-    ap.add_argument("--partition", type=int, default=None, help="split-KV partition tokens")
+    ap.add_argument("--partition", type=int, default=-1, help="split-KV partition tokens (-1: balanced plan)")
     ap.add_argument("--rotate", type=int, default=3, help="independent pools cycled through")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -170,6 +170,8 @@ def main():
     achieved = nbytes / (attn_avg * 1e-3) / 1e9
     info = table.info()
 
+    kernel_label = ("attn_partition_kernel (split-KV merge inside)" if info["max_parts"] <= 32
+                    else "attn_partition_kernel + attn_merge_kernel")
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
     if os.path.exists(tpath):
@@ -201,7 +203,7 @@ def main():
                                  round(float(np.percentile(attn_ms, 90)), 5)],
         "kv_bytes_per_step": nbytes,
         "wall_s": round(wall, 3),
-        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode (partition + split-KV merge)",
+        "roofline": {"bound": "hbm", "kernel": kernel_label,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }

@@ -133,12 +133,13 @@ pkv_status kv_pool_create(const pkv_pool_desc* desc, void* dev_base, size_t dev_
 pkv_status kv_pool_destroy(pkv_pool* pool);
 
 /*
- * Device bytes block_table_upload needs for num_seqs sequences with
- * max_blocks_per_seq table entries each, split into partition_tokens-token
- * partitions (0 = one partition per sequence).  0 for invalid arguments.
+ * Device bytes block_table_upload needs for this batch: the tables, the
+ * lengths and the split-KV plan (which depends on the lengths, the pool's KV
+ * head count and, for partition_tokens = -1, the device's CU count).  Same
+ * arguments as block_table_upload.  0 for invalid arguments.
  */
-size_t block_table_device_bytes(int32_t num_seqs, int32_t max_blocks_per_seq,
-                                int32_t partition_tokens);
+size_t block_table_device_bytes(const pkv_pool* pool, const int32_t* host_seq_lens, int32_t num_seqs,
+                                int32_t max_blocks_per_seq, int32_t partition_tokens);
 
 /*
  * Validate a batch of block tables, plan its split-KV partitions and copy
@@ -152,15 +153,22 @@ size_t block_table_device_bytes(int32_t num_seqs, int32_t max_blocks_per_seq,
  *   host_seq_lens     int32 [num_seqs]: positions visible to the last query row
  *                     of each sequence, counting tokens appended this step;
  *                     1 <= seq_len <= max_blocks_per_seq * 16.
- *   partition_tokens  split-KV partition length, a multiple of 16 (0 = none).
- *                     A sequence with more than one partition is attended as
- *                     independent partitions whose partial results a second
- *                     kernel merges.
+ *   partition_tokens  split-KV plan: a positive multiple of 16 cuts every
+ *                     sequence into partitions of that many tokens (the last
+ *                     one shorter); 0 keeps each sequence whole; -1 cuts each
+ *                     sequence into near-equal partitions sized so the whole
+ *                     batch gives about one wave of work-groups on the device
+ *                     (balanced plan).  A split sequence's partitions are
+ *                     attended independently and their partial results
+ *                     merged (inside the attention kernel for up to 32
+ *                     partitions, by a second kernel beyond that).
  *   dev_buffer        device buffer of >= block_table_device_bytes(...) bytes;
  *                     it must stay valid and unmodified while the table is in use.
  * The host arrays are copied into the handle before returning; the copy to
  * dev_buffer is enqueued on `stream`.  Destroying the handle waits for that
- * copy.  Errors: PKV_ERR_INVALID, PKV_ERR_BLOCK_RANGE, PKV_ERR_SEQ_LEN,
+ * copy.  The buffer also holds the arrival counters of the in-kernel merge,
+ * which every attention call leaves at zero: attention calls that use one
+ * table must not overlap (issue them on one stream).  Errors: PKV_ERR_INVALID, PKV_ERR_BLOCK_RANGE, PKV_ERR_SEQ_LEN,
  * PKV_ERR_WORKSPACE (dev_buffer too small), PKV_ERR_HIP.
  */
 pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_table,
@@ -171,13 +179,13 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
 pkv_status block_table_destroy(pkv_table* table);
 
 /*
- * Facts of an uploaded table (any output pointer may be NULL):
- * number of (sequence, partition) work units, partial-result slots of split
- * sequences, and the longest and shortest sequence.
+ * Facts of an uploaded table (any output pointer may be NULL): number of
+ * (sequence, partition) work units, partial-result slots of split sequences,
+ * the longest and shortest sequence, and the most partitions of one sequence
+ * (above 32, attention calls launch the separate merge kernel).
  */
-pkv_status block_table_info(const pkv_table* table, int32_t* num_units,
-                            int32_t* num_split_slots, int32_t* max_seq_len,
-                            int32_t* min_seq_len);
+pkv_status block_table_info(const pkv_table* table, int32_t* num_units, int32_t* num_split_slots,
+                            int32_t* max_seq_len, int32_t* min_seq_len, int32_t* max_parts);
 
 /*
  * Slot of each (sequence, position) pair through the uploaded tables:

@@ -37,12 +37,13 @@ PROTOTYPES = {
     "kv_pool_bytes": (_c_int64, [ctypes.POINTER(PoolDesc)]),
     "kv_pool_create": (_c_int32, [ctypes.POINTER(PoolDesc), _vp, _c_size, _vp, _vp, ctypes.POINTER(_vp)]),
     "kv_pool_destroy": (_c_int32, [_vp]),
-    "block_table_device_bytes": (_c_size, [_c_int32, _c_int32, _c_int32]),
+    "block_table_device_bytes": (_c_size, [_vp, _vp, _c_int32, _c_int32, _c_int32]),
     "block_table_upload": (_c_int32, [_vp, _vp, _c_int32, _c_int32, _vp, _c_int32, _vp, _c_size, _vp,
                                       ctypes.POINTER(_vp)]),
     "block_table_destroy": (_c_int32, [_vp]),
     "block_table_info": (_c_int32, [_vp, ctypes.POINTER(_c_int32), ctypes.POINTER(_c_int32),
-                                    ctypes.POINTER(_c_int32), ctypes.POINTER(_c_int32)]),
+                                    ctypes.POINTER(_c_int32), ctypes.POINTER(_c_int32),
+                                    ctypes.POINTER(_c_int32)]),
     "slot_mapping_compute": (_c_int32, [_vp, _vp, _vp, _c_int32, _vp, _vp]),
     "reshape_and_cache": (_c_int32, [_vp, _c_int32, _vp, _vp, _c_int32, _vp, _c_int32, _vp]),
     "paged_attention_workspace_bytes": (_c_size, [_vp, _vp, _c_int32, _c_int32]),

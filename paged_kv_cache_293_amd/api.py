@@ -111,9 +111,9 @@ class BlockTable:
         return self._handle
 
     def info(self):
-        vals = [ctypes.c_int32() for _ in range(4)]
+        vals = [ctypes.c_int32() for _ in range(5)]
         _check("block_table_info", lib.block_table_info(self._handle, *[ctypes.byref(v) for v in vals]))
-        keys = ("num_units", "num_split_slots", "max_seq_len", "min_seq_len")
+        keys = ("num_units", "num_split_slots", "max_seq_len", "min_seq_len", "max_parts")
         return dict(zip(keys, (v.value for v in vals)))
 
     def __del__(self):
@@ -123,13 +123,18 @@ class BlockTable:
             self._handle = None
 
 
-def block_table_upload(pool, block_tables, seq_lens, partition_tokens=512, device="cuda"):
-    """Validate and upload host block tables ([B][max_blocks] int32) and lengths ([B])."""
+def block_table_upload(pool, block_tables, seq_lens, partition_tokens=-1, device="cuda"):
+    """Validate and upload host block tables ([B][max_blocks] int32) and lengths ([B]).
+
+    partition_tokens: a multiple of 16 for fixed split-KV partitions, 0 for
+    none, -1 (default) for the balanced plan.
+    """
     bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
     sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
     assert bt.ndim == 2 and sl.ndim == 1 and sl.shape[0] == bt.shape[0]
     B, mb = bt.shape
-    nbytes = int(lib.block_table_device_bytes(B, mb, int(partition_tokens)))
+    nbytes = int(lib.block_table_device_bytes(pool.handle, sl.ctypes.data_as(ctypes.c_void_p), B, mb,
+                                              int(partition_tokens)))
     if nbytes == 0:
         _check("block_table_device_bytes", -1)
     buf = torch.empty(nbytes, dtype=torch.uint8, device=device)

@@ -10,7 +10,7 @@
 #include <new>
 #include <vector>
 
-#include "../../include/pagedkv.h"
+#include "pagedkv.h"
 #include "pkv_internal.h"
 
 struct pkv_pool {
@@ -25,18 +25,22 @@ struct pkv_pool {
 struct pkv_table {
     int32_t num_seqs;
     int32_t max_blocks;
+    int32_t num_kv_heads;
     int32_t partition_tokens;
-    int32_t part_blocks;
     int32_t num_units;
+    int32_t unit_stride;
     int32_t num_split_slots;
+    int32_t max_parts;
     int32_t max_seq_len;
     int32_t min_seq_len;
     int32_t max_block_id;
     int32_t pool_blocks;            // block count of the pool validated against
     int32_t* d_table;
     int32_t* d_seq_lens;
-    int32_t* d_split_base;
+    int32_t* d_seq_parts;
+    int32_t* d_counters;
     int32_t* d_units;
+    int32_t* d_unit_ids;
     std::vector<int32_t> staging;   // source of the asynchronous upload
     hipEvent_t uploaded;
 };
@@ -65,29 +69,138 @@ pkv_status check_desc(const pkv_pool_desc* d) {
     return PKV_OK;
 }
 
-// Device sub-buffers of an uploaded table, in this order, each 256-byte aligned.
-struct TableLayout {
-    size_t table, seq_lens, split_base, units, total;
-    int64_t max_units;
+// Split-KV plan of one batch.  A work unit is one (sequence, partition); the
+// attention kernel runs one work-group per (unit, KV head).
+struct Plan {
+    int32_t num_units = 0;
+    int32_t stride = 0;          // block ids stored per unit
+    int32_t num_split_slots = 0; // partial-result slots (sequences with > 1 part)
+    int32_t max_parts = 0;
+    std::vector<int32_t> units;  // [U][kUnitInts]
+    std::vector<int32_t> seq_parts;  // [B][2] = (parts, first slot or -1)
 };
 
-bool table_layout(int32_t num_seqs, int32_t max_blocks, int32_t partition_tokens, TableLayout* L) {
-    if (num_seqs < 1 || max_blocks < 1 || partition_tokens < 0 || partition_tokens % PKV_BLOCK_SIZE)
-        return false;
-    const int64_t part_blocks = partition_tokens == 0 ? max_blocks : partition_tokens / PKV_BLOCK_SIZE;
-    const int64_t parts_per_seq = (max_blocks + part_blocks - 1) / part_blocks;
-    L->max_units = static_cast<int64_t>(num_seqs) * parts_per_seq;
-    size_t off = 0;
-    L->table = off;
-    off = align_up(off + sizeof(int32_t) * static_cast<size_t>(num_seqs) * max_blocks);
-    L->seq_lens = off;
-    off = align_up(off + sizeof(int32_t) * num_seqs);
-    L->split_base = off;
-    off = align_up(off + sizeof(int32_t) * num_seqs);
-    L->units = off;
-    off = align_up(off + sizeof(int32_t) * 2 * static_cast<size_t>(L->max_units));
-    L->total = off;
+// Device sub-buffers of an uploaded table, in this order, each 256-byte aligned.
+struct TableLayout {
+    size_t table, seq_lens, seq_parts, counters, units, unit_ids, total;
+};
+
+int device_cu_count() {
+    static int cached = 0;
+    if (cached == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cached = n;
+        else
+            cached = 256;
+    }
+    return cached;
+}
+
+// Blocks per unit for the balanced plan: the smallest unit size whose plan has
+// at most kAutoWgsPerCu work-groups per CU over all KV heads, kept within
+// [kAutoMinBlocks, kAutoMaxBlocks].
+int32_t auto_unit_blocks(const std::vector<int32_t>& nblk, int32_t num_kv_heads) {
+    const int64_t target_units = std::max<int64_t>(
+        1, static_cast<int64_t>(device_cu_count()) * pkv::kAutoWgsPerCu / std::max(1, num_kv_heads));
+    int32_t lo = pkv::kAutoMinBlocks, hi = pkv::kAutoMinBlocks;
+    for (int32_t b : nblk) hi = std::max(hi, b);
+    auto units_for = [&](int32_t T) {
+        int64_t u = 0;
+        for (int32_t b : nblk) u += (b + T - 1) / T;
+        return u;
+    };
+    if (units_for(lo) <= target_units) return lo;
+    while (lo < hi) {
+        const int32_t mid = lo + (hi - lo) / 2;
+        if (units_for(mid) <= target_units) hi = mid; else lo = mid + 1;
+    }
+    return std::min(hi, pkv::kAutoMaxBlocks);
+}
+
+// Build the plan.  partition_tokens > 0: fixed partitions of that many tokens
+// (the last one of a sequence shorter); 0: one partition per sequence; -1:
+// balanced, every sequence cut into near-equal parts of at most
+// auto_unit_blocks() blocks.  Units are ordered longest first.
+bool build_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, int32_t partition_tokens,
+                int32_t num_kv_heads, Plan* P) {
+    if (num_seqs < 1 || max_blocks < 1) return false;
+    if (partition_tokens < -1 || (partition_tokens > 0 && partition_tokens % PKV_BLOCK_SIZE)) return false;
+    std::vector<int32_t> nblk(num_seqs);
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t n = seq_lens[s];
+        if (n < 1 || static_cast<int64_t>(n) > static_cast<int64_t>(max_blocks) * PKV_BLOCK_SIZE) return false;
+        nblk[s] = (n + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
+    }
+    int32_t unit_blocks;
+    if (partition_tokens > 0) unit_blocks = partition_tokens / PKV_BLOCK_SIZE;
+    else if (partition_tokens == 0) unit_blocks = max_blocks;
+    else unit_blocks = auto_unit_blocks(nblk, num_kv_heads);
+
+    struct U { int32_t seq, b0, nb, part, parts; };
+    std::vector<U> us;
+    P->seq_parts.assign(2 * static_cast<size_t>(num_seqs), -1);
+    P->num_split_slots = 0;
+    P->max_parts = 0;
+    P->stride = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t parts = (nblk[s] + unit_blocks - 1) / unit_blocks;
+        P->seq_parts[2 * s] = parts;
+        if (parts > 1) {
+            P->seq_parts[2 * s + 1] = P->num_split_slots;
+            P->num_split_slots += parts;
+        }
+        P->max_parts = std::max(P->max_parts, parts);
+        for (int32_t p = 0; p < parts; ++p) {
+            int32_t b0, nb;
+            if (partition_tokens == -1) {      // near-equal parts
+                const int32_t q = nblk[s] / parts, r = nblk[s] % parts;
+                b0 = p * q + std::min(p, r);
+                nb = q + (p < r ? 1 : 0);
+            } else {
+                b0 = p * unit_blocks;
+                nb = std::min(unit_blocks, nblk[s] - b0);
+            }
+            us.push_back({s, b0, nb, p, parts});
+            P->stride = std::max(P->stride, nb);
+        }
+    }
+    std::stable_sort(us.begin(), us.end(), [](const U& x, const U& y) { return x.nb > y.nb; });
+    P->num_units = static_cast<int32_t>(us.size());
+    P->units.assign(static_cast<size_t>(P->num_units) * pkv::kUnitInts, 0);
+    for (size_t i = 0; i < us.size(); ++i) {
+        int32_t* d = &P->units[i * pkv::kUnitInts];
+        const U& u = us[i];
+        d[pkv::kUnitSeq] = u.seq;
+        d[pkv::kUnitB0] = u.b0;
+        d[pkv::kUnitNb] = u.nb;
+        d[pkv::kUnitLen] = seq_lens[u.seq];
+        d[pkv::kUnitPart] = u.part;
+        d[pkv::kUnitParts] = u.parts;
+        d[pkv::kUnitSlot] = u.parts > 1 ? P->seq_parts[2 * u.seq + 1] + u.part : -1;
+        d[pkv::kUnitRot] = u.seq % u.nb;   // sequences sharing blocks start their walk apart
+    }
     return true;
+}
+
+TableLayout table_layout(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads, const Plan& P) {
+    TableLayout L;
+    size_t off = 0;
+    L.table = off;
+    off = align_up(off + sizeof(int32_t) * static_cast<size_t>(num_seqs) * max_blocks);
+    L.seq_lens = off;
+    off = align_up(off + sizeof(int32_t) * num_seqs);
+    L.seq_parts = off;
+    off = align_up(off + sizeof(int32_t) * 2 * num_seqs);
+    L.counters = off;
+    off = align_up(off + sizeof(int32_t) * static_cast<size_t>(num_seqs) * num_kv_heads);
+    L.units = off;
+    off = align_up(off + sizeof(int32_t) * pkv::kUnitInts * static_cast<size_t>(P.num_units));
+    L.unit_ids = off;
+    off = align_up(off + sizeof(int32_t) * static_cast<size_t>(P.num_units) * P.stride);
+    L.total = off;
+    return L;
 }
 
 pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
@@ -152,10 +265,17 @@ pkv_status kv_pool_destroy(pkv_pool* pool) {
     return PKV_OK;
 }
 
-size_t block_table_device_bytes(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t partition_tokens) {
-    TableLayout L;
-    if (!table_layout(num_seqs, max_blocks_per_seq, partition_tokens, &L)) return 0;
-    return L.total;
+size_t block_table_device_bytes(const pkv_pool* pool, const int32_t* host_seq_lens, int32_t num_seqs,
+                                int32_t max_blocks_per_seq, int32_t partition_tokens) {
+    try {
+        if (!pool || !host_seq_lens) return 0;
+        Plan P;
+        if (!build_plan(host_seq_lens, num_seqs, max_blocks_per_seq, partition_tokens, pool->desc.num_kv_heads, &P))
+            return 0;
+        return table_layout(num_seqs, max_blocks_per_seq, pool->desc.num_kv_heads, P).total;
+    } catch (...) {
+        return 0;
+    }
 }
 
 pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_table, int32_t num_seqs,
@@ -167,12 +287,12 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
         *out = nullptr;
         if (!pool || !host_block_table || !host_seq_lens || !dev_buffer) return PKV_ERR_INVALID;
         if (reinterpret_cast<uintptr_t>(dev_buffer) % kAlign) return PKV_ERR_INVALID;
-        TableLayout L;
-        if (!table_layout(num_seqs, max_blocks_per_seq, partition_tokens, &L)) return PKV_ERR_INVALID;
-        if (dev_buffer_bytes < L.total) return PKV_ERR_WORKSPACE;
+        if (num_seqs < 1 || max_blocks_per_seq < 1) return PKV_ERR_INVALID;
+        if (partition_tokens < -1 || (partition_tokens > 0 && partition_tokens % PKV_BLOCK_SIZE))
+            return PKV_ERR_INVALID;
         const int32_t nb_pool = pool->desc.num_blocks;
+        const int32_t hkv = pool->desc.num_kv_heads;
         const int64_t cap = static_cast<int64_t>(max_blocks_per_seq) * PKV_BLOCK_SIZE;
-        const int32_t part_blocks = partition_tokens == 0 ? max_blocks_per_seq : partition_tokens / PKV_BLOCK_SIZE;
 
         int32_t max_len = 0, min_len = INT32_MAX, max_id = -1;
         for (int32_t s = 0; s < num_seqs; ++s) {
@@ -187,39 +307,21 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
                 max_id = std::max(max_id, row[j]);
             }
         }
-
-        // Plan: every (sequence, partition) is a work unit; longest units first
-        // so the tail of the grid holds the short ones.  Split sequences get
-        // consecutive partial-result slots.
-        struct Unit { int32_t tokens, seq, part; };
-        std::vector<Unit> units;
-        units.reserve(static_cast<size_t>(L.max_units));
-        std::vector<int32_t> split_base(num_seqs, -1);
-        int32_t slots = 0;
-        const int64_t part_tokens = static_cast<int64_t>(part_blocks) * PKV_BLOCK_SIZE;
-        for (int32_t s = 0; s < num_seqs; ++s) {
-            const int32_t n = host_seq_lens[s];
-            const int32_t nblk = (n + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
-            const int32_t parts = (nblk + part_blocks - 1) / part_blocks;
-            if (parts > 1) {
-                split_base[s] = slots;
-                slots += parts;
-            }
-            for (int32_t p = 0; p < parts; ++p) {
-                const int64_t left = n - p * part_tokens;
-                units.push_back({static_cast<int32_t>(std::min<int64_t>(left, part_tokens)), s, p});
-            }
-        }
-        std::stable_sort(units.begin(), units.end(),
-                         [](const Unit& x, const Unit& y) { return x.tokens > y.tokens; });
+        Plan P;
+        if (!build_plan(host_seq_lens, num_seqs, max_blocks_per_seq, partition_tokens, hkv, &P))
+            return PKV_ERR_INVALID;
+        const TableLayout L = table_layout(num_seqs, max_blocks_per_seq, hkv, P);
+        if (dev_buffer_bytes < L.total) return PKV_ERR_WORKSPACE;
 
         pkv_table* t = new pkv_table;
         t->num_seqs = num_seqs;
         t->max_blocks = max_blocks_per_seq;
+        t->num_kv_heads = hkv;
         t->partition_tokens = partition_tokens;
-        t->part_blocks = part_blocks;
-        t->num_units = static_cast<int32_t>(units.size());
-        t->num_split_slots = slots;
+        t->num_units = P.num_units;
+        t->unit_stride = P.stride;
+        t->num_split_slots = P.num_split_slots;
+        t->max_parts = P.max_parts;
         t->max_seq_len = max_len;
         t->min_seq_len = min_len;
         t->max_block_id = max_id;
@@ -227,18 +329,30 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
         uint8_t* base = static_cast<uint8_t*>(dev_buffer);
         t->d_table = reinterpret_cast<int32_t*>(base + L.table);
         t->d_seq_lens = reinterpret_cast<int32_t*>(base + L.seq_lens);
-        t->d_split_base = reinterpret_cast<int32_t*>(base + L.split_base);
+        t->d_seq_parts = reinterpret_cast<int32_t*>(base + L.seq_parts);
+        t->d_counters = reinterpret_cast<int32_t*>(base + L.counters);
         t->d_units = reinterpret_cast<int32_t*>(base + L.units);
+        t->d_unit_ids = reinterpret_cast<int32_t*>(base + L.unit_ids);
 
+        // One host image of the whole buffer (counters start at zero), copied once.
         t->staging.assign(L.total / sizeof(int32_t), 0);
         int32_t* hs = t->staging.data();
         std::memcpy(hs + L.table / 4, host_block_table,
                     sizeof(int32_t) * static_cast<size_t>(num_seqs) * max_blocks_per_seq);
         std::memcpy(hs + L.seq_lens / 4, host_seq_lens, sizeof(int32_t) * num_seqs);
-        std::memcpy(hs + L.split_base / 4, split_base.data(), sizeof(int32_t) * num_seqs);
-        for (size_t u = 0; u < units.size(); ++u) {
-            hs[L.units / 4 + 2 * u] = units[u].seq;
-            hs[L.units / 4 + 2 * u + 1] = units[u].part;
+        std::memcpy(hs + L.seq_parts / 4, P.seq_parts.data(), sizeof(int32_t) * 2 * num_seqs);
+        std::memcpy(hs + L.units / 4, P.units.data(), sizeof(int32_t) * P.units.size());
+        for (int32_t u = 0; u < P.num_units; ++u) {
+            const int32_t* d = &P.units[static_cast<size_t>(u) * pkv::kUnitInts];
+            const int32_t* row = host_block_table + static_cast<int64_t>(d[pkv::kUnitSeq]) * max_blocks_per_seq;
+            int32_t* ids = hs + L.unit_ids / 4 + static_cast<size_t>(u) * P.stride;
+            // processing order j = 0 .. nb-1 walks logical blocks b0 + (j + rot) mod nb;
+            // the tail of the stride repeats the first id
+            const int32_t b0 = d[pkv::kUnitB0], nb = d[pkv::kUnitNb], rot = d[pkv::kUnitRot];
+            for (int32_t j = 0; j < P.stride; ++j) {
+                const int32_t jj = j < nb ? (j + rot) % nb : rot;
+                ids[j] = row[b0 + jj];
+            }
         }
         hipStream_t st = static_cast<hipStream_t>(stream);
         hipError_t e = hipEventCreateWithFlags(&t->uploaded, hipEventDisableTiming);
@@ -269,12 +383,13 @@ pkv_status block_table_destroy(pkv_table* table) {
 }
 
 pkv_status block_table_info(const pkv_table* table, int32_t* num_units, int32_t* num_split_slots,
-                            int32_t* max_seq_len, int32_t* min_seq_len) {
+                            int32_t* max_seq_len, int32_t* min_seq_len, int32_t* max_parts) {
     if (!table) return PKV_ERR_INVALID;
     if (num_units) *num_units = table->num_units;
     if (num_split_slots) *num_split_slots = table->num_split_slots;
     if (max_seq_len) *max_seq_len = table->max_seq_len;
     if (min_seq_len) *min_seq_len = table->min_seq_len;
+    if (max_parts) *max_parts = table->max_parts;
     return PKV_OK;
 }
 
@@ -353,6 +468,7 @@ pkv_status paged_attention_verify(const pkv_pool* pool, int32_t layer, const pkv
     if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
     if (table->min_seq_len < query_rows) return PKV_ERR_SEQ_LEN;
     if (table->max_block_id >= pool->desc.num_blocks) return PKV_ERR_BLOCK_RANGE;
+    if (table->num_kv_heads != hkv) return PKV_ERR_INVALID;
     const size_t need = paged_attention_workspace_bytes(pool, table, num_q_heads, query_rows);
     if (need > 0 && (!dev_workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
     if (need > 0 && reinterpret_cast<uintptr_t>(dev_workspace) % kAlign) return PKV_ERR_INVALID;
@@ -361,10 +477,10 @@ pkv_status paged_attention_verify(const pkv_pool* pool, int32_t layer, const pkv
     a.pool = pool->base;
     a.k_scale = pool->k_scale;
     a.v_scale = pool->v_scale;
-    a.block_table = table->d_table;
-    a.seq_lens = table->d_seq_lens;
     a.units = table->d_units;
-    a.split_base = table->d_split_base;
+    a.unit_ids = table->d_unit_ids;
+    a.seq_parts = table->d_seq_parts;
+    a.counters = table->d_counters;
     a.q = dev_q;
     a.out = dev_out;
     const int64_t entries = static_cast<int64_t>(hkv) * table->num_split_slots * group * query_rows;
@@ -383,9 +499,11 @@ pkv_status paged_attention_verify(const pkv_pool* pool, int32_t layer, const pkv
     a.group = group;
     a.rows = group * query_rows;
     a.k_rows = query_rows;
-    a.max_blocks = table->max_blocks;
-    a.part_blocks = table->part_blocks;
+    a.head_dim = pool->desc.head_dim;
+    a.unit_stride = table->unit_stride;
     a.num_split_slots = table->num_split_slots;
+    a.max_parts = table->max_parts;
+    a.fuse_max_parts = pkv::kFuseMaxParts;
     a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
     a.score_scale = scale * 1.4426950408889634f;
     return hip_status(pkv::launch_attention(a, kv, pool->desc.head_dim, table->num_units,

@@ -53,12 +53,39 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// float -> bfloat16 bits, round to nearest even (NaN kept NaN).
+// float -> bfloat16 bits, round to nearest even (the gfx950 converter).
 __device__ __forceinline__ unsigned f32_to_bf16_rne(float f) {
-    unsigned u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    return __builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
+}
+
+// Two floats -> two bf16 (round to nearest even) packed low/high.
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Buffer resource over one block's K tile followed by its V tile.  Loads
+// through it address the tile with a per-lane 32-bit offset plus an immediate,
+// and read 0 beyond the two tiles.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int64_t tile_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0,
+                                             static_cast<int>(2 * tile_bytes), 0x00020000);
+}
+
+// Partial results pass between work-groups of one launch, which may run on
+// different XCDs with separate L2 caches: they are written and read with
+// agent-scope accesses, which the hardware keeps coherent across the device.
+__device__ __forceinline__ void xwg_store(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float xwg_load(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T>
+__device__ __forceinline__ T bload(__amdgpu_buffer_rsrc_t r, int voff, int imm) {
+    if constexpr (sizeof(T) == 16) return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, voff, imm, 0));
+    else if constexpr (sizeof(T) == 8) return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, voff, imm, 0));
+    else return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, imm, 0));
 }
 
 // Two fp8 E4M3 codes (bytes 0-1, or 2-3 when HI, of w) -> two bf16 values packed in one
@@ -78,14 +105,16 @@ template <int KVT, int D> struct TileRegs;
 template <int D> struct TileRegs<KV_BF16, D> {
     u32x4 k[D / 32];   // 8 bf16: token lane%16, dims of chunk 4s + lane/16
     u32x2 v[D / 16];   // 4 bf16: dim 16m + lane%16, tokens 4*(lane/16) .. +3
-    __device__ __forceinline__ void load(const uint8_t* kt, const uint8_t* vt, int lane) {
+    // koff = lane * 16; voff = TILE + (lane % 16) * 32 + (lane / 16) * 8
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int koff, int voff) {
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s)
-            k[s] = *reinterpret_cast<const u32x4*>(kt + (64 * s + lane) * 16);
+        for (int s = 0; s < D / 32; ++s) k[s] = bload<u32x4>(r, koff, 1024 * s);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int m = 0; m < D / 16; ++m)
-            v[m] = *reinterpret_cast<const u32x2*>(vt + (16 * m + (lane & 15)) * 32 + 8 * (lane >> 4));
+        for (int m = 0; m < D / 16; ++m) v[m] = bload<u32x2>(r, voff, 512 * m);
     }
+    static constexpr int kTile = 16 * D * 2;
+    __device__ static int v_offset(int lane) { return kTile + (lane & 15) * 32 + (lane >> 4) * 8; }
     // zero V of tokens >= nvalid among this lane's four (tokens 4j .. 4j+3)
     __device__ __forceinline__ void zero_v_from(int nvalid) {
         if (nvalid >= 4) return;
@@ -99,14 +128,16 @@ template <int D> struct TileRegs<KV_BF16, D> {
 template <int D> struct TileRegs<KV_FP8, D> {
     u32x4 k[D / 64];   // 16 codes: token lane%16, dims of chunk 4r + lane/16
     unsigned v[D / 16];  // 4 codes: dim 16m + lane%16, tokens 4*(lane/16) .. +3
-    __device__ __forceinline__ void load(const uint8_t* kt, const uint8_t* vt, int lane) {
+    // koff = lane * 16; voff = TILE + (lane % 16) * 16 + (lane / 16) * 4
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int koff, int voff) {
 #pragma unroll
-        for (int r = 0; r < D / 64; ++r)
-            k[r] = *reinterpret_cast<const u32x4*>(kt + (64 * r + lane) * 16);
+        for (int q = 0; q < D / 64; ++q) k[q] = bload<u32x4>(r, koff, 1024 * q);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int m = 0; m < D / 16; ++m)
-            v[m] = *reinterpret_cast<const unsigned*>(vt + (16 * m + (lane & 15)) * 16 + 4 * (lane >> 4));
+        for (int m = 0; m < D / 16; ++m) v[m] = bload<unsigned>(r, voff, 256 * m);
     }
+    static constexpr int kTile = 16 * D;
+    __device__ static int v_offset(int lane) { return kTile + (lane & 15) * 16 + (lane >> 4) * 4; }
     __device__ __forceinline__ void zero_v_from(int nvalid) {
         if (nvalid >= 4) return;
         const unsigned msk = nvalid <= 0 ? 0u : (0xffffffffu >> (8 * (4 - nvalid)));
@@ -118,14 +149,16 @@ template <int D> struct TileRegs<KV_FP8, D> {
 template <int D> struct TileRegs<KV_F32, D> {
     f32x4 k[D / 16];   // 4 f32: token lane%16, dims of chunk 4r + lane/16
     f32x4 v[D / 16];   // 4 f32: dim 16m + lane%16, tokens 4*(lane/16) .. +3
-    __device__ __forceinline__ void load(const uint8_t* kt, const uint8_t* vt, int lane) {
+    // koff = lane * 16; voff = TILE + (lane % 16) * 64 + (lane / 16) * 16
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int koff, int voff) {
 #pragma unroll
-        for (int r = 0; r < D / 16; ++r)
-            k[r] = *reinterpret_cast<const f32x4*>(kt + (64 * r + lane) * 16);
+        for (int q = 0; q < D / 16; ++q) k[q] = bload<f32x4>(r, koff, 1024 * q);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int m = 0; m < D / 16; ++m)
-            v[m] = *reinterpret_cast<const f32x4*>(vt + (16 * m + (lane & 15)) * 64 + 16 * (lane >> 4));
+        for (int m = 0; m < D / 16; ++m) v[m] = bload<f32x4>(r, voff, 1024 * m);
     }
+    static constexpr int kTile = 16 * D * 4;
+    __device__ static int v_offset(int lane) { return kTile + (lane & 15) * 64 + (lane >> 4) * 16; }
     __device__ __forceinline__ void zero_v_from(int nvalid) {
         if (nvalid >= 4) return;
 #pragma unroll
@@ -220,9 +253,7 @@ __device__ __forceinline__ void accumulate_pv(const TileRegs<KV_BF16, D>& t, con
     s16x4 pb[NT];
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
-        const unsigned w0 = f32_to_bf16_rne(p[c][0]) | (f32_to_bf16_rne(p[c][1]) << 16);
-        const unsigned w1 = f32_to_bf16_rne(p[c][2]) | (f32_to_bf16_rne(p[c][3]) << 16);
-        pb[c] = __builtin_bit_cast(s16x4, u32x2{w0, w1});
+        pb[c] = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[c][0], p[c][1]), pack_bf16x2(p[c][2], p[c][3])});
     }
 #pragma unroll
     for (int m = 0; m < D / 16; ++m) {
@@ -239,9 +270,7 @@ __device__ __forceinline__ void accumulate_pv(const TileRegs<KV_FP8, D>& t, cons
     s16x4 pb[NT];
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
-        const unsigned w0 = f32_to_bf16_rne(p[c][0]) | (f32_to_bf16_rne(p[c][1]) << 16);
-        const unsigned w1 = f32_to_bf16_rne(p[c][2]) | (f32_to_bf16_rne(p[c][3]) << 16);
-        pb[c] = __builtin_bit_cast(s16x4, u32x2{w0, w1});
+        pb[c] = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[c][0], p[c][1]), pack_bf16x2(p[c][2], p[c][3])});
     }
 #pragma unroll
     for (int m = 0; m < D / 16; ++m) {
@@ -272,9 +301,22 @@ __device__ __forceinline__ float as_used(float p) {
     else return __uint_as_float(f32_to_bf16_rne(p) << 16);
 }
 
+// Final output element (row r of KV head h of sequence seq, dim d).
+__device__ __forceinline__ void store_out(const AttnArgs& a, int seq, int h, int r, int d, float val) {
+    const int G = a.group;
+    const int jr = r / G;
+    const int g = r % G;
+    const int64_t oi = ((static_cast<int64_t>(seq) * a.k_rows + jr) * a.num_q_heads + h * G + g) * a.head_dim + d;
+    if (a.out_bf16)
+        reinterpret_cast<uint16_t*>(a.out)[oi] = static_cast<uint16_t>(f32_to_bf16_rne(val));
+    else
+        reinterpret_cast<float*>(a.out)[oi] = val;
+}
+
 // ------------------------------------------------------- partition kernel
 template <int KVT, int D, int NT>
-__global__ __launch_bounds__(64 * kWaves) void attn_partition_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NT == 1 ? (KVT == KV_FP8 ? 4 : (KVT == KV_BF16 ? 3 : 1)) : (NT == 2 && KVT != KV_F32 ? 2 : 1))))
+void attn_partition_kernel(AttnArgs a) {
     extern __shared__ float smem[];
     const int R = a.rows;
     float* acc_s = smem;                       // [R][D + 1] merged unnormalised output
@@ -287,12 +329,19 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partition_kernel(AttnArgs a)
     const int col = lane & 15;                 // column within a row tile
     const int unit = blockIdx.x;
     const int h = blockIdx.y;
-    const int seq = a.units[2 * unit];
-    const int part = a.units[2 * unit + 1];
-    const int n = a.seq_lens[seq];
-    const int nblk = (n + kBlock - 1) / kBlock;
-    const int b0 = part * a.part_blocks;
-    const int b1 = min(b0 + a.part_blocks, nblk);
+    // Unit descriptor (see the plan built by block_table_upload) and, loaded
+    // independently of it, this wave's first block ids.
+    const int32_t* ud = a.units + static_cast<int64_t>(unit) * kUnitInts;
+    const int32_t* uids = a.unit_ids + static_cast<int64_t>(unit) * a.unit_stride;
+    int id0 = 0;
+    if (wave + kWaves * lane < a.unit_stride) id0 = uids[wave + kWaves * lane];
+    const int seq = ud[kUnitSeq];
+    const int b0 = ud[kUnitB0];
+    const int nb = ud[kUnitNb];
+    const int n = ud[kUnitLen];
+    const int parts = ud[kUnitParts];
+    const int slot = ud[kUnitSlot];
+    const int rot = ud[kUnitRot];
     const int G = a.group;
     const int kq = a.k_rows;
 
@@ -333,12 +382,11 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partition_kernel(AttnArgs a)
         for (int m = 0; m < D / 16; ++m) o[c][m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int32_t* trow = a.block_table + static_cast<int64_t>(seq) * a.max_blocks;
     const int64_t block_stride = static_cast<int64_t>(a.num_kv_heads) * 2 * a.tile_bytes;
     const uint8_t* head_base = a.pool +
         static_cast<int64_t>(a.layer) * a.num_blocks * block_stride + static_cast<int64_t>(h) * 2 * a.tile_bytes;
 
-    auto process = [&](const TileRegs<KVT, D>& tr, int blk) {
+    auto process = [&](TileRegs<KVT, D>& tr, int blk) {
         f32x4 s[NT];
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
@@ -354,8 +402,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partition_kernel(AttnArgs a)
                 for (int i = 0; i < 4; ++i)
                     if (tok0 + i >= lim[c]) s[c][i] = neg_inf();
         }
-        TileRegs<KVT, D> tv = tr;
-        if (blk * kBlock + kBlock > n) tv.zero_v_from(n - tok0);
+        if (blk * kBlock + kBlock > n) tr.zero_v_from(n - tok0);
         f32x4 p[NT];
         bool rescale = false;
         float alpha[NT];
@@ -383,36 +430,41 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partition_kernel(AttnArgs a)
 #pragma unroll
                 for (int m = 0; m < D / 16; ++m) o[c][m] *= alpha[c];
         }
-        accumulate_pv<D, NT>(tv, p, o);
+        accumulate_pv<D, NT>(tr, p, o);
     };
 
-    const int nb = b1 - b0;
+    const int koff = lane * 16;
+    const int voff = TileRegs<KVT, D>::v_offset(lane);
+    // The unit's ids are stored in walking order j = 0 .. nb-1, which visits
+    // logical block b0 + (j + rot) mod nb: sequences that share physical
+    // blocks (a common prefix) start their walk at different blocks instead of
+    // all reading the same block at the same moment.
+    auto logical = [&](int j) { const int x = j + rot; return b0 + (x >= nb ? x - nb : x); };
     for (int base = wave; base < nb; base += 64 * kWaves) {
         const int cnt = min(64, (nb - base + kWaves - 1) / kWaves);
-        int id = lane < cnt ? trow[b0 + base + kWaves * lane] : 0;
+        int id = id0;
+        if (base != wave) {
+            id = 0;
+            if (base + kWaves * lane < a.unit_stride) id = uids[base + kWaves * lane];
+        }
         id = min(max(id, 0), a.num_blocks - 1);
-        auto ktile = [&](int i) {
-            const int pid = __builtin_amdgcn_readlane(id, i);
-            return head_base + static_cast<int64_t>(pid) * block_stride;
+        // The next block's loads are issued unconditionally so the wait counts
+        // stay static; past the last block they go through a zero-sized
+        // resource (no memory traffic, zeros returned).
+        auto rsrc = [&](int i, bool valid) {
+            const int pid = __builtin_amdgcn_readlane(id, min(i, 63));
+            return tile_rsrc(head_base + static_cast<int64_t>(pid) * block_stride, valid ? a.tile_bytes : 0);
         };
         TileRegs<KVT, D> ta, tb;
-        {
-            const uint8_t* t0 = ktile(0);
-            ta.load(t0, t0 + a.tile_bytes, lane);
+        ta.load(rsrc(0, true), koff, voff);
+        int i = 0;
+        for (; i + 1 < cnt; i += 2) {
+            tb.load(rsrc(i + 1, true), koff, voff);
+            process(ta, logical(base + kWaves * i));
+            ta.load(rsrc(i + 2, i + 2 < cnt), koff, voff);
+            process(tb, logical(base + kWaves * (i + 1)));
         }
-        for (int i = 0; i < cnt; i += 2) {
-            if (i + 1 < cnt) {
-                const uint8_t* t1 = ktile(i + 1);
-                tb.load(t1, t1 + a.tile_bytes, lane);
-            }
-            process(ta, b0 + base + kWaves * i);
-            if (i + 1 >= cnt) break;
-            if (i + 2 < cnt) {
-                const uint8_t* t2 = ktile(i + 2);
-                ta.load(t2, t2 + a.tile_bytes, lane);
-            }
-            process(tb, b0 + base + kWaves * (i + 1));
-        }
+        if (i < cnt) process(ta, logical(base + kWaves * i));
     }
 
     // Merge the waves: publish (m, l), rescale O to the common max, add in LDS.
@@ -457,7 +509,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partition_kernel(AttnArgs a)
         __syncthreads();
     }
 
-    const int sbase = a.split_base[seq];
+    const bool split = parts > 1;
     for (int e = threadIdx.x; e < R * D; e += 64 * kWaves) {
         const int r = e / D;
         const int d = e % D;
@@ -470,24 +522,55 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partition_kernel(AttnArgs a)
             for (int w = 0; w < kWaves; ++w) L += l_s[w * R + r] * fast_exp2(m_s[w * R + r] - M);
         }
         const float O = acc_s[r * (D + 1) + d];
-        if (sbase < 0) {
-            const int jr = r / G;
-            const int g = r % G;
-            const int64_t oi = ((static_cast<int64_t>(seq) * kq + jr) * a.num_q_heads + h * G + g) * D + d;
-            const float val = O / L * vscale;
-            if (a.out_bf16)
-                reinterpret_cast<uint16_t*>(a.out)[oi] = static_cast<uint16_t>(f32_to_bf16_rne(val));
-            else
-                reinterpret_cast<float*>(a.out)[oi] = val;
+        if (!split) {
+            store_out(a, seq, h, r, d, O / L * vscale);
         } else {
-            const int64_t slot = static_cast<int64_t>(h) * a.num_split_slots + sbase + part;
-            a.part_o[(slot * R + r) * D + d] = O;
+            const int64_t sl = static_cast<int64_t>(h) * a.num_split_slots + slot;
+            xwg_store(a.part_o + (sl * R + r) * D + d, O);
             if (d == 0) {
-                a.part_m[slot * R + r] = M;
-                a.part_l[slot * R + r] = L;
+                xwg_store(a.part_m + sl * R + r, M);
+                xwg_store(a.part_l + sl * R + r, L);
             }
         }
     }
+    if (!split || parts > a.fuse_max_parts) return;
+
+    // Split-KV merge in the kernel: the last of the sequence's work-groups
+    // (for this KV head) to take a ticket combines all partials.  Every thread
+    // waits until its partial stores have completed before the work-group
+    // takes its ticket; the last one reads the partials only after its ticket.
+    __shared__ int ticket;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int32_t* counter = a.counters + static_cast<int64_t>(seq) * a.num_kv_heads + h;
+    if (threadIdx.x == 0)
+        ticket = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (ticket != parts - 1) return;
+    const int64_t sl0 = static_cast<int64_t>(h) * a.num_split_slots + (slot - ud[kUnitPart]);
+    float* Mr = m_s;          // [R] reused: the common max of each row
+    float* Lr = m_s + R;      // [R] and its sum
+    for (int r = threadIdx.x; r < R; r += 64 * kWaves) {
+        float M = neg_inf();
+        for (int q = 0; q < parts; ++q) M = fmaxf(M, xwg_load(a.part_m + (sl0 + q) * R + r));
+        float L = 0.f;
+        for (int q = 0; q < parts; ++q)
+            L += xwg_load(a.part_l + (sl0 + q) * R + r) * fast_exp2(xwg_load(a.part_m + (sl0 + q) * R + r) - M);
+        Mr[r] = M;
+        Lr[r] = L;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < R * D; e += 64 * kWaves) {
+        const int r = e / D;
+        const int d = e % D;
+        const float M = Mr[r];
+        float O = 0.f;
+        for (int q = 0; q < parts; ++q)
+            O += xwg_load(a.part_o + ((sl0 + q) * R + r) * D + d) * fast_exp2(xwg_load(a.part_m + (sl0 + q) * R + r) - M);
+        store_out(a, seq, h, r, d, O / Lr[r] * vscale);
+    }
+    if (threadIdx.x == 0)   // ready for the next call
+        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------ merge kernel
@@ -501,12 +584,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int fp8) {
     const int seq = blockIdx.x;
     const int h = blockIdx.y;
     const int r = blockIdx.z;
-    const int sbase = a.split_base[seq];
-    if (sbase < 0) return;
+    const int nparts = a.seq_parts[2 * seq];
+    const int sbase = a.seq_parts[2 * seq + 1];
+    if (nparts <= a.fuse_max_parts) return;   // merged inside the partition kernel
     const int R = a.rows;
-    const int n = a.seq_lens[seq];
-    const int nblk = (n + kBlock - 1) / kBlock;
-    const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
     const int64_t slot0 = static_cast<int64_t>(h) * a.num_split_slots + sbase;
     const float* pm = a.part_m + slot0 * R + r;
     const float* pl = a.part_l + slot0 * R + r;
@@ -558,18 +639,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int fp8) {
         for (int g = 1; g < GR; ++g) sum += part_acc[g * Q + tid];
         const float L = red[4] + red[5] + red[6] + red[7];
         const float vscale = fp8 ? a.v_scale[a.layer * a.num_kv_heads + h] : 1.f;
-        const int G = a.group;
-        const int jr = r / G;
-        const int g = r % G;
-        const int64_t oi = ((static_cast<int64_t>(seq) * a.k_rows + jr) * a.num_q_heads + h * G + g) * D + 4 * tid;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float val = sum[i] / L * vscale;
-            if (a.out_bf16)
-                reinterpret_cast<uint16_t*>(a.out)[oi + i] = static_cast<uint16_t>(f32_to_bf16_rne(val));
-            else
-                reinterpret_cast<float*>(a.out)[oi + i] = val;
-        }
+        for (int i = 0; i < 4; ++i) store_out(a, seq, h, r, 4 * tid + i, sum[i] / L * vscale);
     }
 }
 
@@ -580,7 +651,7 @@ hipError_t launch_instance(const AttnArgs& a, int num_units, hipStream_t stream)
     hipLaunchKernelGGL((attn_partition_kernel<KVT, D, NT>), grid, dim3(64 * kWaves), lds, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (a.num_split_slots > 0) {
+    if (a.max_parts > a.fuse_max_parts) {
         dim3 g2(a.num_seqs, a.num_kv_heads, a.rows);
         hipLaunchKernelGGL((attn_merge_kernel<D>), g2, dim3(256), 0, stream, a, KVT == KV_FP8 ? 1 : 0);
         err = hipGetLastError();

@@ -10,15 +10,37 @@ namespace pkv {
 constexpr int kBlock = 16;       // tokens per physical block
 constexpr int kMaxRows = 64;     // query rows per KV head handled by one work-group
 
+// Work-unit descriptor: one (sequence, partition), int32 fields.
+constexpr int kUnitSeq = 0;      // sequence index
+constexpr int kUnitB0 = 1;       // first logical block of the partition
+constexpr int kUnitNb = 2;       // blocks in the partition
+constexpr int kUnitLen = 3;      // sequence length (positions visible to its last row)
+constexpr int kUnitPart = 4;     // partition index within the sequence
+constexpr int kUnitParts = 5;    // partitions of the sequence
+constexpr int kUnitSlot = 6;     // partial-result slot (split sequences) or -1
+constexpr int kUnitRot = 7;      // walking-order rotation, seq mod nb
+constexpr int kUnitInts = 8;
+
+// Sequences with at most this many partitions are merged inside the
+// partition kernel; longer ones by the separate merge kernel.
+constexpr int kFuseMaxParts = 32;
+
+// Balanced plan: about one round of work-groups (kAutoWgsPerCu resident per
+// CU, over all KV heads), with units of kAutoMinBlocks .. kAutoMaxBlocks
+// blocks; large batches are cut into more rounds of at most kAutoMaxBlocks.
+constexpr int kAutoWgsPerCu = 3;
+constexpr int kAutoMinBlocks = 8;
+constexpr int kAutoMaxBlocks = 256;
+
 // Everything the attention kernel reads; built by the host per call.
 struct AttnArgs {
     const uint8_t* pool;         // pool base
     const float* k_scale;        // [L][H_kv] (fp8 pools) or null
     const float* v_scale;
-    const int32_t* block_table;  // [B][max_blocks]
-    const int32_t* seq_lens;     // [B]
-    const int32_t* units;        // [U][2] = (sequence, partition)
-    const int32_t* split_base;   // [B] first partial slot of a split sequence, -1 otherwise
+    const int32_t* units;        // [U][kUnitInts] work-unit descriptors
+    const int32_t* unit_ids;     // [U][unit_stride] physical block ids in walking order
+    const int32_t* seq_parts;    // [B][2] = (partitions, first partial slot or -1)
+    int32_t* counters;           // [B][H_kv] arrival tickets of the in-kernel merge (zero between calls)
     const void* q;               // [B][k][H_q][D]
     void* out;                   // [B][k][H_q][D]
     float* part_o;               // [H_kv][slots][R][D]
@@ -30,12 +52,14 @@ struct AttnArgs {
     int32_t num_seqs;
     int32_t num_kv_heads;
     int32_t num_q_heads;
+    int32_t head_dim;
     int32_t group;               // G = H_q / H_kv
     int32_t rows;                // R = G * k, query rows per KV head
     int32_t k_rows;              // k
-    int32_t max_blocks;          // table row width
-    int32_t part_blocks;         // blocks per partition
+    int32_t unit_stride;
     int32_t num_split_slots;
+    int32_t max_parts;
+    int32_t fuse_max_parts;
     int32_t out_bf16;            // 1: bf16 output, 0: f32 output
     float score_scale;           // softmax scale * log2(e)
 };

@@ -122,8 +122,13 @@ def test_block_table_validation_before_any_device_work(pk):
     assert upload(good, [49, 16]) == -4                              # beyond 3 blocks * 16
     assert upload(good, [48, 16], P=24) == -1                        # partition not a multiple of 16
     assert upload(good, [48, 16], nbytes=16) == -5                   # device buffer too small
-    assert lib.block_table_device_bytes(0, 3, 32) == 0
-    assert lib.block_table_device_bytes(2, 3, 32) >= 4 * (2 * 3 + 2 + 2 + 2 * 2 * 3)
+    lens = np.ascontiguousarray([48, 16], dtype=np.int32)
+    lp = lens.ctypes.data_as(ctypes.c_void_p)
+    assert lib.block_table_device_bytes(pool, lp, 0, 3, 32) == 0
+    assert lib.block_table_device_bytes(pool, lp, 2, 3, 24) == 0
+    assert lib.block_table_device_bytes(None, lp, 2, 3, 32) == 0
+    # table + lens + (parts, slot) + counters + 3 units x 8 ints + ids, each padded to 256 B
+    assert lib.block_table_device_bytes(pool, lp, 2, 3, 32) == 6 * 256
     lib.kv_pool_destroy(pool)
 
 

@@ -34,7 +34,7 @@ def test_parity_reduced_configs(name):
     log(f"  {name}: max abs err {err:.3e}; units {s.table.info()}")
 
 
-@pytest.mark.parametrize("P", [16, 64, 512, 0])
+@pytest.mark.parametrize("P", [16, 64, 512, 0, -1])
 def test_partition_sizes_agree(P):
     log(f"partition {P}")
     w = workloads.make("c2s")
