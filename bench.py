@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--rotate", type=int, default=3, help="independent pools cycled through")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after timing, copy MIB MiB device-to-device 3 times: the known-size "
+                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -207,6 +210,14 @@ def main():
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calibrate_copy_bytes"] = n
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
         image = pools[0].storage.cpu().numpy()
