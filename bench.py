@@ -2,9 +2,10 @@
 """Paged decode-attention benchmark on one MI355X.
 
 One step is the whole hot path over one batch: the slot mapping of each
-sequence's new token, the append of its K and V (reshape_and_cache), and paged
-decode attention over every sequence (partition kernel plus, for split
-sequences, the split-KV merge).  The default workload is the Llama-3-8B-shaped
+sequence's new token, the append of its K and V, and paged decode attention
+over every sequence with the split-KV merge.  By default the step is the
+single fused launch paged_attention_append; --separate runs the same work as
+slot_mapping_compute + reshape_and_cache + paged_attention_decode.  The default workload is the Llama-3-8B-shaped
 decode layer: 32 query / 8 KV heads, head_dim 128, bf16 KV, 16-token blocks,
 64 sequences with lengths uniform in [512, 4096], a seeded random block
 placement over a pool of 1.25x the blocks in use, N(0, 1) values.
@@ -51,6 +52,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=3, help="independent pools cycled through")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="run the step as three calls (slot mapping, append, attention) instead of one")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after timing, copy MIB MiB device-to-device 3 times: the known-size "
                          "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -143,11 +146,15 @@ def main():
 
     def step(i, timed):
         pool = pools[i % len(pools)]
-        pk.slot_mapping_compute(table, sid, pos, out=slots)
-        pk.reshape_and_cache(pool, w.layer, k_new, v_new, slots)
+        if args.separate:
+            pk.slot_mapping_compute(table, sid, pos, out=slots)
+            pk.reshape_and_cache(pool, w.layer, k_new, v_new, slots)
         if timed:
             ev[i][0].record()
-        pk.paged_attention_decode(pool, w.layer, table, q, scale, workspace=ws, out=out)
+        if args.separate:
+            pk.paged_attention_decode(pool, w.layer, table, q, scale, workspace=ws, out=out)
+        else:
+            pk.paged_attention_append(pool, w.layer, table, k_new, v_new, q, scale, workspace=ws, out=out)
         if timed:
             ev[i][1].record()
 
@@ -197,6 +204,8 @@ def main():
         "dtype": w.kv_dtype,
         "data": "synthetic (seeded N(0,1) KV, random block placement)",
         "config": {"workload": WORKLOAD_NAMES[args.workload], "batch": w.batch,
+                   "step": "slot_mapping_compute + reshape_and_cache + paged_attention_decode" if args.separate
+                           else "paged_attention_append (slot mapping, append and attention in one launch)",
                    "tokens": int(w.seq_lens.sum()), "partition_tokens": P,
                    "pools_rotated": len(pools), "work_units": info["num_units"]},
         "seqs_per_s": round(w.batch / (ms_step * 1e-3), 1),

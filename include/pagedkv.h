@@ -270,6 +270,31 @@ pkv_status paged_attention_verify(const pkv_pool* pool, int32_t layer, const pkv
                                   size_t workspace_bytes, void* dev_out, int32_t out_dtype,
                                   void* stream);
 
+/*
+ * One decode (or verify) step in one launch: append the K and V of every
+ * sequence's k newest tokens to the pool, then attend.  Equivalent to
+ * slot_mapping_compute for positions n-k .. n-1 of each sequence, then
+ * reshape_and_cache, then paged_attention_verify (decode when k = 1), and
+ * writes the same pool bytes and outputs (page "KV cache & continuous
+ * batching", section "The core insight": a step extends the cache with the
+ * new token and attends over it; section "2. PagedAttention (vLLM)" for the
+ * slot rule).
+ *   dev_k_new, dev_v_new  [num_seqs][query_rows][num_kv_heads][head_dim] in
+ *                 in_dtype (as reshape_and_cache): row j of sequence s is the
+ *                 token at position seq_len[s] - query_rows + j.
+ *   other arguments as paged_attention_verify.
+ * The tokens are written by the work-group that attends over their block,
+ * before it reads any block.  Errors as paged_attention_verify, plus
+ * PKV_ERR_INVALID for null token pointers and PKV_ERR_UNSUPPORTED for an
+ * in_dtype the pool does not take.
+ */
+pkv_status paged_attention_append(const pkv_pool* pool, int32_t layer, const pkv_table* table,
+                                  const void* dev_k_new, const void* dev_v_new, int32_t in_dtype,
+                                  const void* dev_q, int32_t q_dtype, int32_t query_rows,
+                                  int32_t num_q_heads, float scale, void* dev_workspace,
+                                  size_t workspace_bytes, void* dev_out, int32_t out_dtype,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,6 +51,8 @@ PROTOTYPES = {
                                           _vp, _c_size, _vp, _c_int32, _vp]),
     "paged_attention_verify": (_c_int32, [_vp, _c_int32, _vp, _vp, _c_int32, _c_int32, _c_int32,
                                           ctypes.c_float, _vp, _c_size, _vp, _c_int32, _vp]),
+    "paged_attention_append": (_c_int32, [_vp, _c_int32, _vp, _vp, _vp, _c_int32, _vp, _c_int32, _c_int32,
+                                          _c_int32, ctypes.c_float, _vp, _c_size, _vp, _c_int32, _vp]),
 }
 
 

@@ -211,3 +211,25 @@ def paged_attention_verify(pool, layer, table, q, scale=None, workspace=None, ou
         pool.handle, int(layer), table.handle, _ptr(q), _TORCH_CODE[q.dtype], int(k), Hq, scale,
         _ptr(workspace), ws_bytes, _ptr(out), _TORCH_CODE[out.dtype], _stream(q.device)))
     return out
+
+
+def paged_attention_append(pool, layer, table, k_new, v_new, q, scale=None, workspace=None, out=None,
+                           out_dtype=None):
+    """Append then attend in one launch.
+
+    q: [B][H_q][d] (decode) or [B][k][H_q][d] (verify); k_new, v_new:
+    [B][k][H_kv][d] (k = 1 may be given as [B][H_kv][d]), the K/V of each
+    sequence's k newest positions.  Returns out shaped like q.
+    """
+    decode = q.dim() == 3
+    k = 1 if decode else q.shape[1]
+    assert q.shape[0] == table.num_seqs
+    assert k_new.shape == v_new.shape and k_new.dtype == v_new.dtype and k_new.is_cuda
+    assert k_new.is_contiguous() and v_new.is_contiguous()
+    assert k_new.numel() == table.num_seqs * k * pool.num_kv_heads * pool.head_dim
+    out, workspace, ws_bytes, scale, Hq = _attention(pool, layer, table, q, k, scale, workspace, out, out_dtype)
+    _check("paged_attention_append", lib.paged_attention_append(
+        pool.handle, int(layer), table.handle, _ptr(k_new), _ptr(v_new), _TORCH_CODE[k_new.dtype],
+        _ptr(q), _TORCH_CODE[q.dtype], int(k), Hq, scale, _ptr(workspace), ws_bytes, _ptr(out),
+        _TORCH_CODE[out.dtype], _stream(q.device)))
+    return out

@@ -450,10 +450,16 @@ size_t paged_attention_workspace_bytes(const pkv_pool* pool, const pkv_table* ta
     return o_bytes + 2 * ml_bytes;
 }
 
-pkv_status paged_attention_verify(const pkv_pool* pool, int32_t layer, const pkv_table* table, const void* dev_q,
-                                  int32_t q_dtype, int32_t query_rows, int32_t num_q_heads, float scale,
-                                  void* dev_workspace, size_t workspace_bytes, void* dev_out, int32_t out_dtype,
-                                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Attention over the table's units, optionally appending the k newest tokens
+// of every sequence first (k_new != NULL).
+pkv_status attention_call(const pkv_pool* pool, int32_t layer, const pkv_table* table, const void* k_new,
+                          const void* v_new, int32_t in_dtype, const void* dev_q, int32_t q_dtype,
+                          int32_t query_rows, int32_t num_q_heads, float scale, void* dev_workspace,
+                          size_t workspace_bytes, void* dev_out, int32_t out_dtype, void* stream) {
     if (!pool || !table || !dev_q || !dev_out) return PKV_ERR_INVALID;
     if (layer < 0 || layer >= pool->desc.num_layers) return PKV_ERR_INVALID;
     if (query_rows < 1 || num_q_heads < 1) return PKV_ERR_INVALID;
@@ -472,6 +478,12 @@ pkv_status paged_attention_verify(const pkv_pool* pool, int32_t layer, const pkv
     const size_t need = paged_attention_workspace_bytes(pool, table, num_q_heads, query_rows);
     if (need > 0 && (!dev_workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
     if (need > 0 && reinterpret_cast<uintptr_t>(dev_workspace) % kAlign) return PKV_ERR_INVALID;
+    if (k_new || v_new) {
+        if (!k_new || !v_new) return PKV_ERR_INVALID;
+        const bool ok = (kv == PKV_F32 && in_dtype == PKV_F32) || (kv == PKV_BF16 && in_dtype == PKV_BF16) ||
+                        (kv == PKV_FP8_E4M3 && (in_dtype == PKV_F32 || in_dtype == PKV_BF16));
+        if (!ok) return PKV_ERR_UNSUPPORTED;
+    }
 
     pkv::AttnArgs a;
     a.pool = pool->base;
@@ -483,6 +495,9 @@ pkv_status paged_attention_verify(const pkv_pool* pool, int32_t layer, const pkv
     a.counters = table->d_counters;
     a.q = dev_q;
     a.out = dev_out;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.append_in_f32 = in_dtype == PKV_F32 ? 1 : 0;
     const int64_t entries = static_cast<int64_t>(hkv) * table->num_split_slots * group * query_rows;
     uint8_t* ws = static_cast<uint8_t*>(dev_workspace);
     const size_t o_bytes = align_up(sizeof(float) * static_cast<size_t>(entries) * pool->desc.head_dim);
@@ -508,6 +523,28 @@ pkv_status paged_attention_verify(const pkv_pool* pool, int32_t layer, const pkv
     a.score_scale = scale * 1.4426950408889634f;
     return hip_status(pkv::launch_attention(a, kv, pool->desc.head_dim, table->num_units,
                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_attention_verify(const pkv_pool* pool, int32_t layer, const pkv_table* table, const void* dev_q,
+                                  int32_t q_dtype, int32_t query_rows, int32_t num_q_heads, float scale,
+                                  void* dev_workspace, size_t workspace_bytes, void* dev_out, int32_t out_dtype,
+                                  void* stream) {
+    return attention_call(pool, layer, table, nullptr, nullptr, 0, dev_q, q_dtype, query_rows, num_q_heads, scale,
+                          dev_workspace, workspace_bytes, dev_out, out_dtype, stream);
+}
+
+pkv_status paged_attention_append(const pkv_pool* pool, int32_t layer, const pkv_table* table,
+                                  const void* dev_k_new, const void* dev_v_new, int32_t in_dtype,
+                                  const void* dev_q, int32_t q_dtype, int32_t query_rows, int32_t num_q_heads,
+                                  float scale, void* dev_workspace, size_t workspace_bytes, void* dev_out,
+                                  int32_t out_dtype, void* stream) {
+    if (!dev_k_new || !dev_v_new) return PKV_ERR_INVALID;
+    return attention_call(pool, layer, table, dev_k_new, dev_v_new, in_dtype, dev_q, q_dtype, query_rows,
+                          num_q_heads, scale, dev_workspace, workspace_bytes, dev_out, out_dtype, stream);
 }
 
 pkv_status paged_attention_decode(const pkv_pool* pool, int32_t layer, const pkv_table* table, const void* dev_q,

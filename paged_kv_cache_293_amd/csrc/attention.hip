@@ -34,7 +34,7 @@
 //   fp8 : codes converted to bf16 in registers (exact), then as bf16; the K
 //         scale folds into the score scale, the V scale into the final divide;
 //   f32 : v_mfma_f32_16x16x4_f32 for both products, probabilities in f32.
-#include "pkv_internal.h"
+#include "pkv_device.h"
 
 namespace pkv {
 namespace {
@@ -44,8 +44,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
 constexpr int kWaves = 4;
 
@@ -432,6 +430,43 @@ void attn_partition_kernel(AttnArgs a) {
         }
         accumulate_pv<D, NT>(tr, p, o);
     };
+
+    // Fused append (paged_attention_append): the k newest positions
+    // n-k .. n-1 of the sequence are written into the pool, for this KV head,
+    // by the work-group whose unit holds them, before any tile is read.
+    if (a.k_new != nullptr) {
+        const int first_new = n - kq;
+        const int lo = max(first_new, b0 * kBlock);
+        const int hi = min(n, (b0 + nb) * kBlock);
+        if (lo < hi) {
+            const int ib = a.append_in_f32 ? 4 : 2;
+            for (int t = lo; t < hi; ++t) {
+                int j = t / kBlock - b0 - rot;
+                if (j < 0) j += nb;
+                const int pid = min(max(uids[j], 0), a.num_blocks - 1);
+                uint8_t* blk = const_cast<uint8_t*>(a.pool) +
+                    (static_cast<int64_t>(a.layer) * a.num_blocks + pid) * block_stride;
+                const int64_t row = ((static_cast<int64_t>(seq) * kq + (t - first_new)) * a.num_kv_heads) * D * ib;
+                const uint8_t* kr = reinterpret_cast<const uint8_t*>(a.k_new) + row;
+                const uint8_t* vr = reinterpret_cast<const uint8_t*>(a.v_new) + row;
+                const float* ks = a.k_scale ? a.k_scale + a.layer * a.num_kv_heads : nullptr;
+                const float* vs = a.v_scale ? a.v_scale + a.layer * a.num_kv_heads : nullptr;
+                if constexpr (KVT == KV_FP8) {
+                    if (a.append_in_f32)
+                        write_token<KVT, KV_F32, D>(blk, a.tile_bytes, t % kBlock, kr, vr, h, 1, ks, vs,
+                                                    threadIdx.x, 64 * kWaves);
+                    else
+                        write_token<KVT, KV_BF16, D>(blk, a.tile_bytes, t % kBlock, kr, vr, h, 1, ks, vs,
+                                                     threadIdx.x, 64 * kWaves);
+                } else {
+                    write_token<KVT, KVT, D>(blk, a.tile_bytes, t % kBlock, kr, vr, h, 1, ks, vs,
+                                             threadIdx.x, 64 * kWaves);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);   // this thread's stores have completed
+            __syncthreads();                 // and every thread's, before the tiles are read
+        }
+    }
 
     const int koff = lane * 16;
     const int voff = TileRegs<KVT, D>::v_offset(lane);

@@ -43,6 +43,8 @@ struct AttnArgs {
     int32_t* counters;           // [B][H_kv] arrival tickets of the in-kernel merge (zero between calls)
     const void* q;               // [B][k][H_q][D]
     void* out;                   // [B][k][H_q][D]
+    const void* k_new;           // fused append: [B][k][H_kv][D] K of positions n-k .. n-1, or null
+    const void* v_new;           // and V
     float* part_o;               // [H_kv][slots][R][D]
     float* part_m;               // [H_kv][slots][R]
     float* part_l;               // [H_kv][slots][R]
@@ -61,6 +63,7 @@ struct AttnArgs {
     int32_t max_parts;
     int32_t fuse_max_parts;
     int32_t out_bf16;            // 1: bf16 output, 0: f32 output
+    int32_t append_in_f32;       // fused append input: 1 float32, 0 bfloat16
     float score_scale;           // softmax scale * log2(e)
 };
 

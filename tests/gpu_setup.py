@@ -69,7 +69,7 @@ def assert_close(got, ref, kv_dtype, what=""):
 class Setup:
     """A workload standing on the device, plus the oracle's view of it."""
 
-    def __init__(self, w, partition_tokens=None, poison=True):
+    def __init__(self, w, partition_tokens=None, poison=True, write_new=True):
         import paged_kv_cache_293_amd as pk
         self.pk = pk
         self.w = w
@@ -92,7 +92,8 @@ class Setup:
             self._write(w.pre_seq_ids, w.pre_positions, w.k_pre, w.v_pre)
         else:
             workloads.fill_pool_random(storage, w.kv_dtype, w.seed)
-        self._write(w.new_seq_ids, w.new_positions, w.k_new, w.v_new)
+        if write_new:
+            self._write(w.new_seq_ids, w.new_positions, w.k_new, w.v_new)
         self.q = to_device(w.q[:, 0] if w.k_rows == 1 else w.q, w.q_dtype)
         torch.cuda.synchronize()
 
