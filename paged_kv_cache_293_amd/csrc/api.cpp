@@ -39,6 +39,7 @@ struct pkv_table {
     int32_t* d_seq_lens;
     int32_t* d_seq_parts;
     int32_t* d_counters;
+    int32_t* d_queue;
     int32_t* d_units;
     int32_t* d_unit_ids;
     std::vector<int32_t> staging;   // source of the asynchronous upload
@@ -82,7 +83,7 @@ struct Plan {
 
 // Device sub-buffers of an uploaded table, in this order, each 256-byte aligned.
 struct TableLayout {
-    size_t table, seq_lens, seq_parts, counters, units, unit_ids, total;
+    size_t table, seq_lens, seq_parts, counters, queue, units, unit_ids, total;
 };
 
 int device_cu_count() {
@@ -102,8 +103,16 @@ int device_cu_count() {
 // at most kAutoWgsPerCu work-groups per CU over all KV heads, kept within
 // [kAutoMinBlocks, kAutoMaxBlocks].
 int32_t auto_unit_blocks(const std::vector<int32_t>& nblk, int32_t num_kv_heads) {
-    const int64_t target_units = std::max<int64_t>(
-        1, static_cast<int64_t>(device_cu_count()) * pkv::kAutoWgsPerCu / std::max(1, num_kv_heads));
+    const int64_t slots = static_cast<int64_t>(device_cu_count()) * pkv::kAutoWgsPerCu;
+    int64_t total = 0;
+    for (int32_t b : nblk) total += b;
+    total *= std::max(1, num_kv_heads);
+    // Items per work-group: as many as keep a unit at kAutoMinItemBlocks or more
+    // (a work-group's fixed cost per item is amortised over its blocks), at
+    // most kAutoItemsPerWg.
+    const int64_t per_slot = total / std::max<int64_t>(1, slots);
+    const int64_t items = std::max<int64_t>(1, std::min<int64_t>(pkv::kAutoItemsPerWg, per_slot / pkv::kAutoMinItemBlocks));
+    const int64_t target_units = std::max<int64_t>(1, slots * items / std::max(1, num_kv_heads));
     int32_t lo = pkv::kAutoMinBlocks, hi = pkv::kAutoMinBlocks;
     for (int32_t b : nblk) hi = std::max(hi, b);
     auto units_for = [&](int32_t T) {
@@ -195,6 +204,8 @@ TableLayout table_layout(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_he
     off = align_up(off + sizeof(int32_t) * 2 * num_seqs);
     L.counters = off;
     off = align_up(off + sizeof(int32_t) * static_cast<size_t>(num_seqs) * num_kv_heads);
+    L.queue = off;
+    off = align_up(off + sizeof(int32_t) * 2);
     L.units = off;
     off = align_up(off + sizeof(int32_t) * pkv::kUnitInts * static_cast<size_t>(P.num_units));
     L.unit_ids = off;
@@ -331,6 +342,7 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
         t->d_seq_lens = reinterpret_cast<int32_t*>(base + L.seq_lens);
         t->d_seq_parts = reinterpret_cast<int32_t*>(base + L.seq_parts);
         t->d_counters = reinterpret_cast<int32_t*>(base + L.counters);
+        t->d_queue = reinterpret_cast<int32_t*>(base + L.queue);
         t->d_units = reinterpret_cast<int32_t*>(base + L.units);
         t->d_unit_ids = reinterpret_cast<int32_t*>(base + L.unit_ids);
 
@@ -493,6 +505,7 @@ pkv_status attention_call(const pkv_pool* pool, int32_t layer, const pkv_table* 
     a.unit_ids = table->d_unit_ids;
     a.seq_parts = table->d_seq_parts;
     a.counters = table->d_counters;
+    a.queue = table->d_queue;
     a.q = dev_q;
     a.out = dev_out;
     a.k_new = k_new;
@@ -516,6 +529,7 @@ pkv_status attention_call(const pkv_pool* pool, int32_t layer, const pkv_table* 
     a.k_rows = query_rows;
     a.head_dim = pool->desc.head_dim;
     a.unit_stride = table->unit_stride;
+    a.num_items = table->num_units * hkv;
     a.num_split_slots = table->num_split_slots;
     a.max_parts = table->max_parts;
     a.fuse_max_parts = pkv::kFuseMaxParts;

@@ -10,15 +10,19 @@
 // per sequence with causal visibility among them (page 1, section
 // "5. Speculative decoding").
 //
-// Work decomposition.  One work-group of W = 4 wavefronts handles one
-// (sequence, partition) unit for one KV head.  Its waves take the partition's
-// 16-token blocks round-robin and each keeps an online softmax (running max m,
-// running sum l, unnormalised output O) for all query rows of the KV head:
-// R = G * k rows, held as NT = ceil(R / 16) column tiles of 16.  The waves are
-// merged through LDS at the end (added in wave order, so results are
-// deterministic); a sequence with one partition writes its final
-// output there, a split sequence writes (O, m, l) partials that
-// attn_merge_kernel combines.
+// Work decomposition.  An item is one (sequence, partition) unit for one KV
+// head.  One work-group of W = 4 wavefronts attends over an item: its waves
+// take the partition's 16-token blocks round-robin and each keeps an online
+// softmax (running max m, running sum l, unnormalised output O) for all query
+// rows of the KV head: R = G * k rows, held as NT = ceil(R / 16) column tiles
+// of 16.  The waves are merged through LDS at the end (added in wave order,
+// so results are deterministic); a sequence with one partition writes its
+// final output there, a split sequence writes (O, m, l) partials that the
+// last of its work-groups to finish (or attn_merge_kernel, for many
+// partitions) combines.  The grid holds only as many work-groups as fit on
+// the device at once; they take further items from a queue as they finish,
+// because the memory system serves CUs and XCDs unevenly and equal static
+// shares finish far apart.
 //
 // Matrix cores.  Per block the scores are S^T[token][row] = K[token][:] .
 // Q^T[:][row], a 16 x 16 (tokens x rows) tile per column tile: K is the A
@@ -312,21 +316,22 @@ __device__ __forceinline__ void store_out(const AttnArgs& a, int seq, int h, int
 }
 
 // ------------------------------------------------------- partition kernel
+// One (unit, KV head) item: attend over the unit's blocks with the work-group's
+// four waves, merge the waves, then write the output (unsplit sequence) or the
+// partial result, merging the sequence's partials when this is the last of
+// them to arrive.
 template <int KVT, int D, int NT>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NT == 1 ? (KVT == KV_FP8 ? 4 : (KVT == KV_BF16 ? 3 : 1)) : (NT == 2 && KVT != KV_F32 ? 2 : 1))))
-void attn_partition_kernel(AttnArgs a) {
-    extern __shared__ float smem[];
+__device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, const int h, float* smem,
+                                            int* ticket_s, int& claimed, const int tid) {
     const int R = a.rows;
     float* acc_s = smem;                       // [R][D + 1] merged unnormalised output
     float* m_s = smem + R * (D + 1);           // [W][R]
     float* l_s = m_s + kWaves * R;             // [W][R]
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int lg = lane >> 4;                  // lane group: tokens 4*lg .. +3
     const int col = lane & 15;                 // column within a row tile
-    const int unit = blockIdx.x;
-    const int h = blockIdx.y;
     // Unit descriptor (see the plan built by block_table_upload) and, loaded
     // independently of it, this wave's first block ids.
     const int32_t* ud = a.units + static_cast<int64_t>(unit) * kUnitInts;
@@ -343,7 +348,7 @@ void attn_partition_kernel(AttnArgs a) {
     const int G = a.group;
     const int kq = a.k_rows;
 
-    for (int e = threadIdx.x; e < R * (D + 1); e += 64 * kWaves) acc_s[e] = 0.f;
+    for (int e = tid; e < R * (D + 1); e += 64 * kWaves) acc_s[e] = 0.f;
 
     float sscale = a.score_scale;
     float vscale = 1.f;
@@ -454,13 +459,13 @@ void attn_partition_kernel(AttnArgs a) {
                 if constexpr (KVT == KV_FP8) {
                     if (a.append_in_f32)
                         write_token<KVT, KV_F32, D>(blk, a.tile_bytes, t % kBlock, kr, vr, h, 1, ks, vs,
-                                                    threadIdx.x, 64 * kWaves);
+                                                    tid, 64 * kWaves);
                     else
                         write_token<KVT, KV_BF16, D>(blk, a.tile_bytes, t % kBlock, kr, vr, h, 1, ks, vs,
-                                                     threadIdx.x, 64 * kWaves);
+                                                     tid, 64 * kWaves);
                 } else {
                     write_token<KVT, KVT, D>(blk, a.tile_bytes, t % kBlock, kr, vr, h, 1, ks, vs,
-                                             threadIdx.x, 64 * kWaves);
+                                             tid, 64 * kWaves);
                 }
             }
             __builtin_amdgcn_s_waitcnt(0);   // this thread's stores have completed
@@ -501,6 +506,11 @@ void attn_partition_kernel(AttnArgs a) {
         }
         if (i < cnt) process(ta, logical(base + kWaves * i));
     }
+
+    // This work-group's blocks are read: claim its next item now, while the
+    // waves merge, so work-groups that finish early take more items.
+    if (tid == 0 && a.num_items > static_cast<int>(gridDim.x))
+        claimed = __hip_atomic_fetch_add(a.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // Merge the waves: publish (m, l), rescale O to the common max, add in LDS.
 #pragma unroll
@@ -545,7 +555,7 @@ void attn_partition_kernel(AttnArgs a) {
     }
 
     const bool split = parts > 1;
-    for (int e = threadIdx.x; e < R * D; e += 64 * kWaves) {
+    for (int e = tid; e < R * D; e += 64 * kWaves) {
         const int r = e / D;
         const int d = e % D;
         float M = neg_inf();
@@ -574,18 +584,17 @@ void attn_partition_kernel(AttnArgs a) {
     // (for this KV head) to take a ticket combines all partials.  Every thread
     // waits until its partial stores have completed before the work-group
     // takes its ticket; the last one reads the partials only after its ticket.
-    __shared__ int ticket;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int32_t* counter = a.counters + static_cast<int64_t>(seq) * a.num_kv_heads + h;
-    if (threadIdx.x == 0)
-        ticket = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0)
+        *ticket_s = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (ticket != parts - 1) return;
+    if (*ticket_s != parts - 1) return;
     const int64_t sl0 = static_cast<int64_t>(h) * a.num_split_slots + (slot - ud[kUnitPart]);
     float* Mr = m_s;          // [R] reused: the common max of each row
     float* Lr = m_s + R;      // [R] and its sum
-    for (int r = threadIdx.x; r < R; r += 64 * kWaves) {
+    for (int r = tid; r < R; r += 64 * kWaves) {
         float M = neg_inf();
         for (int q = 0; q < parts; ++q) M = fmaxf(M, xwg_load(a.part_m + (sl0 + q) * R + r));
         float L = 0.f;
@@ -595,7 +604,7 @@ void attn_partition_kernel(AttnArgs a) {
         Lr[r] = L;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < R * D; e += 64 * kWaves) {
+    for (int e = tid; e < R * D; e += 64 * kWaves) {
         const int r = e / D;
         const int d = e % D;
         const float M = Mr[r];
@@ -604,8 +613,75 @@ void attn_partition_kernel(AttnArgs a) {
             O += xwg_load(a.part_o + ((sl0 + q) * R + r) * D + d) * fast_exp2(xwg_load(a.part_m + (sl0 + q) * R + r) - M);
         store_out(a, seq, h, r, d, O / Lr[r] * vscale);
     }
-    if (threadIdx.x == 0)   // ready for the next call
+    if (tid == 0)   // ready for the next call
         __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Item i -> (unit, KV head).  Items come in groups of kXcds units x H_kv heads
+// (the last group may hold fewer units); within a group the unit is the
+// fastest index.  Work-groups are handed to the XCDs round-robin by index, so
+// in the first round every head of a unit runs on the same XCD, which then
+// reads the unit's blocks whole (all heads of a block are adjacent) and
+// touches fewer pages.  Units are numbered longest first, and so are groups.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void item_coords(int item, int num_units, int hkv, int& unit, int& h) {
+    const int group = item / (kXcds * hkv);
+    const int r = item - group * kXcds * hkv;
+    const int in_group = min(kXcds, num_units - group * kXcds);
+    h = r / in_group;
+    unit = group * kXcds + (r - h * in_group);
+}
+
+// Persistent work-groups: work-group b first takes item b, then items
+// gridDim.x, gridDim.x + 1, ... in the order they are claimed from the
+// queue, until none is left; a work-group claims its next item when it has
+// read all blocks of the current one.  Items are ordered longest unit first.  Every
+// work-group leaves the loop after exactly one claim past the end; the last
+// to leave sets both queue counters back to zero for the next call.  When the
+// grid has a work-group per item nothing is claimed and the queue is not
+// touched.  No work-group ever waits for another.
+template <int KVT, int D, int NT>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NT == 1 ? (KVT == KV_F32 ? 1 : 3) : (NT == 2 && KVT != KV_F32 ? 2 : 1))))
+void attn_partition_kernel(AttnArgs a) {
+    extern __shared__ float smem[];
+    __shared__ int ticket;
+    __shared__ int next_item;
+    const int wave_s = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    int item = blockIdx.x;
+    while (item < a.num_items) {
+        int claimed = a.num_items;   // thread 0: the next item's place in the queue
+        // The arguments are read afresh from the kernel-argument segment for
+        // every item (the pointer is made opaque to the optimiser), so values
+        // derived from them are not kept live across the whole loop.
+#if defined(__HIP_DEVICE_COMPILE__)
+        typedef const AttnArgs __attribute__((address_space(4)))* KernargPtr;
+        KernargPtr ap = (KernargPtr)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(ap));
+        const AttnArgs ia = *ap;
+#else
+        const AttnArgs ia = a;
+#endif
+        int unit, h;
+        item_coords(item, ia.num_items / ia.num_kv_heads, ia.num_kv_heads, unit, h);
+        // The thread index is made opaque per item as well, so lane-derived
+        // offsets are computed inside the item instead of held (or spilled)
+        // across the whole loop.
+        int tid = wave_s * 64 + static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
+        asm volatile("" : "+v"(tid));
+        attend_item<KVT, D, NT>(ia, unit, h, smem, &ticket, claimed, tid);
+        if (threadIdx.x == 0) next_item = static_cast<int>(gridDim.x) + claimed;
+        __syncthreads();   // next_item visible; this item's LDS reads are done
+        item = next_item;
+    }
+    if (threadIdx.x == 0 && a.num_items > static_cast<int>(gridDim.x)) {
+        // The claim that ended the loop has returned before this add is issued,
+        // so when the last work-group counts itself no claim is outstanding.
+        const int left = __hip_atomic_fetch_add(a.queue + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (left == static_cast<int>(gridDim.x) - 1) {
+            __hip_atomic_store(a.queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.queue + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 // ------------------------------------------------------------ merge kernel
@@ -679,11 +755,31 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int fp8) {
     }
 }
 
+// Work-groups of one instance that fit on the device at once (all CUs).
+template <int KVT, int D, int NT>
+int resident_work_groups() {
+    static int per_cu = 0;   // same for every device of one architecture
+    if (per_cu == 0) {
+        constexpr size_t lds_max = (static_cast<size_t>(16 * NT) * (D + 1) + 2 * kWaves * 16 * NT) * sizeof(float);
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_partition_kernel<KVT, D, NT>, 64 * kWaves,
+                                                         lds_max) != hipSuccess || n < 1)
+            n = 1;
+        per_cu = n;
+    }
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    return per_cu * cus;
+}
+
 template <int KVT, int D, int NT>
 hipError_t launch_instance(const AttnArgs& a, int num_units, hipStream_t stream) {
+    (void)num_units;
     const size_t lds = (static_cast<size_t>(a.rows) * (D + 1) + 2 * kWaves * a.rows) * sizeof(float);
-    dim3 grid(num_units, a.num_kv_heads);
-    hipLaunchKernelGGL((attn_partition_kernel<KVT, D, NT>), grid, dim3(64 * kWaves), lds, stream, a);
+    const int grid = std::min(a.num_items, resident_work_groups<KVT, D, NT>());
+    hipLaunchKernelGGL((attn_partition_kernel<KVT, D, NT>), dim3(grid), dim3(64 * kWaves), lds, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (a.max_parts > a.fuse_max_parts) {

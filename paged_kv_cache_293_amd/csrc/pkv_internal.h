@@ -25,10 +25,21 @@ constexpr int kUnitInts = 8;
 // partition kernel; longer ones by the separate merge kernel.
 constexpr int kFuseMaxParts = 32;
 
-// Balanced plan: about one round of work-groups (kAutoWgsPerCu resident per
-// CU, over all KV heads), with units of kAutoMinBlocks .. kAutoMaxBlocks
-// blocks; large batches are cut into more rounds of at most kAutoMaxBlocks.
+// Balanced plan: units sized so the batch gives up to kAutoItemsPerWg
+// (unit, KV head) items per resident work-group (kAutoWgsPerCu per CU), as
+// many as keep units at kAutoMinItemBlocks blocks or more, with units of
+// kAutoMinBlocks .. kAutoMaxBlocks blocks.  The attention kernel's
+// work-groups take items from a queue, so work-groups that drain early (the
+// memory system does not serve CUs and XCDs evenly) take more of them.
+#ifndef PKV_AUTO_ITEMS_PER_WG
+#define PKV_AUTO_ITEMS_PER_WG 3
+#endif
+#ifndef PKV_AUTO_MIN_ITEM_BLOCKS
+#define PKV_AUTO_MIN_ITEM_BLOCKS 96
+#endif
 constexpr int kAutoWgsPerCu = 3;
+constexpr int kAutoItemsPerWg = PKV_AUTO_ITEMS_PER_WG;
+constexpr int kAutoMinItemBlocks = PKV_AUTO_MIN_ITEM_BLOCKS;
 constexpr int kAutoMinBlocks = 8;
 constexpr int kAutoMaxBlocks = 256;
 
@@ -41,6 +52,7 @@ struct AttnArgs {
     const int32_t* unit_ids;     // [U][unit_stride] physical block ids in walking order
     const int32_t* seq_parts;    // [B][2] = (partitions, first partial slot or -1)
     int32_t* counters;           // [B][H_kv] arrival tickets of the in-kernel merge (zero between calls)
+    int32_t* queue;              // [2] items taken beyond the grid, work-groups finished (zero between calls)
     const void* q;               // [B][k][H_q][D]
     void* out;                   // [B][k][H_q][D]
     const void* k_new;           // fused append: [B][k][H_kv][D] K of positions n-k .. n-1, or null
@@ -59,6 +71,7 @@ struct AttnArgs {
     int32_t rows;                // R = G * k, query rows per KV head
     int32_t k_rows;              // k
     int32_t unit_stride;
+    int32_t num_items;           // units * H_kv; item i is unit i / H_kv, KV head i % H_kv
     int32_t num_split_slots;
     int32_t max_parts;
     int32_t fuse_max_parts;

@@ -127,8 +127,9 @@ def test_block_table_validation_before_any_device_work(pk):
     assert lib.block_table_device_bytes(pool, lp, 0, 3, 32) == 0
     assert lib.block_table_device_bytes(pool, lp, 2, 3, 24) == 0
     assert lib.block_table_device_bytes(None, lp, 2, 3, 32) == 0
-    # table + lens + (parts, slot) + counters + 3 units x 8 ints + ids, each padded to 256 B
-    assert lib.block_table_device_bytes(pool, lp, 2, 3, 32) == 6 * 256
+    # table + lens + (parts, slot) + counters + work queue + 3 units x 8 ints + ids,
+    # each padded to 256 B
+    assert lib.block_table_device_bytes(pool, lp, 2, 3, 32) == 7 * 256
     lib.kv_pool_destroy(pool)
 
 

@@ -216,3 +216,28 @@ def test_repeated_calls_are_deterministic():
     a = out_values(s.run())
     b = out_values(s.run())
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("P", [16, -1])
+def test_work_queue_many_items(P):
+    """Far more (unit, KV head) items than resident work-groups: the
+    work-groups take the rest from the table's queue.  Three calls in a row
+    give bitwise-identical outputs that match the oracle, and leave the
+    table's device buffer (merge tickets, queue counters) exactly as uploaded."""
+    log(f"work queue P={P}")
+    rng = np.random.default_rng(2930)
+    lens = rng.integers(700, 2600, size=48).tolist() + [1, 16, 17]
+    w = workloads.custom(41, lens, num_q_heads=32, num_kv_heads=8, head_dim=128, kv_dtype="bf16",
+                         partition_tokens=P)
+    s = Setup(w)
+    torch.cuda.synchronize()
+    before = s.table.buffer.cpu().numpy().copy()
+    info = s.table.info()
+    log(f"  units {info}")
+    if P == 16:
+        assert info["num_units"] * w.num_kv_heads > 4 * 768
+    outs = [out_values(s.run()) for _ in range(3)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+    after = s.table.buffer.cpu().numpy()
+    assert np.array_equal(before, after), "queue counters or merge tickets not back at zero"
+    assert_close(outs[0], s.oracle(), "bf16", f"queue P={P}")
