@@ -295,6 +295,32 @@ pkv_status paged_attention_append(const pkv_pool* pool, int32_t layer, const pkv
                                   size_t workspace_bytes, void* dev_out, int32_t out_dtype,
                                   void* stream);
 
+/*
+ * Chunked-prefill attention (page "KV cache & continuous batching", section
+ * "3. Chunked prefill": a long prompt is fed in chunks of a few thousand
+ * tokens, each attending over the cache of all earlier positions and over
+ * itself; page "LLM Inference Optimization: KV Cache, Batching, and
+ * Speculative Decoding", section "Prefill Optimization").  Every sequence
+ * carries chunk_tokens (= C) query tokens at positions n-C .. n-1 (n =
+ * seq_len[s]) whose K/V were appended beforehand (reshape_and_cache); row j
+ * attends causally to positions t <= n - C + j:
+ *   out[s][j][g] = softmax( scale * q[s][j][g] . K_s[t][h]^T, t <= n-C+j ) V_s[t][h],
+ *   h = g / (num_q_heads / num_kv_heads).
+ * It is the computation of paged_attention_verify with C rows, for any C:
+ * the kernel keeps each work-group's 256 query rows resident and streams the
+ * visible K/V blocks through LDS, bound by the matrix cores.
+ *   dev_q    [num_seqs][C][num_q_heads][head_dim] bfloat16.
+ *   dev_out  [num_seqs][C][num_q_heads][head_dim], out_dtype PKV_BF16 or PKV_F32.
+ *   Pools: PKV_BF16 or PKV_FP8_E4M3 (PKV_F32 pools: PKV_ERR_UNSUPPORTED).
+ * No workspace.  The table's split-KV plan is not used (any partition_tokens).
+ * Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_SEQ_LEN (a sequence
+ * shorter than C), PKV_ERR_BLOCK_RANGE, PKV_ERR_HIP.
+ */
+pkv_status paged_attention_prefill(const pkv_pool* pool, int32_t layer, const pkv_table* table,
+                                   const void* dev_q, int32_t q_dtype, int32_t chunk_tokens,
+                                   int32_t num_q_heads, float scale, void* dev_out, int32_t out_dtype,
+                                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -98,3 +98,37 @@ def decode(desc, pool_u8, layer, block_tables, seq_lens, q, scale,
     q = np.asarray(q, dtype=np.float64)
     return verify(desc, pool_u8, layer, block_tables, seq_lens, q[:, None], 1, scale,
                   k_scale, v_scale, seqs)[:, 0]
+
+
+def prefill(desc, pool_u8, layer, block_tables, seq_lens, q, chunk, scale,
+            k_scale=None, v_scale=None, seqs=None, rows=None):
+    """Chunked-prefill attention (page "KV cache & continuous batching",
+    section "3. Chunked prefill": a prompt is fed in chunks, each attending
+    over the cache of all earlier positions and over itself).
+
+    q: [B][C][H_q][d] for the C = chunk tokens of each sequence, at positions
+    n_s - C .. n_s - 1 with their K/V already in the pool; row j sees
+    positions t <= n_s - C + j.  That is the k-row computation of ``verify``
+    with k = C.  ``rows`` (chunk indices) limits the work to those rows of the
+    selected sequences; the others are left zero.
+    """
+    if rows is None:
+        return verify(desc, pool_u8, layer, block_tables, seq_lens, q, chunk, scale,
+                      k_scale, v_scale, seqs)
+    q = np.asarray(q, dtype=np.float64)
+    B, C, Hq, d = q.shape
+    assert C == chunk
+    Hkv = desc.num_kv_heads
+    G = Hq // Hkv
+    out = np.zeros_like(q)
+    rows = [int(j) for j in rows]
+    for s in (range(B) if seqs is None else seqs):
+        n = int(seq_lens[s])
+        if n < C:
+            raise ValueError("sequence shorter than its chunk")
+        visible = [n - C + j + 1 for j in rows]
+        for h in range(Hkv):
+            K, V = gather_kv(desc, pool_u8, layer, block_tables[s], n, h, k_scale, v_scale)
+            for g in range(h * G, (h + 1) * G):
+                out[s, rows, g, :] = softmax_attention(q[s, rows, g, :], K, V, scale, visible)
+    return out

@@ -53,6 +53,8 @@ PROTOTYPES = {
                                           ctypes.c_float, _vp, _c_size, _vp, _c_int32, _vp]),
     "paged_attention_append": (_c_int32, [_vp, _c_int32, _vp, _vp, _vp, _c_int32, _vp, _c_int32, _c_int32,
                                           _c_int32, ctypes.c_float, _vp, _c_size, _vp, _c_int32, _vp]),
+    "paged_attention_prefill": (_c_int32, [_vp, _c_int32, _vp, _vp, _c_int32, _c_int32, _c_int32, ctypes.c_float,
+                                           _vp, _c_int32, _vp]),
 }
 
 

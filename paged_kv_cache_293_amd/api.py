@@ -233,3 +233,25 @@ def paged_attention_append(pool, layer, table, k_new, v_new, q, scale=None, work
         _ptr(q), _TORCH_CODE[q.dtype], int(k), Hq, scale, _ptr(workspace), ws_bytes, _ptr(out),
         _TORCH_CODE[out.dtype], _stream(q.device)))
     return out
+
+
+def paged_attention_prefill(pool, layer, table, q, scale=None, out=None, out_dtype=None):
+    """Chunked-prefill attention: q [B][C][H_q][d] bf16 -> out [B][C][H_q][d].
+
+    Row j of sequence s is position seq_len[s] - C + j (its K/V already
+    appended) and sees positions t <= seq_len[s] - C + j.
+    """
+    assert q.dim() == 4 and q.shape[0] == table.num_seqs
+    assert q.is_cuda and q.is_contiguous() and q.dtype == torch.bfloat16
+    C, Hq = q.shape[1], q.shape[2]
+    if out_dtype is None:
+        out_dtype = torch.bfloat16
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    assert out.shape == q.shape and out.is_contiguous() and out.dtype in _TORCH_CODE
+    if scale is None:
+        scale = 1.0 / math.sqrt(pool.head_dim)
+    _check("paged_attention_prefill", lib.paged_attention_prefill(
+        pool.handle, int(layer), table.handle, _ptr(q), BF16, int(C), int(Hq), float(scale),
+        _ptr(out), _TORCH_CODE[out.dtype], _stream(q.device)))
+    return out

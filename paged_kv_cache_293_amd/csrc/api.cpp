@@ -561,6 +561,47 @@ pkv_status paged_attention_append(const pkv_pool* pool, int32_t layer, const pkv
                           num_q_heads, scale, dev_workspace, workspace_bytes, dev_out, out_dtype, stream);
 }
 
+pkv_status paged_attention_prefill(const pkv_pool* pool, int32_t layer, const pkv_table* table, const void* dev_q,
+                                   int32_t q_dtype, int32_t chunk_tokens, int32_t num_q_heads, float scale,
+                                   void* dev_out, int32_t out_dtype, void* stream) {
+    if (!pool || !table || !dev_q || !dev_out) return PKV_ERR_INVALID;
+    if (layer < 0 || layer >= pool->desc.num_layers) return PKV_ERR_INVALID;
+    if (chunk_tokens < 1 || num_q_heads < 1 || !std::isfinite(scale)) return PKV_ERR_INVALID;
+    const int32_t hkv = pool->desc.num_kv_heads;
+    if (num_q_heads % hkv || table->num_kv_heads != hkv) return PKV_ERR_INVALID;
+    const int32_t kv = pool->desc.kv_dtype;
+    if (kv != PKV_BF16 && kv != PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+    if (q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (table->min_seq_len < chunk_tokens) return PKV_ERR_SEQ_LEN;
+    if (table->max_block_id >= pool->desc.num_blocks) return PKV_ERR_BLOCK_RANGE;
+    const int64_t rows = static_cast<int64_t>(chunk_tokens) * (num_q_heads / hkv);
+    const int64_t tiles = (rows + pkv::kPrefillRows - 1) / pkv::kPrefillRows;
+    if (tiles * table->num_seqs * hkv > INT32_MAX) return PKV_ERR_UNSUPPORTED;
+    pkv::PrefillArgs a;
+    a.pool = pool->base;
+    a.k_scale = pool->k_scale;
+    a.v_scale = pool->v_scale;
+    a.table = table->d_table;
+    a.seq_lens = table->d_seq_lens;
+    a.q = dev_q;
+    a.out = dev_out;
+    a.tile_bytes = pool->tile_bytes;
+    a.layer = layer;
+    a.num_blocks = pool->desc.num_blocks;
+    a.num_seqs = table->num_seqs;
+    a.num_kv_heads = hkv;
+    a.num_q_heads = num_q_heads;
+    a.group = num_q_heads / hkv;
+    a.chunk = chunk_tokens;
+    a.max_blocks = table->max_blocks;
+    a.row_tiles = static_cast<int32_t>(tiles);
+    a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
+    a.score_scale = scale * 1.4426950408889634f;
+    const int32_t kvt = kv == PKV_BF16 ? 1 : 2;
+    return hip_status(pkv::launch_prefill(a, kvt, pool->desc.head_dim, static_cast<hipStream_t>(stream)));
+}
+
 pkv_status paged_attention_decode(const pkv_pool* pool, int32_t layer, const pkv_table* table, const void* dev_q,
                                   int32_t q_dtype, int32_t num_q_heads, float scale, void* dev_workspace,
                                   size_t workspace_bytes, void* dev_out, int32_t out_dtype, void* stream) {

@@ -38,214 +38,12 @@
 //   fp8 : codes converted to bf16 in registers (exact), then as bf16; the K
 //         scale folds into the score scale, the V scale into the final divide;
 //   f32 : v_mfma_f32_16x16x4_f32 for both products, probabilities in f32.
-#include "pkv_device.h"
+#include "pkv_mfma.h"
 
 namespace pkv {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kWaves = 4;
-
-__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// float -> bfloat16 bits, round to nearest even (the gfx950 converter).
-__device__ __forceinline__ unsigned f32_to_bf16_rne(float f) {
-    return __builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
-}
-
-// Two floats -> two bf16 (round to nearest even) packed low/high.
-__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
-}
-
-// Buffer resource over one block's K tile followed by its V tile.  Loads
-// through it address the tile with a per-lane 32-bit offset plus an immediate,
-// and read 0 beyond the two tiles.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int64_t tile_bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0,
-                                             static_cast<int>(2 * tile_bytes), 0x00020000);
-}
-
-// Partial results pass between work-groups of one launch, which may run on
-// different XCDs with separate L2 caches: they are written and read with
-// agent-scope accesses, which the hardware keeps coherent across the device.
-__device__ __forceinline__ void xwg_store(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float xwg_load(const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-template <typename T>
-__device__ __forceinline__ T bload(__amdgpu_buffer_rsrc_t r, int voff, int imm) {
-    if constexpr (sizeof(T) == 16) return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, voff, imm, 0));
-    else if constexpr (sizeof(T) == 8) return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, voff, imm, 0));
-    else return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, imm, 0));
-}
-
-// Two fp8 E4M3 codes (bytes 0-1, or 2-3 when HI, of w) -> two bf16 values packed in one
-// dword.  The hardware conversion yields exact float32 values; their upper
-// halves are the exact bf16 values (E4M3 has 3 mantissa bits).
-template <bool HI>
-__device__ __forceinline__ unsigned fp8x2_to_bf16x2(unsigned w) {
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HI);
-    return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
-}
-
-// ------------------------------------------------------------------ tiles
-// Per-lane registers of one block's K and V tiles, and their loads.
-template <int KVT, int D> struct TileRegs;
-
-template <int D> struct TileRegs<KV_BF16, D> {
-    u32x4 k[D / 32];   // 8 bf16: token lane%16, dims of chunk 4s + lane/16
-    u32x2 v[D / 16];   // 4 bf16: dim 16m + lane%16, tokens 4*(lane/16) .. +3
-    // koff = lane * 16; voff = TILE + (lane % 16) * 32 + (lane / 16) * 8
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int koff, int voff) {
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s) k[s] = bload<u32x4>(r, koff, 1024 * s);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < D / 16; ++m) v[m] = bload<u32x2>(r, voff, 512 * m);
-    }
-    static constexpr int kTile = 16 * D * 2;
-    __device__ static int v_offset(int lane) { return kTile + (lane & 15) * 32 + (lane >> 4) * 8; }
-    // zero V of tokens >= nvalid among this lane's four (tokens 4j .. 4j+3)
-    __device__ __forceinline__ void zero_v_from(int nvalid) {
-        if (nvalid >= 4) return;
-        const unsigned m0 = nvalid <= 0 ? 0u : (nvalid == 1 ? 0x0000ffffu : 0xffffffffu);
-        const unsigned m1 = nvalid <= 2 ? 0u : 0x0000ffffu;
-#pragma unroll
-        for (int m = 0; m < D / 16; ++m) { v[m][0] &= m0; v[m][1] &= m1; }
-    }
-};
-
-template <int D> struct TileRegs<KV_FP8, D> {
-    u32x4 k[D / 64];   // 16 codes: token lane%16, dims of chunk 4r + lane/16
-    unsigned v[D / 16];  // 4 codes: dim 16m + lane%16, tokens 4*(lane/16) .. +3
-    // koff = lane * 16; voff = TILE + (lane % 16) * 16 + (lane / 16) * 4
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int koff, int voff) {
-#pragma unroll
-        for (int q = 0; q < D / 64; ++q) k[q] = bload<u32x4>(r, koff, 1024 * q);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < D / 16; ++m) v[m] = bload<unsigned>(r, voff, 256 * m);
-    }
-    static constexpr int kTile = 16 * D;
-    __device__ static int v_offset(int lane) { return kTile + (lane & 15) * 16 + (lane >> 4) * 4; }
-    __device__ __forceinline__ void zero_v_from(int nvalid) {
-        if (nvalid >= 4) return;
-        const unsigned msk = nvalid <= 0 ? 0u : (0xffffffffu >> (8 * (4 - nvalid)));
-#pragma unroll
-        for (int m = 0; m < D / 16; ++m) v[m] &= msk;
-    }
-};
-
-template <int D> struct TileRegs<KV_F32, D> {
-    f32x4 k[D / 16];   // 4 f32: token lane%16, dims of chunk 4r + lane/16
-    f32x4 v[D / 16];   // 4 f32: dim 16m + lane%16, tokens 4*(lane/16) .. +3
-    // koff = lane * 16; voff = TILE + (lane % 16) * 64 + (lane / 16) * 16
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int koff, int voff) {
-#pragma unroll
-        for (int q = 0; q < D / 16; ++q) k[q] = bload<f32x4>(r, koff, 1024 * q);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < D / 16; ++m) v[m] = bload<f32x4>(r, voff, 1024 * m);
-    }
-    static constexpr int kTile = 16 * D * 4;
-    __device__ static int v_offset(int lane) { return kTile + (lane & 15) * 64 + (lane >> 4) * 16; }
-    __device__ __forceinline__ void zero_v_from(int nvalid) {
-        if (nvalid >= 4) return;
-#pragma unroll
-        for (int m = 0; m < D / 16; ++m)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (e >= nvalid) v[m][e] = 0.f;
-    }
-};
-
-// ---------------------------------------------------------- query operand
-// B operand of the score MFMA for column tile t: query row 16t + lane%16,
-// dims matching the K chunk each lane group holds.
-template <int KVT, int D> struct QRegs;
-
-template <int D> struct QRegs<KV_BF16, D> {
-    bf16x8 q[D / 32];   // step s: dims (4s + lane/16) * 8 .. +8
-    __device__ __forceinline__ void load(const uint16_t* row, bool valid, int lane) {
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-            u32x4 w = valid ? *reinterpret_cast<const u32x4*>(row + (4 * s + (lane >> 4)) * 8)
-                            : u32x4{0u, 0u, 0u, 0u};
-            q[s] = __builtin_bit_cast(bf16x8, w);
-        }
-    }
-};
-
-template <int D> struct QRegs<KV_FP8, D> {
-    bf16x8 q[D / 32];   // step 2r + hh: dims (4r + lane/16) * 16 + 8 hh .. +8
-    __device__ __forceinline__ void load(const uint16_t* row, bool valid, int lane) {
-#pragma unroll
-        for (int st = 0; st < D / 32; ++st) {
-            const int dim0 = (4 * (st >> 1) + (lane >> 4)) * 16 + 8 * (st & 1);
-            u32x4 w = valid ? *reinterpret_cast<const u32x4*>(row + dim0) : u32x4{0u, 0u, 0u, 0u};
-            q[st] = __builtin_bit_cast(bf16x8, w);
-        }
-    }
-};
-
-template <int D> struct QRegs<KV_F32, D> {
-    f32x4 q[D / 16];    // r: dims (4r + lane/16) * 4 .. +4, one MFMA per element
-    __device__ __forceinline__ void load(const float* row, bool valid, int lane) {
-#pragma unroll
-        for (int r = 0; r < D / 16; ++r)
-            q[r] = valid ? *reinterpret_cast<const f32x4*>(row + (4 * r + (lane >> 4)) * 4)
-                         : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-};
-
-// S^T tile (tokens x rows) of one block for one column tile.
-template <int D>
-__device__ __forceinline__ f32x4 scores(const TileRegs<KV_BF16, D>& t, const QRegs<KV_BF16, D>& q) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[s]), q.q[s], acc, 0, 0, 0);
-    return acc;
-}
-
-template <int D>
-__device__ __forceinline__ f32x4 scores(const TileRegs<KV_FP8, D>& t, const QRegs<KV_FP8, D>& q) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < D / 64; ++r) {
-        const u32x4 w = t.k[r];
-        u32x4 lo = {fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]),
-                    fp8x2_to_bf16x2<false>(w[1]), fp8x2_to_bf16x2<true>(w[1])};
-        u32x4 hi = {fp8x2_to_bf16x2<false>(w[2]), fp8x2_to_bf16x2<true>(w[2]),
-                    fp8x2_to_bf16x2<false>(w[3]), fp8x2_to_bf16x2<true>(w[3])};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo), q.q[2 * r], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi), q.q[2 * r + 1], acc, 0, 0, 0);
-    }
-    return acc;
-}
-
-template <int D>
-__device__ __forceinline__ f32x4 scores(const TileRegs<KV_F32, D>& t, const QRegs<KV_F32, D>& q) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < D / 16; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(t.k[r][e], q.q[r][e], acc, 0, 0, 0);
-    return acc;
-}
 
 // O^T[dim tile m] += V^T tile . P^T for one column tile; p holds this lane's
 // probabilities of tokens 4*(lane/16) .. +3.

@@ -85,6 +85,37 @@ struct AttnArgs {
 hipError_t launch_attention(const AttnArgs& a, int kv_dtype, int head_dim, int num_units,
                             hipStream_t stream);
 
+// Chunked-prefill attention: every sequence carries `chunk` query tokens at
+// positions n-chunk .. n-1 (their K/V already in the pool); row (j, g) sees
+// positions t <= n - chunk + j.  One work-group per (sequence, KV head, tile
+// of kPrefillRows query rows).
+constexpr int kPrefillRows = 256;
+
+struct PrefillArgs {
+    const uint8_t* pool;
+    const float* k_scale;        // [L][H_kv] (fp8 pools) or null
+    const float* v_scale;
+    const int32_t* table;        // [B][max_blocks] block table (validated at upload)
+    const int32_t* seq_lens;     // [B]
+    const void* q;               // [B][chunk][H_q][D] bfloat16
+    void* out;                   // [B][chunk][H_q][D]
+    int64_t tile_bytes;
+    int32_t layer;
+    int32_t num_blocks;
+    int32_t num_seqs;
+    int32_t num_kv_heads;
+    int32_t num_q_heads;
+    int32_t group;               // G = H_q / H_kv
+    int32_t chunk;               // query tokens per sequence
+    int32_t max_blocks;          // table row stride
+    int32_t row_tiles;           // ceil(chunk * G / kPrefillRows)
+    int32_t out_bf16;
+    float score_scale;           // softmax scale * log2(e)
+};
+
+// Launch the prefill kernel; kv_dtype is KV_BF16 or KV_FP8, head_dim 64 or 128.
+hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, hipStream_t stream);
+
 struct CacheArgs {
     uint8_t* pool;
     const float* k_scale;

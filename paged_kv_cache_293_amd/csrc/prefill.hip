@@ -1,0 +1,347 @@
+// Chunked-prefill paged attention for gfx950.
+//
+// Method (page "KV cache & continuous batching", section "3. Chunked
+// prefill": a long prompt is processed in chunks of a few thousand tokens,
+// each chunk attending over the cached K/V of everything before it and over
+// itself; sections "The core insight" and "2. PagedAttention (vLLM)" for the
+// cache and the gather through the block table; page "LLM Inference
+// Optimization: KV Cache, Batching, and Speculative Decoding", section
+// "Prefill Optimization": prefill is a compute-bound matrix product):
+//   row (j, g) of sequence s is chunk token j (position n - C + j) for query
+//   head h*G + g; out = softmax(scale * q . K[t]^T over t <= n - C + j) V[t],
+//   with K, V of KV head h read through the block table.  It is the verify
+//   computation with C rows, at sizes where the matrix cores bound it.
+//
+// Work decomposition.  One work-group of 4 waves per (sequence, KV head,
+// tile of 256 query rows); rows are ordered (token, head of the group), so
+// the G heads of one token sit side by side.  Each wave owns 64 rows as four
+// 16-row column tiles, with their queries resident in registers.  The K/V of
+// the visible blocks stream through a three-stage LDS ring, two blocks (a
+// "pair") per stage, copied straight from the pool into LDS by
+// global_load_lds_dwordx4 (no register staging); each wave issues its share
+// of the pair two steps ahead, and one barrier per pair publishes it.
+//
+// Matrix cores.  Scores: S^T[token][row] = K[token][:] . Q^T[:][row] with
+// v_mfma_f32_16x16x32_bf16 per block (K is the A operand, one 16-byte LDS
+// read per lane, as in the decode kernel).  Output: O^T[dim][row] +=
+// V^T[dim][32 tokens] . P^T[32 tokens][row] with one v_mfma_f32_16x16x32_bf16
+// per 16 dims over the pair: lane group lg supplies tokens 4lg..4lg+3 of
+// each block of the pair (its 4 + 4 probabilities straight from the two score
+// tiles, and the matching 8-byte V^T reads), so the contraction runs at the
+// full-rate 32-deep instruction.  fp8 codes are converted to bf16 exactly
+// after the LDS read; the K scale folds into the score scale, the V scale
+// into the final divide.
+//
+// Work-group order: groups of 8 (sequence, KV head) pairs x all row tiles,
+// the pair fastest; work-groups go to the 8 XCDs round-robin, so each XCD
+// serves one pair's row tiles and its L2 holds that pair's K/V for all of
+// them.  Row tiles go longest (most visible tokens) first.
+#include "pkv_mfma.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kPfWaves = 4;
+constexpr int kPfNT = kPrefillRows / (16 * kPfWaves);   // column tiles per wave (4)
+constexpr int kPfStages = 3;
+constexpr int kPfIdWindow = 2048;                       // block ids held in LDS at a time
+constexpr int kPfXcds = 8;
+
+template <int KVT, int D> struct PfGeom {
+    static constexpr int EB = KVT == KV_FP8 ? 1 : 2;
+    static constexpr int TILE = 16 * D * EB;               // one K or V tile
+    static constexpr int PAIR = 4 * TILE;                  // K_A, V_A, K_B, V_B
+    static constexpr int LOADS = PAIR / 1024 / kPfWaves;   // 1 KiB wave loads per wave per pair
+    static_assert(LOADS >= 1, "a pair must give every wave at least one load");
+    static constexpr int LDS = kPfStages * PAIR + 4 * kPfIdWindow;
+};
+
+// s_waitcnt immediate: vector-memory count <= N, no wait on the other counters.
+template <int N> constexpr int vmcnt_imm() { return (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14); }
+
+// Copy one pair (blocks id_a, id_b) of this KV head into an LDS stage: this
+// wave's share of the 1 KiB pieces, 16 bytes per lane, straight into LDS.
+template <int KVT, int D>
+__device__ __forceinline__ void pf_issue(const uint8_t* head_base, int64_t block_stride, int id_a, int id_b,
+                                         uint8_t* stage, int wave, int lane) {
+    using Gm = PfGeom<KVT, D>;
+    constexpr int PER_TILE = Gm::TILE / 1024;
+#pragma unroll
+    for (int k = 0; k < Gm::LOADS; ++k) {
+        const int gk = wave + kPfWaves * k;
+        const int tile = gk / PER_TILE;                 // 0 K_A, 1 V_A, 2 K_B, 3 V_B
+        const int off = (gk % PER_TILE) * 1024;
+        const int id = tile < 2 ? id_a : id_b;
+        const uint8_t* src = head_base + static_cast<int64_t>(id) * block_stride + (tile & 1) * Gm::TILE + off +
+                             lane * 16;
+        __builtin_amdgcn_global_load_lds(src, stage + tile * Gm::TILE + off, 16, 0, 0);
+    }
+}
+
+// K operand registers of one block from its LDS tile (same per-lane reads as
+// the decode kernel's buffer loads: token lane % 16, 16-byte chunk).
+template <int KVT, int D>
+__device__ __forceinline__ void pf_k_regs(TileRegs<KVT, D>& t, const uint8_t* tile, int lane) {
+    if constexpr (KVT == KV_BF16) {
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) t.k[s] = *reinterpret_cast<const u32x4*>(tile + lane * 16 + 1024 * s);
+    } else {
+#pragma unroll
+        for (int q = 0; q < D / 64; ++q) t.k[q] = *reinterpret_cast<const u32x4*>(tile + lane * 16 + 1024 * q);
+    }
+}
+
+// V^T operand of dims 16m .. 16m+15 over the pair: this lane's dim 16m +
+// lane % 16, tokens 4lg .. 4lg+3 of block A then of block B, as 8 bf16.
+template <int KVT, int D>
+__device__ __forceinline__ u32x4 pf_v_op(const uint8_t* va, const uint8_t* vb, int m, int col, int lg) {
+    if constexpr (KVT == KV_BF16) {
+        const int off = (16 * m + col) * 32 + lg * 8;
+        const u32x2 x = *reinterpret_cast<const u32x2*>(va + off);
+        const u32x2 y = *reinterpret_cast<const u32x2*>(vb + off);
+        return u32x4{x[0], x[1], y[0], y[1]};
+    } else {
+        const int off = (16 * m + col) * 16 + lg * 4;
+        const unsigned x = *reinterpret_cast<const unsigned*>(va + off);
+        const unsigned y = *reinterpret_cast<const unsigned*>(vb + off);
+        return u32x4{fp8x2_to_bf16x2<false>(x), fp8x2_to_bf16x2<true>(x), fp8x2_to_bf16x2<false>(y),
+                     fp8x2_to_bf16x2<true>(y)};
+    }
+}
+
+// Zero the bf16 values of an operand built by pf_v_op whose tokens are >= n
+// (tokens t0 + 4lg + e of block A, t0 + 16 + 4lg + e of block B).
+__device__ __forceinline__ u32x4 pf_zero_tail(u32x4 v, int t0, int lg, int n) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int first = t0 + 16 * half + 4 * lg;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            unsigned keep = 0;
+            if (first + 2 * w < n) keep |= 0x0000ffffu;
+            if (first + 2 * w + 1 < n) keep |= 0xffff0000u;
+            v[2 * half + w] &= keep;
+        }
+    }
+    return v;
+}
+
+__device__ __forceinline__ float bf16_round(float p) { return __uint_as_float(f32_to_bf16_rne(p) << 16); }
+
+template <int KVT, int D>
+__global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_prefill_kernel(PrefillArgs a) {
+    using Gm = PfGeom<KVT, D>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t pf_smem[];
+    int32_t* ids = reinterpret_cast<int32_t*>(pf_smem + kPfStages * Gm::PAIR);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lg = lane >> 4;
+    const int col = lane & 15;
+
+    // Work-group -> (sequence, KV head, row tile).
+    const int H = a.num_kv_heads;
+    const int RT = a.row_tiles;
+    const int pairs_sh = a.num_seqs * H;
+    const int grp = blockIdx.x / (kPfXcds * RT);
+    const int r = blockIdx.x - grp * kPfXcds * RT;
+    const int in_group = min(kPfXcds, pairs_sh - grp * kPfXcds);
+    const int sh = grp * kPfXcds + r % in_group;
+    const int rt = RT - 1 - r / in_group;
+    const int s = sh / H;
+    const int h = sh - s * H;
+
+    const int n = a.seq_lens[s];
+    const int C = a.chunk;
+    const int G = a.group;
+    const int Rt = C * G;                       // query rows of this (sequence, KV head)
+    const int first = n - C;                    // position of chunk token 0
+    const int row_wg = rt * kPrefillRows;
+    const int last_row = min(Rt, row_wg + kPrefillRows) - 1;
+    const int nblk = (first + last_row / G + kBlock) / kBlock;   // blocks the tile's last row sees
+    const int npair = (nblk + 1) >> 1;
+    const int row_w = row_wg + wave * 16 * kPfNT;
+    const int lim_lo = row_w < Rt ? first + row_w / G + 1 : 0;  // fewest positions a row of this wave sees
+
+    float sscale = a.score_scale;
+    float vscale = 1.f;
+    if constexpr (KVT == KV_FP8) {
+        sscale *= a.k_scale[a.layer * H + h];
+        vscale = a.v_scale[a.layer * H + h];
+    }
+
+    QRegs<KVT, D> qr[kPfNT];
+    int lim[kPfNT];
+#pragma unroll
+    for (int c = 0; c < kPfNT; ++c) {
+        const int row = row_w + 16 * c + col;
+        const bool valid = row < Rt;
+        const int j = valid ? row / G : 0;
+        const int g = valid ? row - (row / G) * G : 0;
+        const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) +
+            ((static_cast<int64_t>(s) * C + j) * a.num_q_heads + h * G + g) * D;
+        qr[c].load(qrow, valid, lane);
+        lim[c] = valid ? first + j + 1 : 0;
+    }
+
+    f32x4 o[kPfNT][D / 16];
+    float m_run[kPfNT], l_run[kPfNT];
+#pragma unroll
+    for (int c = 0; c < kPfNT; ++c) {
+        m_run[c] = neg_inf();
+        l_run[c] = 0.f;
+#pragma unroll
+        for (int m = 0; m < D / 16; ++m) o[c][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int64_t block_stride = static_cast<int64_t>(H) * 2 * a.tile_bytes;
+    const uint8_t* head_base = a.pool + static_cast<int64_t>(a.layer) * a.num_blocks * block_stride +
+                               static_cast<int64_t>(h) * 2 * a.tile_bytes;
+    const int32_t* trow = a.table + static_cast<int64_t>(s) * a.max_blocks;
+
+    // The tile's block ids, a window of them at a time, in LDS.
+    int win_lo = 0;
+    auto load_window = [&](int lo) {
+        const int cnt = min(kPfIdWindow, nblk - lo);
+        for (int e = tid; e < cnt; e += 64 * kPfWaves) ids[e] = trow[lo + e];
+        win_lo = lo;
+    };
+    auto issue = [&](int q) {
+        const int b = 2 * q - win_lo;
+        const int ia = __builtin_amdgcn_readfirstlane(ids[b]);
+        const int ib = 2 * q + 1 < nblk ? __builtin_amdgcn_readfirstlane(ids[b + 1]) : ia;
+        pf_issue<KVT, D>(head_base, block_stride, ia, ib, pf_smem + (q % kPfStages) * Gm::PAIR, wave, lane);
+    };
+    load_window(0);
+    __syncthreads();
+    issue(0);
+    if (npair > 1) issue(1);
+
+    for (int p = 0; p < npair; ++p) {
+        // This wave's pieces of pair p have landed (pair p+1 may still be in
+        // flight); the barrier makes every wave's pieces visible and ensures
+        // pair p-1's stage is no longer read.
+        if (p + 1 < npair) __builtin_amdgcn_s_waitcnt(vmcnt_imm<Gm::LOADS>());
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+        __builtin_amdgcn_s_barrier();
+        if (p + 2 < npair) {
+            const int q = p + 2;
+            if (min(2 * q + 1, nblk - 1) >= win_lo + kPfIdWindow) {
+                // next window of ids: drain, swap, publish (once per 2048 blocks)
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+                __builtin_amdgcn_s_barrier();
+                load_window(2 * q);
+                __syncthreads();
+            }
+            issue(q);
+        }
+
+        const uint8_t* st = pf_smem + (p % kPfStages) * Gm::PAIR;
+        const int t0 = 32 * p;
+        TileRegs<KVT, D> ka, kb;
+        pf_k_regs<KVT, D>(ka, st, lane);
+        pf_k_regs<KVT, D>(kb, st + 2 * Gm::TILE, lane);
+        const bool need_mask = t0 + 32 > lim_lo;
+        u32x4 pop[kPfNT];
+        float alpha[kPfNT];
+        bool rescale = false;
+#pragma unroll
+        for (int c = 0; c < kPfNT; ++c) {
+            f32x4 sa = scores<D>(ka, qr[c]);
+            f32x4 sb = scores<D>(kb, qr[c]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sa[i] *= sscale;
+                sb[i] *= sscale;
+            }
+            if (need_mask) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (t0 + 4 * lg + i >= lim[c]) sa[i] = neg_inf();
+                    if (t0 + 16 + 4 * lg + i >= lim[c]) sb[i] = neg_inf();
+                }
+            }
+            float mx = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
+                             fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mnew = fmaxf(m_run[c], mx);
+            const float muse = (mnew == neg_inf()) ? 0.f : mnew;
+            alpha[c] = fast_exp2(m_run[c] - muse);
+            float pa[4], pb[4];
+            float psum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pa[i] = fast_exp2(sa[i] - muse);
+                pb[i] = fast_exp2(sb[i] - muse);
+                psum += bf16_round(pa[i]) + bf16_round(pb[i]);
+            }
+            l_run[c] = l_run[c] * alpha[c] + psum;
+            m_run[c] = mnew;
+            rescale |= alpha[c] != 1.f;
+            pop[c] = u32x4{pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3]), pack_bf16x2(pb[0], pb[1]),
+                           pack_bf16x2(pb[2], pb[3])};
+        }
+        if (__ballot(rescale)) {
+#pragma unroll
+            for (int c = 0; c < kPfNT; ++c)
+#pragma unroll
+                for (int m = 0; m < D / 16; ++m) o[c][m] *= alpha[c];
+        }
+        const bool tail = t0 + 32 > n;
+        const uint8_t* va = st + Gm::TILE;
+        const uint8_t* vb = st + 3 * Gm::TILE;
+#pragma unroll
+        for (int m = 0; m < D / 16; ++m) {
+            u32x4 v = pf_v_op<KVT, D>(va, vb, m, col, lg);
+            if (tail) v = pf_zero_tail(v, t0, lg, n);
+            const bf16x8 av = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+            for (int c = 0; c < kPfNT; ++c)
+                o[c][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, pop[c]), o[c][m],
+                                                                  0, 0, 0);
+        }
+    }
+
+    // Normalise and store: lane holds dims 16m + 4lg .. +3 of row 16c + col.
+#pragma unroll
+    for (int c = 0; c < kPfNT; ++c) {
+        float l = l_run[c];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        const int row = row_w + 16 * c + col;
+        if (row >= Rt) continue;
+        const int j = row / G;
+        const int g = row - j * G;
+        const float inv = vscale / l;
+        const int64_t base = ((static_cast<int64_t>(s) * C + j) * a.num_q_heads + h * G + g) * D + 4 * lg;
+#pragma unroll
+        for (int m = 0; m < D / 16; ++m) {
+            const f32x4 v = o[c][m] * inv;
+            if (a.out_bf16) {
+                *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + base + 16 * m) =
+                    u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            } else {
+                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + base + 16 * m) = v;
+            }
+        }
+    }
+}
+
+template <int KVT, int D>
+hipError_t launch_pf(const PrefillArgs& a, hipStream_t stream) {
+    const int grid = a.num_seqs * a.num_kv_heads * a.row_tiles;
+    constexpr size_t lds = PfGeom<KVT, D>::LDS;
+    hipLaunchKernelGGL((attn_prefill_kernel<KVT, D>), dim3(grid), dim3(64 * kPfWaves), lds, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, hipStream_t stream) {
+    if (kv_dtype == KV_BF16) return head_dim == 128 ? launch_pf<KV_BF16, 128>(a, stream) : launch_pf<KV_BF16, 64>(a, stream);
+    return head_dim == 128 ? launch_pf<KV_FP8, 128>(a, stream) : launch_pf<KV_FP8, 64>(a, stream);
+}
+
+}  // namespace pkv

@@ -145,6 +145,21 @@ class Setup:
         torch.cuda.synchronize()
         return out
 
+    def run_prefill(self, out_dtype=None, scale=None):
+        w = self.w
+        scale = w.scale if scale is None else scale
+        od = None if out_dtype is None else {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+        out = self.pk.paged_attention_prefill(self.pool, w.layer, self.table, self.q, scale, out_dtype=od)
+        torch.cuda.synchronize()
+        return out
+
+    def oracle_prefill(self, seqs=None, rows=None, scale=None):
+        w = self.w
+        scale = w.scale if scale is None else scale
+        q = q_values(w.q, w.q_dtype)
+        return oatt.prefill(self.desc, self.oracle_image(), w.layer, w.block_tables, w.seq_lens, q,
+                            w.k_rows, scale, self.k_scale, self.v_scale, seqs=seqs, rows=rows)
+
     def oracle(self, seqs=None, scale=None):
         w = self.w
         scale = w.scale if scale is None else scale

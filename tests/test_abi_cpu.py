@@ -28,7 +28,8 @@ def _declared_functions():
 def test_header_declares_the_boundary_calls():
     names = _declared_functions()
     for must in ("kv_pool_create", "block_table_upload", "reshape_and_cache",
-                 "paged_attention_decode", "paged_attention_verify", "slot_mapping_compute"):
+                 "paged_attention_decode", "paged_attention_verify", "slot_mapping_compute",
+                 "paged_attention_append", "paged_attention_prefill"):
         assert must in names
     assert len(names) >= 15
 
@@ -138,6 +139,7 @@ def test_calls_without_handles_are_refused(pk):
     nul = ctypes.c_void_p(0)
     assert lib.paged_attention_decode(nul, 0, nul, nul, 1, 8, 1.0, nul, 0, nul, 1, nul) == -1
     assert lib.paged_attention_verify(nul, 0, nul, nul, 1, 2, 8, 1.0, nul, 0, nul, 1, nul) == -1
+    assert lib.paged_attention_prefill(nul, 0, nul, nul, 1, 64, 8, 1.0, nul, 1, nul) == -1
     assert lib.reshape_and_cache(nul, 0, nul, nul, 1, nul, 4, nul) == -1
     assert lib.slot_mapping_compute(nul, nul, nul, 4, nul, nul) == -1
     assert lib.paged_attention_workspace_bytes(nul, nul, 8, 1) == 0

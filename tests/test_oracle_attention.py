@@ -140,6 +140,47 @@ def test_cached_equals_uncached_causal_attention():
     assert not np.allclose(dec[0, 0], full_causal(7)[-1], rtol=0, atol=1e-6)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (3, 1)])
+def test_chunked_prefill_equals_full_causal_attention(Hq, Hkv):
+    # Page "KV cache & continuous batching", section "3. Chunked prefill": a
+    # prompt fed in chunks, each appended to the cache and then attended,
+    # gives the rows of full causal attention over the whole prompt.  The
+    # reference is the textbook dense form: one masked score matrix per query
+    # head, softmax along rows, times V.
+    rng = np.random.default_rng(303 + Hq)
+    n, d = 37, 8
+    G = Hq // Hkv
+    K = rng.standard_normal((n, Hkv, d)).astype(np.float32)
+    V = rng.standard_normal((n, Hkv, d)).astype(np.float32)
+    Q = rng.standard_normal((n, Hq, d))
+    scale = 1.0 / math.sqrt(d)
+    full = np.zeros((n, Hq, d))
+    mask = np.triu(np.full((n, n), -np.inf), 1)
+    for g in range(Hq):
+        h = g // G
+        S = (Q[:, g] @ K[:, h].astype(np.float64).T) * scale + mask
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        P = P / P.sum(axis=1, keepdims=True)
+        full[:, g] = P @ V[:, h].astype(np.float64)
+    desc = opool.PoolDesc(1, 6, Hkv, d, "f32")
+    tab = np.array([[4, 0, 5]], dtype=np.int32)          # three blocks, out of order
+    img = opool.empty_pool(desc)
+    pos = 0
+    for C in (5, 16, 1, 15):
+        slots = opool.slot_mapping(tab, [0] * C, list(range(pos, pos + C)), desc.num_blocks)
+        img = opool.cache_write(desc, img, 0, K[pos:pos + C], V[pos:pos + C], "f32", slots)
+        got = oatt.prefill(desc, img, 0, tab, np.array([pos + C]), Q[None, pos:pos + C], C, scale)
+        assert np.allclose(got[0], full[pos:pos + C], rtol=0, atol=1e-12)
+        some = oatt.prefill(desc, img, 0, tab, np.array([pos + C]), Q[None, pos:pos + C], C, scale,
+                            rows=[C - 1, 0])
+        assert np.array_equal(some[0, [C - 1, 0]], got[0, [C - 1, 0]])
+        pos += C
+    # negative control: rows that also see the next position break the identity
+    C = 15
+    wrong = oatt.prefill(desc, img, 0, tab, np.array([n]), Q[None, n - C - 1:n - 1], C, scale)
+    assert not np.allclose(wrong[0], full[n - C - 1:n - 1], rtol=0, atol=1e-6)
+
+
 def test_softmax_rows_sum_to_one_and_ones_in_ones_out():
     rng = np.random.default_rng(9)
     K = rng.standard_normal((300, 8)) * 3

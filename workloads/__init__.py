@@ -23,6 +23,9 @@ c5     Speculative verify over a shared prefix: 32 / 8 heads, d 128, fp8 E4M3 KV
        table entries name the same 128 physical blocks (a 2048-token prefix),
        then a private suffix of uniform [64, 1024] cached tokens, then 5 query
        positions (4 draft + 1 bonus) at the end.
+pf     Chunked prefill, Llama-3-8B-shaped layer (32 / 8 heads, d 128, bf16):
+       8 sequences, each a cached prefix of uniform [0, 14336] tokens followed
+       by a chunk of 2048 query tokens.
 =====  ==========================================================================
 
 Reduced variants (``c2s`` ... ``c5s``) keep the head shapes and the length mix
@@ -46,7 +49,7 @@ Conventions (readings recorded in the design notes):
   values (K and V separately); full-size workloads whose pool is filled on the
   device use (4/448) * (1 + h/8) for head h with codes drawn as e4m3(x*448/4).
 
-Seeds: 293000 + config number (c1 -> 293001, ...).
+Seeds: 293000 + config number (c1 -> 293001, ...; pf, pfs -> 293006).
 """
 
 import math
@@ -225,7 +228,10 @@ def _uniform(rng, lo, hi, size):
 
 
 def make(name, materialize=None, seed=None):
-    """Build workload `name` (c1..c5 full size, c2s..c5s reduced)."""
+    """Build workload `name` (c1..c5 full size, c2s..c5s reduced; pf / pfs:
+    chunked prefill, full size / reduced)."""
+    if name in ("pf", "pfs"):
+        return _make_prefill(name, materialize, seed)
     num = int(name[1])
     seed = SEED_BASE + num if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -276,6 +282,24 @@ def make(name, materialize=None, seed=None):
                      kv_dtype="fp8", k_rows=5, shared_prefix_tokens=256,
                      materialize=materialize, partition_tokens=128)
     raise ValueError(name)
+
+
+def _make_prefill(name, materialize, seed):
+    """Chunked prefill on the Llama-3-8B-shaped layer (32 / 8 heads, d 128,
+    bf16 KV): every sequence has a cached prefix of uniform [0, P] tokens and
+    a chunk of C query tokens after it (their K/V appended before attention).
+    pf: 8 sequences, C = 2048, P = 14336 (contexts up to 16K);
+    pfs: 3 sequences, C = 200, P = 300 (a ragged chunk spanning several
+    256-row tiles and partial blocks)."""
+    seed = SEED_BASE + 6 if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    small = name == "pfs"
+    if materialize is None:
+        materialize = small
+    B, C, P = (3, 200, 300) if small else (8, 2048, 14336)
+    lens = _uniform(rng, 0, P, B) + C
+    return build(name, seed, rng, lens, num_q_heads=32, num_kv_heads=8, head_dim=128, kv_dtype="bf16",
+                 k_rows=C, materialize=materialize, partition_tokens=0)
 
 
 def custom(seed, seq_lens, **kw):
