@@ -34,12 +34,16 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "paged decode attention KV GB/s (% HBM peak) + seqs/s, Llama-3-8B GQA shapes"
 WORKLOAD_NAMES = {
     "c2": "llama3-8b-decode-layer bf16 kv, 32q/8kv heads, d128, block16, batch64, ctx U[512,4096]",
     "c3": "llama3-70b-decode-layer bf16 kv, 64q/8kv heads, d128, block16, batch256, ctx 179xU[128,1024]+77xU[4096,32768]",
     "c4": "long-context split-kv bf16 kv, 32q/8kv heads, d128, block16, batch4, ctx 131072, 512-token partitions",
+    "pf": "llama3-8b chunked-prefill layer bf16 kv, 32q/8kv heads, d128, block16, batch8, "
+          "2048-token chunks after cached prefixes U[0,14336]",
 }
+PREFILL_METRIC = "chunked-prefill paged attention TFLOP/s (causal, visible query-key pairs only)"
 
 
 def parse():
@@ -100,6 +104,9 @@ def main():
               "(the path shards by sequence or KV head with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "pf":
+        return run_prefill(args)
 
     import numpy as np
     import torch
@@ -232,6 +239,132 @@ def main():
         image = pools[0].storage.cpu().numpy()
         result["cpu_baseline"] = cpu_baseline(w, image, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def prefill_flops(w):
+    """4 * H_q * d per visible (query row, key) pair: row j of a sequence of
+    length n sees n - C + j + 1 positions."""
+    C = w.k_rows
+    pairs = sum(int(C) * (int(n) - C) + C * (C + 1) // 2 for n in w.seq_lens)
+    return 4 * w.num_q_heads * w.head_dim * pairs
+
+
+def run_prefill(args):
+    """The chunked-prefill step: slot mapping of every chunk token, the append
+    of their K/V, and paged prefill attention over each sequence's cache."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_293_amd as pk
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = workloads.make("pf", materialize=False)
+    pools = []
+    for r in range(max(1, args.rotate)):
+        nbytes = pk.kv_pool_bytes(w.num_layers, w.num_blocks, w.num_kv_heads, w.head_dim, w.kv_dtype)
+        storage = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        workloads.fill_pool_random(storage, w.kv_dtype, w.seed + 7919 * r)
+        pools.append(pk.kv_pool_create(w.num_layers, w.num_blocks, w.num_kv_heads, w.head_dim, w.kv_dtype,
+                                       storage=storage))
+    table = pk.block_table_upload(pools[0], w.block_tables, w.seq_lens, 0)
+
+    def bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q = bf16(w.q)
+    k_new = bf16(w.k_new)
+    v_new = bf16(w.v_new)
+    sid = torch.from_numpy(w.new_seq_ids).to(dev)
+    pos = torch.from_numpy(w.new_positions).to(dev)
+    slots = torch.empty(sid.numel(), dtype=torch.int64, device=dev)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    K, W = args.steps, args.warmup
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+
+    def step(i, timed):
+        pool = pools[i % len(pools)]
+        pk.slot_mapping_compute(table, sid, pos, out=slots)
+        pk.reshape_and_cache(pool, w.layer, k_new, v_new, slots)
+        if timed:
+            ev[i][0].record()
+        pk.paged_attention_prefill(pool, w.layer, table, q, w.scale, out=out)
+        if timed:
+            ev[i][1].record()
+
+    for i in range(W):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(K):
+        step(i, True)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / K
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    flops = prefill_flops(w)
+    C = w.k_rows
+    result = {
+        "metric": PREFILL_METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) KV and queries, random block placement)",
+        "config": {"workload": WORKLOAD_NAMES["pf"], "batch": w.batch, "chunk": C,
+                   "context_tokens": int(w.seq_lens.sum()),
+                   "step": "slot_mapping_compute + reshape_and_cache + paged_attention_prefill",
+                   "pools_rotated": len(pools)},
+        "tokens_per_s": round(w.batch * C / (ms_step * 1e-3), 1),
+        "attention_ms": round(attn_avg, 5),
+        "attention_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 5),
+                                 round(float(np.percentile(attn_ms, 90)), 5)],
+        "flops_per_step": flops,
+        "wall_s": round(wall, 3),
+        "roofline": {"bound": "mfma", "kernel": "attn_prefill_kernel<bf16,128>",
+                     "achieved": round(flops / (attn_avg * 1e-3) / 1e12, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (attn_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefill_cpu_baseline(w, pools[0].storage.cpu().numpy(), args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def prefill_cpu_baseline(w, pool_image, budget_s):
+    """The float64 oracle, one thread, on as many chunk rows of sequence 0 as fit the budget."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as oatt
+    from oracle import pool as opool
+
+    desc = opool.PoolDesc(w.num_layers, w.num_blocks, w.num_kv_heads, w.head_dim, w.kv_dtype)
+    q = opool.bf16_bits_to_float(w.q[:1])
+    C = w.k_rows
+    n = int(w.seq_lens[0])
+    done, flops = 0, 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for j in range(C - 1, -1, -1):
+            oatt.prefill(desc, pool_image, w.layer, w.block_tables[:1], w.seq_lens[:1], q, C, w.scale,
+                         seqs=[0], rows=[j])
+            done += 1
+            flops += 4 * w.num_q_heads * w.head_dim * (n - C + j + 1)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 numpy oracle prefill of the last {done} of {C} chunk rows of sequence 0 "
+                      f"(n = {n}, all {w.num_q_heads} query heads, {dt:.1f} s, one thread)"}
 
 
 def _kernel_digest():

@@ -307,7 +307,7 @@ pkv_status paged_attention_append(const pkv_pool* pool, int32_t layer, const pkv
  *   out[s][j][g] = softmax( scale * q[s][j][g] . K_s[t][h]^T, t <= n-C+j ) V_s[t][h],
  *   h = g / (num_q_heads / num_kv_heads).
  * It is the computation of paged_attention_verify with C rows, for any C:
- * the kernel keeps each work-group's 256 query rows resident and streams the
+ * the kernel keeps each work-group's 192 query rows resident and streams the
  * visible K/V blocks through LDS, bound by the matrix cores.
  *   dev_q    [num_seqs][C][num_q_heads][head_dim] bfloat16.
  *   dev_out  [num_seqs][C][num_q_heads][head_dim], out_dtype PKV_BF16 or PKV_F32.

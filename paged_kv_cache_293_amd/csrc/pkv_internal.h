@@ -89,7 +89,7 @@ hipError_t launch_attention(const AttnArgs& a, int kv_dtype, int head_dim, int n
 // positions n-chunk .. n-1 (their K/V already in the pool); row (j, g) sees
 // positions t <= n - chunk + j.  One work-group per (sequence, KV head, tile
 // of kPrefillRows query rows).
-constexpr int kPrefillRows = 256;
+constexpr int kPrefillRows = 192;
 
 struct PrefillArgs {
     const uint8_t* pool;

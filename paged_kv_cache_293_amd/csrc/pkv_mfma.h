@@ -23,9 +23,21 @@ __device__ __forceinline__ unsigned f32_to_bf16_rne(float f) {
     return __builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
 }
 
-// Two floats -> two bf16 (round to nearest even) packed low/high.
+// Two floats -> two bf16 (round to nearest even) packed low/high, in one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+// Maximum of x over the four lanes l, l^16, l^32, l^48 (the four 16-lane
+// rows of the wave), with the gfx950 row-swap permutes (no LDS traffic).
+__device__ __forceinline__ float max_over_rows(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Buffer resource over one block's K tile followed by its V tile.  Loads

@@ -13,9 +13,11 @@
 //   computation with C rows, at sizes where the matrix cores bound it.
 //
 // Work decomposition.  One work-group of 4 waves per (sequence, KV head,
-// tile of 256 query rows); rows are ordered (token, head of the group), so
-// the G heads of one token sit side by side.  Each wave owns 64 rows as four
-// 16-row column tiles, with their queries resident in registers.  The K/V of
+// tile of 192 query rows); rows are ordered (token, head of the group), so
+// the G heads of one token sit side by side.  Each wave owns 48 rows as three
+// 16-row column tiles, with their queries resident in registers; the rest of
+// its state fits in 256 VGPRs, so two work-groups share a CU and their waves
+// interleave softmax (VALU) and matrix work on each SIMD.  The K/V of
 // the visible blocks stream through a three-stage LDS ring, two blocks (a
 // "pair") per stage, copied straight from the pool into LDS by
 // global_load_lds_dwordx4 (no register staging); each wave issues its share
@@ -42,10 +44,11 @@ namespace pkv {
 namespace {
 
 constexpr int kPfWaves = 4;
-constexpr int kPfNT = kPrefillRows / (16 * kPfWaves);   // column tiles per wave (4)
+constexpr int kPfNT = kPrefillRows / (16 * kPfWaves);   // column tiles per wave (3)
 constexpr int kPfStages = 3;
 constexpr int kPfIdWindow = 2048;                       // block ids held in LDS at a time
 constexpr int kPfXcds = 8;
+constexpr float kLazyMax = 8.f;                         // exp2 units the running max may lag
 
 template <int KVT, int D> struct PfGeom {
     static constexpr int EB = KVT == KV_FP8 ? 1 : 2;
@@ -109,27 +112,26 @@ __device__ __forceinline__ u32x4 pf_v_op(const uint8_t* va, const uint8_t* vb, i
     }
 }
 
-// Zero the bf16 values of an operand built by pf_v_op whose tokens are >= n
-// (tokens t0 + 4lg + e of block A, t0 + 16 + 4lg + e of block B).
-__device__ __forceinline__ u32x4 pf_zero_tail(u32x4 v, int t0, int lg, int n) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int first = t0 + 16 * half + 4 * lg;
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-            unsigned keep = 0;
-            if (first + 2 * w < n) keep |= 0x0000ffffu;
-            if (first + 2 * w + 1 < n) keep |= 0xffff0000u;
-            v[2 * half + w] &= keep;
-        }
+// Zero, in an LDS stage, the V entries of tokens >= n of both blocks of the
+// pair starting at token t0 (bytes past the sequence end, or the second block
+// of an odd count, hold no value of this sequence; their probability is 0,
+// but 0 times a NaN would not be).  One thread per (block, dim) row of the
+// transposed V tiles.
+template <int KVT, int D>
+__device__ __forceinline__ void pf_zero_v_tail(uint8_t* stage, int t0, int n, int tid) {
+    using Gm = PfGeom<KVT, D>;
+    for (int r = tid; r < 2 * D; r += 64 * kPfWaves) {
+        const int blk = r / D;
+        const int dim = r - blk * D;
+        const int cut = n - (t0 + 16 * blk);          // tokens of this block below n
+        uint8_t* row = stage + (2 * blk + 1) * Gm::TILE + dim * 16 * Gm::EB;
+        for (int o = max(cut, 0); o < 16; ++o)
+            for (int b = 0; b < Gm::EB; ++b) row[o * Gm::EB + b] = 0;
     }
-    return v;
 }
 
-__device__ __forceinline__ float bf16_round(float p) { return __uint_as_float(f32_to_bf16_rne(p) << 16); }
-
 template <int KVT, int D>
-__global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_kernel(PrefillArgs a) {
     using Gm = PfGeom<KVT, D>;
     extern __shared__ __attribute__((aligned(16))) uint8_t pf_smem[];
@@ -185,15 +187,20 @@ void attn_prefill_kernel(PrefillArgs a) {
         lim[c] = valid ? first + j + 1 : 0;
     }
 
+    // o: unnormalised output per (column tile, 16 dims); ol: the row sums of
+    // the bf16 probabilities, accumulated by the matrix cores against a tile
+    // of ones (every entry of a column holds that row's sum).
     f32x4 o[kPfNT][D / 16];
-    float m_run[kPfNT], l_run[kPfNT];
+    f32x4 ol[kPfNT];
+    float m_run[kPfNT];
 #pragma unroll
     for (int c = 0; c < kPfNT; ++c) {
         m_run[c] = neg_inf();
-        l_run[c] = 0.f;
+        ol[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < D / 16; ++m) o[c][m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
     const int64_t block_stride = static_cast<int64_t>(H) * 2 * a.tile_bytes;
     const uint8_t* head_base = a.pool + static_cast<int64_t>(a.layer) * a.num_blocks * block_stride +
@@ -237,8 +244,13 @@ void attn_prefill_kernel(PrefillArgs a) {
             issue(q);
         }
 
-        const uint8_t* st = pf_smem + (p % kPfStages) * Gm::PAIR;
+        uint8_t* st = pf_smem + (p % kPfStages) * Gm::PAIR;
         const int t0 = 32 * p;
+        if (t0 + 32 > n) {
+            // only the last pair reaches past the sequence end; nothing is in flight
+            pf_zero_v_tail<KVT, D>(st, t0, n, tid);
+            __syncthreads();
+        }
         TileRegs<KVT, D> ka, kb;
         pf_k_regs<KVT, D>(ka, st, lane);
         pf_k_regs<KVT, D>(kb, st + 2 * Gm::TILE, lane);
@@ -250,11 +262,6 @@ void attn_prefill_kernel(PrefillArgs a) {
         for (int c = 0; c < kPfNT; ++c) {
             f32x4 sa = scores<D>(ka, qr[c]);
             f32x4 sb = scores<D>(kb, qr[c]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sa[i] *= sscale;
-                sb[i] *= sscale;
-            }
             if (need_mask) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -262,41 +269,45 @@ void attn_prefill_kernel(PrefillArgs a) {
                     if (t0 + 16 + 4 * lg + i >= lim[c]) sb[i] = neg_inf();
                 }
             }
+            // Running max in exp2 units, kept stale: it moves (and the
+            // accumulators are rescaled) only when a score exceeds it by more
+            // than kLazyMax, so probabilities stay <= 2^kLazyMax.  O and its
+            // row sum share the same max, so O / sum is unchanged.
             float mx = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
                              fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(m_run[c], mx);
-            const float muse = (mnew == neg_inf()) ? 0.f : mnew;
-            alpha[c] = fast_exp2(m_run[c] - muse);
+            mx = max_over_rows(mx) * sscale;
+            alpha[c] = 1.f;
+            if (mx > m_run[c] + kLazyMax) {
+                alpha[c] = fast_exp2(m_run[c] - mx);
+                m_run[c] = mx;
+                rescale = true;
+            }
+            const float muse = m_run[c] == neg_inf() ? 0.f : m_run[c];
             float pa[4], pb[4];
-            float psum = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pa[i] = fast_exp2(sa[i] - muse);
-                pb[i] = fast_exp2(sb[i] - muse);
-                psum += bf16_round(pa[i]) + bf16_round(pb[i]);
+                pa[i] = fast_exp2(__builtin_fmaf(sa[i], sscale, -muse));
+                pb[i] = fast_exp2(__builtin_fmaf(sb[i], sscale, -muse));
             }
-            l_run[c] = l_run[c] * alpha[c] + psum;
-            m_run[c] = mnew;
-            rescale |= alpha[c] != 1.f;
             pop[c] = u32x4{pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3]), pack_bf16x2(pb[0], pb[1]),
                            pack_bf16x2(pb[2], pb[3])};
         }
         if (__ballot(rescale)) {
 #pragma unroll
-            for (int c = 0; c < kPfNT; ++c)
+            for (int c = 0; c < kPfNT; ++c) {
+                ol[c] *= alpha[c];
 #pragma unroll
                 for (int m = 0; m < D / 16; ++m) o[c][m] *= alpha[c];
+            }
         }
-        const bool tail = t0 + 32 > n;
+#pragma unroll
+        for (int c = 0; c < kPfNT; ++c)
+            ol[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, pop[c]), ol[c], 0, 0, 0);
         const uint8_t* va = st + Gm::TILE;
         const uint8_t* vb = st + 3 * Gm::TILE;
 #pragma unroll
         for (int m = 0; m < D / 16; ++m) {
-            u32x4 v = pf_v_op<KVT, D>(va, vb, m, col, lg);
-            if (tail) v = pf_zero_tail(v, t0, lg, n);
-            const bf16x8 av = __builtin_bit_cast(bf16x8, v);
+            const bf16x8 av = __builtin_bit_cast(bf16x8, pf_v_op<KVT, D>(va, vb, m, col, lg));
 #pragma unroll
             for (int c = 0; c < kPfNT; ++c)
                 o[c][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, pop[c]), o[c][m],
@@ -307,9 +318,7 @@ void attn_prefill_kernel(PrefillArgs a) {
     // Normalise and store: lane holds dims 16m + 4lg .. +3 of row 16c + col.
 #pragma unroll
     for (int c = 0; c < kPfNT; ++c) {
-        float l = l_run[c];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        const float l = ol[c][0];
         const int row = row_w + 16 * c + col;
         if (row >= Rt) continue;
         const int j = row / G;
