@@ -64,6 +64,11 @@ typedef int32_t pkv_status;
 #define PKV_BF16     1  /* bfloat16 (upper half of a binary32)                  */
 #define PKV_FP8_E4M3 2  /* OCP FP8 E4M3 ("e4m3fn": bias 7, max 448, NaN S.1111.111,
                            no infinities) times a float32 scale per (layer, KV head) */
+#define PKV_INT8     3  /* symmetric int8 code in [-127, 127] times a float32 scale per
+                           (layer, KV head); written as sat127(round-half-even(
+                           f32(x) * f32(1 / scale))), NaN written as 0 (page "KV cache &
+                           continuous batching", section "KV cache memory math": one
+                           byte per element for fp8 or int8) */
 
 /*
  * Pool geometry.
@@ -85,7 +90,7 @@ typedef int32_t pkv_status;
  * V tile, element (o, i) is element number  i * 16 + o  (V stored transposed).
  * Token position t of a sequence with block table row `bt` lives at block
  * bt[t / 16], offset t % 16; its flat slot is bt[t / 16] * 16 + t % 16.
- * For PKV_FP8_E4M3 the stored code c of head h in layer l stands for the value
+ * For PKV_FP8_E4M3 and PKV_INT8 the stored code c of head h in layer l stands for the value
  * decode(c) * scale[l][h], with separate K and V scale arrays.
  */
 typedef struct pkv_pool_desc {
@@ -94,7 +99,7 @@ typedef struct pkv_pool_desc {
     int32_t num_kv_heads;  /* >= 1                                    */
     int32_t head_dim;      /* 64 or 128                               */
     int32_t block_size;    /* must be PKV_BLOCK_SIZE (16)             */
-    int32_t kv_dtype;      /* PKV_F32, PKV_BF16 or PKV_FP8_E4M3       */
+    int32_t kv_dtype;      /* PKV_F32, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 */
 } pkv_pool_desc;
 
 typedef struct pkv_pool pkv_pool;
@@ -122,7 +127,7 @@ int64_t kv_pool_bytes(const pkv_pool_desc* desc);
  * Wrap a caller-allocated pool buffer in a handle.
  *   dev_base   device buffer of at least kv_pool_bytes(desc) bytes, 256-byte aligned.
  *   dev_k_scale, dev_v_scale  float32 [num_layers][num_kv_heads] device arrays;
- *              required (non-NULL) for PKV_FP8_E4M3, ignored otherwise.
+ *              required (non-NULL) for PKV_FP8_E4M3 and PKV_INT8, ignored otherwise.
  * Errors: PKV_ERR_INVALID (null, short or misaligned buffer, bad counts),
  *         PKV_ERR_UNSUPPORTED (block_size != 16, head_dim not 64/128, dtype).
  * The buffer contents are not touched.
@@ -311,7 +316,7 @@ pkv_status paged_attention_append(const pkv_pool* pool, int32_t layer, const pkv
  * visible K/V blocks through LDS, bound by the matrix cores.
  *   dev_q    [num_seqs][C][num_q_heads][head_dim] bfloat16.
  *   dev_out  [num_seqs][C][num_q_heads][head_dim], out_dtype PKV_BF16 or PKV_F32.
- *   Pools: PKV_BF16 or PKV_FP8_E4M3 (PKV_F32 pools: PKV_ERR_UNSUPPORTED).
+ *   Pools: PKV_BF16, PKV_FP8_E4M3 or PKV_INT8 (PKV_F32 pools: PKV_ERR_UNSUPPORTED).
  * No workspace.  The table's split-KV plan is not used (any partition_tokens).
  * Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_SEQ_LEN (a sequence
  * shorter than C), PKV_ERR_BLOCK_RANGE, PKV_ERR_HIP.

@@ -24,8 +24,9 @@ so the oracle reads the pool from the definition, not from library code):
   consecutive dims, chunk-major, token-minor);
 * inside a V tile, element (token o, dim i) is element number i * 16 + o
   (dim-major: the V tile is stored transposed);
-* b = 4 (float32), 2 (bfloat16) or 1 (fp8 E4M3 with a float32 scale per
-  (layer, KV head), separately for K and V; value = code * scale).
+* b = 4 (float32), 2 (bfloat16) or 1 (fp8 E4M3, or symmetric int8, with a
+  float32 scale per (layer, KV head), separately for K and V; value = code *
+  scale).
 
 Pins: the layout formula is checked against hand-computed offsets stored in
 ``tests/golden/pool_layout.txt``; the slot rule against the page-1 block-table
@@ -36,9 +37,10 @@ gather against each other and against brute-force loops in the tests.
 import numpy as np
 
 from . import fp8 as _fp8
+from . import int8 as _int8
 from .kv_math import BLOCK_SIZE, slot_of
 
-DTYPE_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+DTYPE_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}
 
 
 class PoolDesc:
@@ -141,6 +143,8 @@ def _decode_raw(desc, raw, scale):
         return raw.astype(np.float64)
     if desc.kv_dtype == "bf16":
         return bf16_bits_to_float(raw)
+    if desc.kv_dtype == "int8":
+        return _int8.decode(raw.view(np.int8), scale)
     return _fp8.decode(raw) * np.float64(np.float32(scale))
 
 
@@ -182,7 +186,8 @@ def cache_write(desc, pool_u8, layer, k_new, v_new, in_dtype, slots,
     k_new, v_new: [T][H_kv][d] raw input values; in_dtype "f32" (float32
     array) or "bf16" (uint16 bit patterns).  A slot < 0 skips its token.
     f32 and bf16 pools store the input bits unchanged (the input dtype must
-    equal the pool dtype); fp8 pools store fp8.quantize(x, scale[layer][h]).
+    equal the pool dtype); fp8 pools store fp8.quantize(x, scale[layer][h]),
+    int8 pools int8.quantize(x, scale[layer][h]).
     Returns a new array; the input image is not modified.
     """
     pool = pool_u8.copy()
@@ -210,6 +215,11 @@ def cache_write(desc, pool_u8, layer, k_new, v_new, in_dtype, slots,
                 vx = _input_to_f32(v_new[t, h], in_dtype)
                 raw[k_at] = _fp8.quantize(kx, k_scale[layer][h])
                 raw[v_at] = _fp8.quantize(vx, v_scale[layer][h])
+            elif desc.kv_dtype == "int8":
+                kx = _input_to_f32(k_new[t, h], in_dtype)
+                vx = _input_to_f32(v_new[t, h], in_dtype)
+                raw[k_at] = _int8.quantize(kx, k_scale[layer][h]).view(np.uint8)
+                raw[v_at] = _int8.quantize(vx, v_scale[layer][h]).view(np.uint8)
             else:
                 raw[k_at] = k_new[t, h]
                 raw[v_at] = v_new[t, h]

@@ -57,6 +57,7 @@ int elem_bytes(int32_t dtype) {
         case PKV_F32: return 4;
         case PKV_BF16: return 2;
         case PKV_FP8_E4M3: return 1;
+        case PKV_INT8: return 1;
         default: return 0;
     }
 }
@@ -256,13 +257,14 @@ pkv_status kv_pool_create(const pkv_pool_desc* desc, void* dev_base, size_t dev_
         if (st != PKV_OK) return st;
         if (!dev_base || reinterpret_cast<uintptr_t>(dev_base) % kAlign) return PKV_ERR_INVALID;
         if (dev_bytes < static_cast<size_t>(kv_pool_bytes(desc))) return PKV_ERR_INVALID;
-        if (desc->kv_dtype == PKV_FP8_E4M3 && (!dev_k_scale || !dev_v_scale)) return PKV_ERR_INVALID;
+        const bool scaled = desc->kv_dtype == PKV_FP8_E4M3 || desc->kv_dtype == PKV_INT8;
+        if (scaled && (!dev_k_scale || !dev_v_scale)) return PKV_ERR_INVALID;
         pkv_pool* p = new pkv_pool;
         p->desc = *desc;
         p->base = static_cast<uint8_t*>(dev_base);
         p->bytes = dev_bytes;
-        p->k_scale = desc->kv_dtype == PKV_FP8_E4M3 ? dev_k_scale : nullptr;
-        p->v_scale = desc->kv_dtype == PKV_FP8_E4M3 ? dev_v_scale : nullptr;
+        p->k_scale = scaled ? dev_k_scale : nullptr;
+        p->v_scale = scaled ? dev_v_scale : nullptr;
         p->tile_bytes = static_cast<int64_t>(PKV_BLOCK_SIZE) * desc->head_dim * elem_bytes(desc->kv_dtype);
         *out = p;
         return PKV_OK;
@@ -428,7 +430,7 @@ pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, const void* de
     if (layer < 0 || layer >= pool->desc.num_layers) return PKV_ERR_INVALID;
     const int32_t kv = pool->desc.kv_dtype;
     const bool ok = (kv == PKV_F32 && in_dtype == PKV_F32) || (kv == PKV_BF16 && in_dtype == PKV_BF16) ||
-                    (kv == PKV_FP8_E4M3 && (in_dtype == PKV_F32 || in_dtype == PKV_BF16));
+                    ((kv == PKV_FP8_E4M3 || kv == PKV_INT8) && (in_dtype == PKV_F32 || in_dtype == PKV_BF16));
     if (!ok) return PKV_ERR_UNSUPPORTED;
     if (num_tokens == 0) return PKV_OK;
     if (!dev_k_new || !dev_v_new || !dev_slot_mapping) return PKV_ERR_INVALID;
@@ -493,7 +495,7 @@ pkv_status attention_call(const pkv_pool* pool, int32_t layer, const pkv_table* 
     if (k_new || v_new) {
         if (!k_new || !v_new) return PKV_ERR_INVALID;
         const bool ok = (kv == PKV_F32 && in_dtype == PKV_F32) || (kv == PKV_BF16 && in_dtype == PKV_BF16) ||
-                        (kv == PKV_FP8_E4M3 && (in_dtype == PKV_F32 || in_dtype == PKV_BF16));
+                        ((kv == PKV_FP8_E4M3 || kv == PKV_INT8) && (in_dtype == PKV_F32 || in_dtype == PKV_BF16));
         if (!ok) return PKV_ERR_UNSUPPORTED;
     }
 
@@ -570,7 +572,7 @@ pkv_status paged_attention_prefill(const pkv_pool* pool, int32_t layer, const pk
     const int32_t hkv = pool->desc.num_kv_heads;
     if (num_q_heads % hkv || table->num_kv_heads != hkv) return PKV_ERR_INVALID;
     const int32_t kv = pool->desc.kv_dtype;
-    if (kv != PKV_BF16 && kv != PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+    if (kv != PKV_BF16 && kv != PKV_FP8_E4M3 && kv != PKV_INT8) return PKV_ERR_UNSUPPORTED;
     if (q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
     if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
     if (table->min_seq_len < chunk_tokens) return PKV_ERR_SEQ_LEN;
@@ -598,7 +600,7 @@ pkv_status paged_attention_prefill(const pkv_pool* pool, int32_t layer, const pk
     a.row_tiles = static_cast<int32_t>(tiles);
     a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
     a.score_scale = scale * 1.4426950408889634f;
-    const int32_t kvt = kv == PKV_BF16 ? 1 : 2;
+    const int32_t kvt = kv;   // PKV_* element codes equal the kernels' KV_* codes
     return hip_status(pkv::launch_prefill(a, kvt, pool->desc.head_dim, static_cast<hipStream_t>(stream)));
 }
 

@@ -64,8 +64,8 @@ __device__ __forceinline__ void accumulate_pv(const TileRegs<KV_BF16, D>& t, con
     }
 }
 
-template <int D, int NT>
-__device__ __forceinline__ void accumulate_pv(const TileRegs<KV_FP8, D>& t, const f32x4 (&p)[NT],
+template <int KVT, int D, int NT>
+__device__ __forceinline__ void accumulate_pv_1b(const TileRegs<KVT, D>& t, const f32x4 (&p)[NT],
                                               f32x4 (&o)[NT][D / 16]) {
     s16x4 pb[NT];
 #pragma unroll
@@ -74,12 +74,24 @@ __device__ __forceinline__ void accumulate_pv(const TileRegs<KV_FP8, D>& t, cons
     }
 #pragma unroll
     for (int m = 0; m < D / 16; ++m) {
-        const u32x2 vb = {fp8x2_to_bf16x2<false>(t.v[m]), fp8x2_to_bf16x2<true>(t.v[m])};
+        const u32x2 vb = {byte2_to_bf16x2<KVT, false>(t.v[m]), byte2_to_bf16x2<KVT, true>(t.v[m])};
         const s16x4 a = __builtin_bit_cast(s16x4, vb);
 #pragma unroll
         for (int c = 0; c < NT; ++c)
             o[c][m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb[c], o[c][m], 0, 0, 0);
     }
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void accumulate_pv(const TileRegs<KV_FP8, D>& t, const f32x4 (&p)[NT],
+                                              f32x4 (&o)[NT][D / 16]) {
+    accumulate_pv_1b<KV_FP8, D, NT>(t, p, o);
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void accumulate_pv(const TileRegs<KV_INT8, D>& t, const f32x4 (&p)[NT],
+                                              f32x4 (&o)[NT][D / 16]) {
+    accumulate_pv_1b<KV_INT8, D, NT>(t, p, o);
 }
 
 template <int D, int NT>
@@ -150,7 +162,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
 
     float sscale = a.score_scale;
     float vscale = 1.f;
-    if constexpr (KVT == KV_FP8) {
+    if constexpr (kv_scaled<KVT>()) {
         sscale *= a.k_scale[a.layer * a.num_kv_heads + h];
         vscale = a.v_scale[a.layer * a.num_kv_heads + h];
     }
@@ -254,7 +266,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
                 const uint8_t* vr = reinterpret_cast<const uint8_t*>(a.v_new) + row;
                 const float* ks = a.k_scale ? a.k_scale + a.layer * a.num_kv_heads : nullptr;
                 const float* vs = a.v_scale ? a.v_scale + a.layer * a.num_kv_heads : nullptr;
-                if constexpr (KVT == KV_FP8) {
+                if constexpr (kv_scaled<KVT>()) {
                     if (a.append_in_f32)
                         write_token<KVT, KV_F32, D>(blk, a.tile_bytes, t % kBlock, kr, vr, h, 1, ks, vs,
                                                     tid, 64 * kWaves);
@@ -487,7 +499,7 @@ void attn_partition_kernel(AttnArgs a) {
 // partitions' (O, m, l):  M = max m_p,  L = sum l_p 2^(m_p - M),
 // out = sum O_p 2^(m_p - M) / L  (times the V scale of fp8 pools).
 template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int fp8) {
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int scaled) {
     __shared__ float red[8];
     __shared__ f32x4 part_acc[256];
     const int seq = blockIdx.x;
@@ -547,7 +559,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int fp8) {
         f32x4 sum = part_acc[tid];
         for (int g = 1; g < GR; ++g) sum += part_acc[g * Q + tid];
         const float L = red[4] + red[5] + red[6] + red[7];
-        const float vscale = fp8 ? a.v_scale[a.layer * a.num_kv_heads + h] : 1.f;
+        const float vscale = scaled ? a.v_scale[a.layer * a.num_kv_heads + h] : 1.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) store_out(a, seq, h, r, 4 * tid + i, sum[i] / L * vscale);
     }
@@ -582,7 +594,7 @@ hipError_t launch_instance(const AttnArgs& a, int num_units, hipStream_t stream)
     if (err != hipSuccess) return err;
     if (a.max_parts > a.fuse_max_parts) {
         dim3 g2(a.num_seqs, a.num_kv_heads, a.rows);
-        hipLaunchKernelGGL((attn_merge_kernel<D>), g2, dim3(256), 0, stream, a, KVT == KV_FP8 ? 1 : 0);
+        hipLaunchKernelGGL((attn_merge_kernel<D>), g2, dim3(256), 0, stream, a, kv_scaled<KVT>() ? 1 : 0);
         err = hipGetLastError();
     }
     return err;
@@ -606,6 +618,9 @@ hipError_t launch_attention(const AttnArgs& a, int kv_dtype, int head_dim, int n
     if (kv_dtype == KV_FP8)
         return head_dim == 128 ? launch_rows<KV_FP8, 128>(a, num_units, stream)
                                : launch_rows<KV_FP8, 64>(a, num_units, stream);
+    if (kv_dtype == KV_INT8)
+        return head_dim == 128 ? launch_rows<KV_INT8, 128>(a, num_units, stream)
+                               : launch_rows<KV_INT8, 64>(a, num_units, stream);
     return head_dim == 128 ? launch_rows<KV_F32, 128>(a, num_units, stream)
                            : launch_rows<KV_F32, 64>(a, num_units, stream);
 }

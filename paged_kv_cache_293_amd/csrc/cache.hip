@@ -27,9 +27,9 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheArgs a) {
     constexpr int EB = KVT == KV_F32 ? 4 : (KVT == KV_BF16 ? 2 : 1);
     constexpr int IB = IN == KV_F32 ? 4 : 2;
     uint8_t* bbase = a.pool + (static_cast<int64_t>(a.layer) * a.num_blocks + blk) * H * 2 * a.tile_bytes;
-    const int64_t row = static_cast<int64_t>(t) * H * D * (KVT == KV_FP8 ? IB : EB);
-    const float* ks = KVT == KV_FP8 ? a.k_scale + a.layer * H : nullptr;
-    const float* vs = KVT == KV_FP8 ? a.v_scale + a.layer * H : nullptr;
+    const int64_t row = static_cast<int64_t>(t) * H * D * (kv_scaled<KVT>() ? IB : EB);
+    const float* ks = kv_scaled<KVT>() ? a.k_scale + a.layer * H : nullptr;
+    const float* vs = kv_scaled<KVT>() ? a.v_scale + a.layer * H : nullptr;
     write_token<KVT, IN, D>(bbase, a.tile_bytes, off, reinterpret_cast<const uint8_t*>(a.k_new) + row,
                             reinterpret_cast<const uint8_t*>(a.v_new) + row, 0, H, ks, vs,
                             threadIdx.x, blockDim.x);
@@ -63,6 +63,9 @@ hipError_t launch_reshape_and_cache(const CacheArgs& a, int kv_dtype, int in_dty
     if (a.num_tokens <= 0) return hipSuccess;
     if (kv_dtype == KV_F32) return launch_cache_dim<KV_F32, KV_F32>(a, stream);
     if (kv_dtype == KV_BF16) return launch_cache_dim<KV_BF16, KV_BF16>(a, stream);
+    if (kv_dtype == KV_INT8)
+        return in_dtype == KV_F32 ? launch_cache_dim<KV_INT8, KV_F32>(a, stream)
+                                  : launch_cache_dim<KV_INT8, KV_BF16>(a, stream);
     if (in_dtype == KV_F32) return launch_cache_dim<KV_FP8, KV_F32>(a, stream);
     return launch_cache_dim<KV_FP8, KV_BF16>(a, stream);
 }

@@ -6,7 +6,10 @@
 
 namespace pkv {
 
-enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_INT8 = 3 };
+
+// One-byte element types carry a float32 scale per (layer, KV head).
+template <int KVT> constexpr bool kv_scaled() { return KVT == KV_FP8 || KVT == KV_INT8; }
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -18,6 +21,22 @@ __device__ __forceinline__ unsigned quantize_e4m3(float x, float inv) {
     y = (y > 448.f) ? 448.f : y;
     y = (y < -448.f) ? -448.f : y;
     return static_cast<unsigned>(__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false)) & 0xffu;
+}
+
+// Symmetric int8 code of x * inv: one float32 multiply (round to nearest
+// even), NaN -> 0, round to the nearest integer with ties to even, saturate to
+// +-127 (the code -128 is never written).
+__device__ __forceinline__ unsigned quantize_i8(float x, float inv) {
+    float y = __fmul_rn(x, inv);
+    y = (y == y) ? y : 0.f;
+    y = __builtin_rintf(fminf(fmaxf(y, -127.f), 127.f));
+    return static_cast<unsigned>(static_cast<int>(y)) & 0xffu;
+}
+
+template <int KVT>
+__device__ __forceinline__ unsigned quantize_code(float x, float inv) {
+    if constexpr (KVT == KV_INT8) return quantize_i8(x, inv);
+    else return quantize_e4m3(x, inv);
 }
 
 // Element i of an input row as float (float32 or bfloat16 input).
@@ -48,14 +67,14 @@ __device__ __forceinline__ void write_token(uint8_t* blk, int64_t tile_bytes, in
         const int ch = c % CH;
         uint8_t* dst = blk + static_cast<int64_t>(h) * 2 * tile_bytes + (ch * kBlock + off) * 16;
         const int64_t src = static_cast<int64_t>(h) * D + ch * X;
-        if constexpr (KVT == KV_FP8) {
+        if constexpr (kv_scaled<KVT>()) {
             const float inv = 1.0f / k_scale[h];
             unsigned w[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 unsigned b = 0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) b |= quantize_e4m3(load_in<IN>(k_row, src + 4 * q + e), inv) << (8 * e);
+                for (int e = 0; e < 4; ++e) b |= quantize_code<KVT>(load_in<IN>(k_row, src + 4 * q + e), inv) << (8 * e);
                 w[q] = b;
             }
             *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{w[0], w[1], w[2], w[3]};
@@ -69,8 +88,8 @@ __device__ __forceinline__ void write_token(uint8_t* blk, int64_t tile_bytes, in
         const int i = e % D;
         uint8_t* dst = blk + (static_cast<int64_t>(h) * 2 + 1) * tile_bytes + (i * kBlock + off) * EB;
         const int64_t src = static_cast<int64_t>(h) * D + i;
-        if constexpr (KVT == KV_FP8) {
-            *dst = static_cast<uint8_t>(quantize_e4m3(load_in<IN>(v_row, src), 1.0f / v_scale[h]));
+        if constexpr (kv_scaled<KVT>()) {
+            *dst = static_cast<uint8_t>(quantize_code<KVT>(load_in<IN>(v_row, src), 1.0f / v_scale[h]));
         } else if constexpr (KVT == KV_BF16) {
             *reinterpret_cast<uint16_t*>(dst) = reinterpret_cast<const uint16_t*>(v_row)[src];
         } else {

@@ -75,6 +75,23 @@ __device__ __forceinline__ unsigned fp8x2_to_bf16x2(unsigned w) {
     return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
 }
 
+// Two int8 codes (bytes 0-1, or 2-3 when HI, of w) -> two bf16 values packed
+// in one dword.  |code| <= 127 has at most 8 significant bits, so the float32
+// conversion is exact and so is its upper half.
+template <bool HI>
+__device__ __forceinline__ unsigned i8x2_to_bf16x2(unsigned w) {
+    const float f0 = static_cast<float>(static_cast<int8_t>(w >> (HI ? 16 : 0)));
+    const float f1 = static_cast<float>(static_cast<int8_t>(w >> (HI ? 24 : 8)));
+    return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+}
+
+// Two one-byte codes of type KVT -> two exact bf16 values.
+template <int KVT, bool HI>
+__device__ __forceinline__ unsigned byte2_to_bf16x2(unsigned w) {
+    if constexpr (KVT == KV_INT8) return i8x2_to_bf16x2<HI>(w);
+    else return fp8x2_to_bf16x2<HI>(w);
+}
+
 // ------------------------------------------------------------------ tiles
 // Per-lane registers of one block's K and V tiles, and their loads.
 template <int KVT, int D> struct TileRegs;
@@ -102,7 +119,7 @@ template <int D> struct TileRegs<KV_BF16, D> {
     }
 };
 
-template <int D> struct TileRegs<KV_FP8, D> {
+template <int D> struct TileRegs1B {
     u32x4 k[D / 64];   // 16 codes: token lane%16, dims of chunk 4r + lane/16
     unsigned v[D / 16];  // 4 codes: dim 16m + lane%16, tokens 4*(lane/16) .. +3
     // koff = lane * 16; voff = TILE + (lane % 16) * 16 + (lane / 16) * 4
@@ -122,6 +139,9 @@ template <int D> struct TileRegs<KV_FP8, D> {
         for (int m = 0; m < D / 16; ++m) v[m] &= msk;
     }
 };
+// fp8 and int8 tiles share the byte layout; only the code conversion differs.
+template <int D> struct TileRegs<KV_FP8, D> : TileRegs1B<D> {};
+template <int D> struct TileRegs<KV_INT8, D> : TileRegs1B<D> {};
 
 template <int D> struct TileRegs<KV_F32, D> {
     f32x4 k[D / 16];   // 4 f32: token lane%16, dims of chunk 4r + lane/16
@@ -163,7 +183,7 @@ template <int D> struct QRegs<KV_BF16, D> {
     }
 };
 
-template <int D> struct QRegs<KV_FP8, D> {
+template <int D> struct QRegs1B {
     bf16x8 q[D / 32];   // step 2r + hh: dims (4r + lane/16) * 16 + 8 hh .. +8
     __device__ __forceinline__ void load(const uint16_t* row, bool valid, int lane) {
 #pragma unroll
@@ -174,6 +194,8 @@ template <int D> struct QRegs<KV_FP8, D> {
         }
     }
 };
+template <int D> struct QRegs<KV_FP8, D> : QRegs1B<D> {};
+template <int D> struct QRegs<KV_INT8, D> : QRegs1B<D> {};
 
 template <int D> struct QRegs<KV_F32, D> {
     f32x4 q[D / 16];    // r: dims (4r + lane/16) * 4 .. +4, one MFMA per element
@@ -195,20 +217,30 @@ __device__ __forceinline__ f32x4 scores(const TileRegs<KV_BF16, D>& t, const QRe
     return acc;
 }
 
-template <int D>
-__device__ __forceinline__ f32x4 scores(const TileRegs<KV_FP8, D>& t, const QRegs<KV_FP8, D>& q) {
+template <int KVT, int D>
+__device__ __forceinline__ f32x4 scores_1b(const TileRegs<KVT, D>& t, const QRegs<KVT, D>& q) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < D / 64; ++r) {
         const u32x4 w = t.k[r];
-        u32x4 lo = {fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]),
-                    fp8x2_to_bf16x2<false>(w[1]), fp8x2_to_bf16x2<true>(w[1])};
-        u32x4 hi = {fp8x2_to_bf16x2<false>(w[2]), fp8x2_to_bf16x2<true>(w[2]),
-                    fp8x2_to_bf16x2<false>(w[3]), fp8x2_to_bf16x2<true>(w[3])};
+        u32x4 lo = {byte2_to_bf16x2<KVT, false>(w[0]), byte2_to_bf16x2<KVT, true>(w[0]),
+                    byte2_to_bf16x2<KVT, false>(w[1]), byte2_to_bf16x2<KVT, true>(w[1])};
+        u32x4 hi = {byte2_to_bf16x2<KVT, false>(w[2]), byte2_to_bf16x2<KVT, true>(w[2]),
+                    byte2_to_bf16x2<KVT, false>(w[3]), byte2_to_bf16x2<KVT, true>(w[3])};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo), q.q[2 * r], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi), q.q[2 * r + 1], acc, 0, 0, 0);
     }
     return acc;
+}
+
+template <int D>
+__device__ __forceinline__ f32x4 scores(const TileRegs<KV_FP8, D>& t, const QRegs<KV_FP8, D>& q) {
+    return scores_1b<KV_FP8, D>(t, q);
+}
+
+template <int D>
+__device__ __forceinline__ f32x4 scores(const TileRegs<KV_INT8, D>& t, const QRegs<KV_INT8, D>& q) {
+    return scores_1b<KV_INT8, D>(t, q);
 }
 
 template <int D>

@@ -31,8 +31,8 @@
 // each block of the pair (its 4 + 4 probabilities straight from the two score
 // tiles, and the matching 8-byte V^T reads), so the contraction runs at the
 // full-rate 32-deep instruction.  fp8 codes are converted to bf16 exactly
-// after the LDS read; the K scale folds into the score scale, the V scale
-// into the final divide.
+// after the LDS read, and so are int8 codes; the K scale folds into the score
+// scale, the V scale into the final divide.
 //
 // Work-group order: groups of 8 (sequence, KV head) pairs x all row tiles,
 // the pair fastest; work-groups go to the 8 XCDs round-robin, so each XCD
@@ -45,13 +45,18 @@ namespace {
 
 constexpr int kPfWaves = 4;
 constexpr int kPfNT = kPrefillRows / (16 * kPfWaves);   // column tiles per wave (3)
-constexpr int kPfStages = 3;
+#ifndef PKV_PREFILL_STAGES
+#define PKV_PREFILL_STAGES 3
+#endif
+constexpr int kPfStages = PKV_PREFILL_STAGES;           // LDS ring of block pairs
+constexpr int kPfAhead = kPfStages - 1;                 // pairs in flight ahead of the one computed
+static_assert(kPfAhead >= 1 && kPfAhead <= 3, "the wait counts cover up to 3 pairs in flight");
 constexpr int kPfIdWindow = 2048;                       // block ids held in LDS at a time
 constexpr int kPfXcds = 8;
 constexpr float kLazyMax = 8.f;                         // exp2 units the running max may lag
 
 template <int KVT, int D> struct PfGeom {
-    static constexpr int EB = KVT == KV_FP8 ? 1 : 2;
+    static constexpr int EB = KVT == KV_BF16 ? 2 : 1;
     static constexpr int TILE = 16 * D * EB;               // one K or V tile
     static constexpr int PAIR = 4 * TILE;                  // K_A, V_A, K_B, V_B
     static constexpr int LOADS = PAIR / 1024 / kPfWaves;   // 1 KiB wave loads per wave per pair
@@ -107,8 +112,8 @@ __device__ __forceinline__ u32x4 pf_v_op(const uint8_t* va, const uint8_t* vb, i
         const int off = (16 * m + col) * 16 + lg * 4;
         const unsigned x = *reinterpret_cast<const unsigned*>(va + off);
         const unsigned y = *reinterpret_cast<const unsigned*>(vb + off);
-        return u32x4{fp8x2_to_bf16x2<false>(x), fp8x2_to_bf16x2<true>(x), fp8x2_to_bf16x2<false>(y),
-                     fp8x2_to_bf16x2<true>(y)};
+        return u32x4{byte2_to_bf16x2<KVT, false>(x), byte2_to_bf16x2<KVT, true>(x), byte2_to_bf16x2<KVT, false>(y),
+                     byte2_to_bf16x2<KVT, true>(y)};
     }
 }
 
@@ -168,7 +173,7 @@ void attn_prefill_kernel(PrefillArgs a) {
 
     float sscale = a.score_scale;
     float vscale = 1.f;
-    if constexpr (KVT == KV_FP8) {
+    if constexpr (kv_scaled<KVT>()) {
         sscale *= a.k_scale[a.layer * H + h];
         vscale = a.v_scale[a.layer * H + h];
     }
@@ -222,18 +227,21 @@ void attn_prefill_kernel(PrefillArgs a) {
     };
     load_window(0);
     __syncthreads();
-    issue(0);
-    if (npair > 1) issue(1);
+#pragma unroll
+    for (int q = 0; q < kPfAhead; ++q)
+        if (q < npair) issue(q);
 
     for (int p = 0; p < npair; ++p) {
-        // This wave's pieces of pair p have landed (pair p+1 may still be in
-        // flight); the barrier makes every wave's pieces visible and ensures
-        // pair p-1's stage is no longer read.
-        if (p + 1 < npair) __builtin_amdgcn_s_waitcnt(vmcnt_imm<Gm::LOADS>());
+        // This wave's pieces of pair p have landed (the next pairs may still
+        // be in flight); the barrier makes every wave's pieces visible and
+        // ensures pair p-1's stage is no longer read.
+        const int later = min(kPfAhead - 1, npair - 1 - p);   // pairs issued after p
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * Gm::LOADS>());
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm<Gm::LOADS>());
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
         __builtin_amdgcn_s_barrier();
-        if (p + 2 < npair) {
-            const int q = p + 2;
+        if (p + kPfAhead < npair) {
+            const int q = p + kPfAhead;
             if (min(2 * q + 1, nblk - 1) >= win_lo + kPfIdWindow) {
                 // next window of ids: drain, swap, publish (once per 2048 blocks)
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
@@ -350,6 +358,7 @@ hipError_t launch_pf(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, hipStream_t stream) {
     if (kv_dtype == KV_BF16) return head_dim == 128 ? launch_pf<KV_BF16, 128>(a, stream) : launch_pf<KV_BF16, 64>(a, stream);
+    if (kv_dtype == KV_INT8) return head_dim == 128 ? launch_pf<KV_INT8, 128>(a, stream) : launch_pf<KV_INT8, 64>(a, stream);
     return head_dim == 128 ? launch_pf<KV_FP8, 128>(a, stream) : launch_pf<KV_FP8, 64>(a, stream);
 }
 

@@ -45,9 +45,11 @@ Conventions (readings recorded in the design notes):
 * draw order: lengths, placement, Q, prefill K/V (materialised workloads
   only), new-token K/V;
 * softmax scale 1/sqrt(d);
-* fp8 scales: materialised workloads use amax/448 of each head's prefilled
-  values (K and V separately); full-size workloads whose pool is filled on the
-  device use (4/448) * (1 + h/8) for head h with codes drawn as e4m3(x*448/4).
+* fp8 / int8 scales: materialised workloads use amax/448 (amax/127 for int8)
+  of each head's prefilled values (K and V separately); full-size workloads
+  whose pool is filled on the device use (4/448) * (1 + h/8) (int8:
+  (4/127) * (1 + h/8)) for head h with codes drawn as e4m3(x*448/4) (int8:
+  round(x*127/4) saturated to +-127).
 
 Seeds: 293000 + config number (c1 -> 293001, ...; pf, pfs -> 293006).
 """
@@ -69,7 +71,7 @@ class Workload:
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
-    kv_dtype: str                 # "f32" | "bf16" | "fp8"
+    kv_dtype: str                 # "f32" | "bf16" | "fp8" | "int8"
     q_dtype: str                  # "f32" | "bf16"
     out_dtype: str                # "f32" | "bf16"
     k_rows: int                   # query rows per sequence (1 = decode)
@@ -90,7 +92,7 @@ class Workload:
     pre_positions: Optional[np.ndarray] = None
     k_pre: Optional[np.ndarray] = None
     v_pre: Optional[np.ndarray] = None
-    k_scale: Optional[np.ndarray] = None   # float32 [L][H_kv] (fp8 only)
+    k_scale: Optional[np.ndarray] = None   # float32 [L][H_kv] (fp8 and int8 only)
     v_scale: Optional[np.ndarray] = None
     shared_prefix_tokens: int = 0
     info: dict = field(default_factory=dict)
@@ -195,16 +197,17 @@ def build(name, seed, rng, seq_lens, *, num_q_heads, num_kv_heads, head_dim, kv_
     v_new = _cast(rng.standard_normal((T_new, Hkv, d), dtype=np.float32), in_dtype)
 
     k_scale = v_scale = None
-    if kv_dtype == "fp8":
+    if kv_dtype in ("fp8", "int8"):
+        qmax = np.float32(448.0 if kv_dtype == "fp8" else 127.0)
         if materialize:
             kv = values_f32(k_pre, in_dtype) if k_pre.shape[0] else np.ones((1, Hkv, d), np.float32)
             vv = values_f32(v_pre, in_dtype) if v_pre.shape[0] else np.ones((1, Hkv, d), np.float32)
             k_amax = np.abs(kv).max(axis=(0, 2))
             v_amax = np.abs(vv).max(axis=(0, 2))
-            k_scale = (k_amax / np.float32(448.0)).astype(np.float32)[None, :]
-            v_scale = (v_amax / np.float32(448.0)).astype(np.float32)[None, :]
+            k_scale = (k_amax / qmax).astype(np.float32)[None, :]
+            v_scale = (v_amax / qmax).astype(np.float32)[None, :]
         else:
-            base = np.float32(4.0 / 448.0)
+            base = np.float32(4.0) / qmax
             per_head = (base * (1.0 + np.arange(Hkv, dtype=np.float32) / 8.0)).astype(np.float32)
             k_scale = per_head[None, :].copy()
             v_scale = per_head[None, :].copy()
@@ -227,11 +230,15 @@ def _uniform(rng, lo, hi, size):
     return rng.integers(lo, hi, size=size, endpoint=True)
 
 
-def make(name, materialize=None, seed=None):
+def make(name, materialize=None, seed=None, kv_dtype=None):
     """Build workload `name` (c1..c5 full size, c2s..c5s reduced; pf / pfs:
-    chunked prefill, full size / reduced)."""
+    chunked prefill, full size / reduced; a trailing "i8" (c2i8, c5si8, ...)
+    keeps the config but stores the KV cache as int8)."""
     if name in ("pf", "pfs"):
         return _make_prefill(name, materialize, seed)
+    if name.endswith("i8"):
+        # int8 KV variant of a config: same seed, lengths and placement
+        return make(name[:-2], materialize, seed, kv_dtype="int8")
     num = int(name[1])
     seed = SEED_BASE + num if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -246,40 +253,40 @@ def make(name, materialize=None, seed=None):
     if name == "c2":
         lens = _uniform(rng, 512, 4096, 64)
         return build(name, seed, rng, lens, num_q_heads=32, num_kv_heads=8, head_dim=128,
-                     kv_dtype="bf16", materialize=materialize, partition_tokens=512)
+                     kv_dtype=kv_dtype or "bf16", materialize=materialize, partition_tokens=512)
     if name == "c2s":
         lens = _uniform(rng, 17, 700, 6)
         return build(name, seed, rng, lens, num_q_heads=32, num_kv_heads=8, head_dim=128,
-                     kv_dtype="bf16", materialize=materialize, partition_tokens=128)
+                     kv_dtype=kv_dtype or "bf16", materialize=materialize, partition_tokens=128)
     if name == "c3":
         lens = np.concatenate([_uniform(rng, 128, 1024, 179), _uniform(rng, 4096, 32768, 77)])
         lens = lens[rng.permutation(lens.shape[0])]
         return build(name, seed, rng, lens, num_q_heads=64, num_kv_heads=8, head_dim=128,
-                     kv_dtype="bf16", materialize=materialize, partition_tokens=512)
+                     kv_dtype=kv_dtype or "bf16", materialize=materialize, partition_tokens=512)
     if name == "c3s":
         lens = np.concatenate([_uniform(rng, 16, 200, 7), _uniform(rng, 600, 1500, 3)])
         lens = lens[rng.permutation(lens.shape[0])]
         return build(name, seed, rng, lens, num_q_heads=64, num_kv_heads=8, head_dim=128,
-                     kv_dtype="bf16", materialize=materialize, partition_tokens=256)
+                     kv_dtype=kv_dtype or "bf16", materialize=materialize, partition_tokens=256)
     if name == "c4":
         lens = np.full(4, 131072)
         return build(name, seed, rng, lens, num_q_heads=32, num_kv_heads=8, head_dim=128,
-                     kv_dtype="bf16", materialize=materialize, partition_tokens=512)
+                     kv_dtype=kv_dtype or "bf16", materialize=materialize, partition_tokens=512)
     if name == "c4s":
         lens = np.full(2, 4100)
         return build(name, seed, rng, lens, num_q_heads=32, num_kv_heads=8, head_dim=128,
-                     kv_dtype="bf16", materialize=materialize, partition_tokens=512)
+                     kv_dtype=kv_dtype or "bf16", materialize=materialize, partition_tokens=512)
     if name == "c5":
         suffix = _uniform(rng, 64, 1024, 128)
         lens = 2048 + suffix + 5
         return build(name, seed, rng, lens, num_q_heads=32, num_kv_heads=8, head_dim=128,
-                     kv_dtype="fp8", k_rows=5, shared_prefix_tokens=2048,
+                     kv_dtype=kv_dtype or "fp8", k_rows=5, shared_prefix_tokens=2048,
                      materialize=materialize, partition_tokens=512)
     if name == "c5s":
         suffix = _uniform(rng, 5, 100, 6)
         lens = 256 + suffix + 5
         return build(name, seed, rng, lens, num_q_heads=32, num_kv_heads=8, head_dim=128,
-                     kv_dtype="fp8", k_rows=5, shared_prefix_tokens=256,
+                     kv_dtype=kv_dtype or "fp8", k_rows=5, shared_prefix_tokens=256,
                      materialize=materialize, partition_tokens=128)
     raise ValueError(name)
 
@@ -315,7 +322,8 @@ def fill_pool_random(pool_u8, kv_dtype, seed, num_kv_heads=None):
 
     bf16/f32 pools get N(0, 1) in every element.  fp8 pools get
     e4m3(x * 448 / 4) codes of N(0, 1) draws, i.e. values x * scale / (4/448)
-    under the per-head scales ``build`` assigns to unmaterialised workloads.
+    under the per-head scales ``build`` assigns to unmaterialised workloads;
+    int8 pools get round(x * 127 / 4) saturated to +-127.
     Used for full-size workloads whose prefilled cache is too large to draw on
     the host; the oracle reads the filled pool back.
     """
@@ -326,6 +334,15 @@ def fill_pool_random(pool_u8, kv_dtype, seed, num_kv_heads=None):
         pool_u8.view(torch.float32).normal_(generator=g)
     elif kv_dtype == "bf16":
         pool_u8.view(torch.bfloat16).normal_(generator=g)
+    elif kv_dtype == "int8":
+        chunk = 1 << 26
+        flat = pool_u8.view(-1)
+        for start in range(0, flat.numel(), chunk):
+            part = flat[start:start + chunk]
+            x = torch.randn(part.numel(), generator=g, device=pool_u8.device,
+                            dtype=torch.float32) * (127.0 / 4.0)
+            x = torch.round(x).clamp(-127.0, 127.0)
+            part.copy_(x.to(torch.int8).view(torch.uint8))
     elif kv_dtype == "fp8":
         chunk = 1 << 26
         flat = pool_u8.view(-1)
