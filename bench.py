@@ -40,6 +40,10 @@ WORKLOAD_NAMES = {
     "c2": "llama3-8b-decode-layer bf16 kv, 32q/8kv heads, d128, block16, batch64, ctx U[512,4096]",
     "c3": "llama3-70b-decode-layer bf16 kv, 64q/8kv heads, d128, block16, batch256, ctx 179xU[128,1024]+77xU[4096,32768]",
     "c4": "long-context split-kv bf16 kv, 32q/8kv heads, d128, block16, batch4, ctx 131072, 512-token partitions",
+    "c2i8": "llama3-8b-decode-layer int8 kv (per-head scales), 32q/8kv heads, d128, block16, batch64, "
+            "ctx U[512,4096]",
+    "c5": "speculative verify fp8 kv, 32q/8kv heads, d128, block16, batch128, k=5 rows, "
+          "2048-token shared prefix + U[64,1024] private",
     "pf": "llama3-8b chunked-prefill layer bf16 kv, 32q/8kv heads, d128, block16, batch8, "
           "2048-token chunks after cached prefixes U[0,14336]",
 }
@@ -65,7 +69,7 @@ def parse():
 
 
 def kv_bytes(w):
-    elem = {"f32": 4, "bf16": 2, "fp8": 1}[w.kv_dtype]
+    elem = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[w.kv_dtype]
     return int(w.seq_lens.astype("int64").sum()) * 2 * w.num_kv_heads * w.head_dim * elem
 
 
@@ -77,23 +81,24 @@ def cpu_baseline(w, pool_image, budget_s):
     from oracle import pool as opool
 
     desc = opool.PoolDesc(w.num_layers, w.num_blocks, w.num_kv_heads, w.head_dim, w.kv_dtype)
-    q = opool.bf16_bits_to_float(w.q[:, 0]) if w.q_dtype == "bf16" else w.q[:, 0].astype(np.float64)
+    q = opool.bf16_bits_to_float(w.q) if w.q_dtype == "bf16" else w.q.astype(np.float64)
     done, tokens = 0, 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         for s in range(w.batch):
-            oatt.decode(desc, pool_image, w.layer, w.block_tables, w.seq_lens, q, w.scale,
+            oatt.verify(desc, pool_image, w.layer, w.block_tables, w.seq_lens, q, w.k_rows, w.scale,
                         w.k_scale, w.v_scale, seqs=[s])
             done += 1
             tokens += int(w.seq_lens[s])
             if time.perf_counter() - t0 > budget_s:
                 break
         dt = time.perf_counter() - t0
-    elem = {"f32": 4, "bf16": 2, "fp8": 1}[w.kv_dtype]
+    elem = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[w.kv_dtype]
     nbytes = tokens * 2 * w.num_kv_heads * w.head_dim * elem
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seqs_per_s": round(done / dt, 3),
-            "sample": f"float64 numpy oracle decode of the first {done} of {w.batch} sequences "
+            "sample": f"float64 numpy oracle {'decode' if w.k_rows == 1 else f'{w.k_rows}-row verify'} "
+                      f"of the first {done} of {w.batch} sequences "
                       f"({tokens} tokens, {dt:.1f} s, one thread)"}
 
 
@@ -120,7 +125,7 @@ def main():
     P = w.partition_tokens if args.partition is None else args.partition
 
     ks = vs = None
-    if w.kv_dtype == "fp8":
+    if w.kv_dtype in ("fp8", "int8"):
         ks = torch.from_numpy(w.k_scale).to(dev)
         vs = torch.from_numpy(w.v_scale).to(dev)
     pools = []
@@ -137,14 +142,18 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
         return torch.from_numpy(np.ascontiguousarray(x, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    q = dev_raw(w.q[:, 0], w.q_dtype)
+    kq = w.k_rows
+    q = dev_raw(w.q[:, 0] if kq == 1 else w.q, w.q_dtype)
     k_new = dev_raw(w.k_new, w.in_dtype)
     v_new = dev_raw(w.v_new, w.in_dtype)
     sid = torch.from_numpy(w.new_seq_ids).to(dev)
     pos = torch.from_numpy(w.new_positions).to(dev)
     slots = torch.empty(sid.numel(), dtype=torch.int64, device=dev)
     out = torch.empty(q.shape, dtype=torch.bfloat16 if w.kv_dtype != "f32" else torch.float32, device=dev)
-    ws_bytes = pk.paged_attention_workspace_bytes(pools[0], table, w.num_q_heads, 1)
+    if kq > 1:
+        k_new = k_new.view(w.batch, kq, w.num_kv_heads, w.head_dim)
+        v_new = v_new.view(w.batch, kq, w.num_kv_heads, w.head_dim)
+    ws_bytes = pk.paged_attention_workspace_bytes(pools[0], table, w.num_q_heads, kq)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     scale = w.scale
 
@@ -158,8 +167,10 @@ def main():
             pk.reshape_and_cache(pool, w.layer, k_new, v_new, slots)
         if timed:
             ev[i][0].record()
-        if args.separate:
+        if args.separate and kq == 1:
             pk.paged_attention_decode(pool, w.layer, table, q, scale, workspace=ws, out=out)
+        elif args.separate:
+            pk.paged_attention_verify(pool, w.layer, table, q, scale, workspace=ws, out=out)
         else:
             pk.paged_attention_append(pool, w.layer, table, k_new, v_new, q, scale, workspace=ws, out=out)
         if timed:
@@ -213,7 +224,9 @@ def main():
         "config": {"workload": WORKLOAD_NAMES[args.workload], "batch": w.batch,
                    "step": "slot_mapping_compute + reshape_and_cache + paged_attention_decode" if args.separate
                            else "paged_attention_append (slot mapping, append and attention in one launch)",
-                   "tokens": int(w.seq_lens.sum()), "partition_tokens": P,
+                   "tokens": int(w.seq_lens.sum()), "query_rows": kq, "partition_tokens": P,
+                   "unique_kv_bytes": int(w.info["blocks_used"]) * 16 * 2 * w.num_kv_heads * w.head_dim
+                                      * {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[w.kv_dtype],
                    "pools_rotated": len(pools), "work_units": info["num_units"]},
         "seqs_per_s": round(w.batch / (ms_step * 1e-3), 1),
         "pct_hbm_peak_step": round(100.0 * value / HBM_PEAK_GBS, 2),

@@ -131,8 +131,9 @@ int32_t auto_unit_blocks(const std::vector<int32_t>& nblk, int32_t num_kv_heads)
 
 // Build the plan.  partition_tokens > 0: fixed partitions of that many tokens
 // (the last one of a sequence shorter); 0: one partition per sequence; -1:
-// balanced, every sequence cut into near-equal parts of at most
-// auto_unit_blocks() blocks.  Units are ordered longest first.
+// balanced, every sequence cut into near-equal parts of about
+// auto_unit_blocks() blocks (no part under 2 * kAutoMinItemBlocks when the
+// batch alone fills the device).  Units are ordered longest first.
 bool build_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, int32_t partition_tokens,
                 int32_t num_kv_heads, Plan* P) {
     if (num_seqs < 1 || max_blocks < 1) return false;
@@ -144,9 +145,18 @@ bool build_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, i
         nblk[s] = (n + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
     }
     int32_t unit_blocks;
+    int32_t min_part = 1;   // balanced plan: smallest part a sequence is cut into
     if (partition_tokens > 0) unit_blocks = partition_tokens / PKV_BLOCK_SIZE;
     else if (partition_tokens == 0) unit_blocks = max_blocks;
-    else unit_blocks = auto_unit_blocks(nblk, num_kv_heads);
+    else {
+        unit_blocks = auto_unit_blocks(nblk, num_kv_heads);
+        // When whole sequences already give every resident work-group an item,
+        // cutting them further only balances the long ones: parts stay at
+        // 2 * kAutoMinItemBlocks or more (each part costs a partial result and
+        // its merge, more so with many query rows).
+        const int64_t slots = static_cast<int64_t>(device_cu_count()) * pkv::kAutoWgsPerCu;
+        if (static_cast<int64_t>(num_seqs) * num_kv_heads >= slots) min_part = 2 * pkv::kAutoMinItemBlocks;
+    }
 
     struct U { int32_t seq, b0, nb, part, parts; };
     std::vector<U> us;
@@ -155,7 +165,7 @@ bool build_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, i
     P->max_parts = 0;
     P->stride = 0;
     for (int32_t s = 0; s < num_seqs; ++s) {
-        const int32_t parts = (nblk[s] + unit_blocks - 1) / unit_blocks;
+        const int32_t parts = std::max(1, std::min((nblk[s] + unit_blocks - 1) / unit_blocks, nblk[s] / min_part));
         P->seq_parts[2 * s] = parts;
         if (parts > 1) {
             P->seq_parts[2 * s + 1] = P->num_split_slots;
