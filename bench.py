@@ -46,8 +46,10 @@ WORKLOAD_NAMES = {
           "2048-token shared prefix + U[64,1024] private",
     "pf": "llama3-8b chunked-prefill layer bf16 kv, 32q/8kv heads, d128, block16, batch8, "
           "2048-token chunks after cached prefixes U[0,14336]",
+    "sp": "speculative acceptance: batch128, 4 drafted tokens + bonus row, vocab 128256, float32 p and q",
 }
 PREFILL_METRIC = "chunked-prefill paged attention TFLOP/s (causal, visible query-key pairs only)"
+SPEC_METRIC = "exact speculative acceptance, sequences/s (Llama-3 vocabulary, 4 drafted tokens)"
 
 
 def parse():
@@ -112,6 +114,8 @@ def main():
 
     if args.workload == "pf":
         return run_prefill(args)
+    if args.workload == "sp":
+        return run_speculative(args)
 
     import numpy as np
     import torch
@@ -378,6 +382,64 @@ def prefill_cpu_baseline(w, pool_image, budget_s):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
             "sample": f"float64 numpy oracle prefill of the last {done} of {C} chunk rows of sequence 0 "
                       f"(n = {n}, all {w.num_q_heads} query heads, {dt:.1f} s, one thread)"}
+
+
+def run_speculative(args):
+    """One step: speculative_accept over the batch (inputs resident in HBM)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_293_amd as pk
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = workloads.make_spec("sp")
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    p, q, draft, ua, us = t(w.p), t(w.q), t(w.draft), t(w.u_accept), t(w.u_sample)
+    na = torch.empty(w.batch, dtype=torch.int32, device=dev)
+    toks = torch.empty(w.batch, w.k + 1, dtype=torch.int32, device=dev)
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        pk.speculative_accept(p, q, draft, ua, us, na, toks)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(K):
+        pk.speculative_accept(p, q, draft, ua, us, na, toks)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / K
+    acc = na.cpu().numpy()
+    # algorithmic bytes: the 2K tested entries, then one row (two for a residual)
+    nbytes = int(sum(8 * w.k + (2 if a < w.k else 1) * 4 * w.vocab for a in acc))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": SPEC_METRIC, "value": round(w.batch / (ms * 1e-3), 1), "unit": "sequences/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded logits, softmax p and q, draft tokens drawn from q, uniform draws)",
+        "config": {"workload": WORKLOAD_NAMES["sp"], "batch": w.batch, "draft_tokens": w.k, "vocab": w.vocab,
+                   "mean_accepted": round(float(acc.mean()), 3)},
+        "bytes_per_step": nbytes, "wall_s": round(wall, 3),
+        "roofline": {"bound": "hbm", "kernel": "speculative_accept_kernel", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import speculative as osp
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0) and done < w.batch:
+            osp.accept_sequence(w.p[done], w.q[done], w.draft[done], w.u_accept[done], w.u_sample[done])
+            done += 1
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(done / dt, 1), "unit": "sequences/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"float64 numpy oracle on the first {done} of {w.batch} sequences, "
+                                            f"{dt:.1f} s, one thread"}
+    print(json.dumps(result), flush=True)
 
 
 def _kernel_digest():

@@ -326,6 +326,38 @@ pkv_status paged_attention_prefill(const pkv_pool* pool, int32_t layer, const pk
                                    int32_t num_q_heads, float scale, void* dev_out, int32_t out_dtype,
                                    void* stream);
 
+/*
+ * Exact speculative acceptance (page "LLM Serving - KV Cache, Batching,
+ * Speculative Decoding", section "Speculative decoding: distribution and
+ * break-even"; page "KV cache & continuous batching", section "5. Speculative
+ * decoding").  For each sequence the draft proposed K = draft_tokens tokens
+ * x_0..x_{K-1} from its distributions q_0..q_{K-1}, and one target pass (the
+ * verify attention above) gave p_0..p_K.  Position i accepts x_i with
+ * probability min(1, p_i(x_i) / q_i(x_i)), decided as the float32 test
+ * u_accept[i] * q_i(x_i) < p_i(x_i); a draft token outside [0, vocab) is
+ * rejected.  The first rejected position a emits a token drawn from
+ * max(p_a - q_a, 0) (p_a itself if that has no mass); a fully accepted block
+ * (a = K) emits a bonus token drawn from p_K.  Drawing from weights w with u:
+ * the smallest j with w_0 + .. + w_j > u * sum(w), sums in float32.  The
+ * emitted tokens follow the target's distribution.
+ *   dev_p         float32 [num_seqs][K+1][vocab] target probabilities
+ *   dev_q         float32 [num_seqs][K][vocab] draft probabilities
+ *                 (both 16-byte aligned; rows need not sum to exactly 1)
+ *   dev_draft     int32 [num_seqs][K]
+ *   dev_u_accept  float32 [num_seqs][K] uniforms in [0, 1)
+ *   dev_u_sample  float32 [num_seqs] uniforms in [0, 1)
+ *   dev_num_accepted  int32 [num_seqs] out: a
+ *   dev_tokens    int32 [num_seqs][K+1] out: x_0..x_{a-1}, the drawn token, then -1
+ * One work-group per sequence reads the K tested entries and one row (two
+ * for a residual).  Errors: PKV_ERR_INVALID (null or misaligned pointer,
+ * draft_tokens < 1, vocab < 1), PKV_ERR_UNSUPPORTED (draft_tokens > 1024),
+ * PKV_ERR_HIP.
+ */
+pkv_status speculative_accept(const float* dev_p, const float* dev_q, const int32_t* dev_draft,
+                              const float* dev_u_accept, const float* dev_u_sample, int32_t num_seqs,
+                              int32_t draft_tokens, int32_t vocab, int32_t* dev_num_accepted,
+                              int32_t* dev_tokens, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

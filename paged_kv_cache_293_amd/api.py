@@ -256,3 +256,24 @@ def paged_attention_prefill(pool, layer, table, q, scale=None, out=None, out_dty
         pool.handle, int(layer), table.handle, _ptr(q), BF16, int(C), int(Hq), float(scale),
         _ptr(out), _TORCH_CODE[out.dtype], _stream(q.device)))
     return out
+
+
+def speculative_accept(p, q, draft, u_accept, u_sample, num_accepted=None, tokens=None):
+    """Exact speculative acceptance: p [B][K+1][V], q [B][K][V] float32,
+    draft [B][K] int32, u_accept [B][K], u_sample [B] float32 uniforms in
+    [0, 1).  Returns (num_accepted [B], tokens [B][K+1]) int32 tensors."""
+    B, K1, V = p.shape
+    K = K1 - 1
+    assert q.shape == (B, K, V) and draft.shape == (B, K) and u_accept.shape == (B, K)
+    assert u_sample.shape == (B,)
+    for t, dt in ((p, torch.float32), (q, torch.float32), (u_accept, torch.float32), (u_sample, torch.float32),
+                  (draft, torch.int32)):
+        assert t.is_cuda and t.is_contiguous() and t.dtype == dt
+    if num_accepted is None:
+        num_accepted = torch.empty(B, dtype=torch.int32, device=p.device)
+    if tokens is None:
+        tokens = torch.empty(B, K + 1, dtype=torch.int32, device=p.device)
+    _check("speculative_accept", lib.speculative_accept(
+        _ptr(p), _ptr(q), _ptr(draft), _ptr(u_accept), _ptr(u_sample), int(B), int(K), int(V),
+        _ptr(num_accepted), _ptr(tokens), _stream(p.device)))
+    return num_accepted, tokens

@@ -614,6 +614,32 @@ pkv_status paged_attention_prefill(const pkv_pool* pool, int32_t layer, const pk
     return hip_status(pkv::launch_prefill(a, kvt, pool->desc.head_dim, static_cast<hipStream_t>(stream)));
 }
 
+pkv_status speculative_accept(const float* dev_p, const float* dev_q, const int32_t* dev_draft,
+                              const float* dev_u_accept, const float* dev_u_sample, int32_t num_seqs,
+                              int32_t draft_tokens, int32_t vocab, int32_t* dev_num_accepted, int32_t* dev_tokens,
+                              void* stream) {
+    if (num_seqs < 0 || draft_tokens < 1 || vocab < 1) return PKV_ERR_INVALID;
+    if (num_seqs == 0) return PKV_OK;
+    if (!dev_p || !dev_q || !dev_draft || !dev_u_accept || !dev_u_sample || !dev_num_accepted || !dev_tokens)
+        return PKV_ERR_INVALID;
+    if (draft_tokens > 1024) return PKV_ERR_UNSUPPORTED;
+    // float4 reads of the rows need 16-byte aligned rows
+    if (reinterpret_cast<uintptr_t>(dev_p) % 16 || reinterpret_cast<uintptr_t>(dev_q) % 16) return PKV_ERR_INVALID;
+    pkv::SpecArgs a;
+    a.p = dev_p;
+    a.q = dev_q;
+    a.draft = dev_draft;
+    a.u_accept = dev_u_accept;
+    a.u_sample = dev_u_sample;
+    a.num_accepted = dev_num_accepted;
+    a.tokens = dev_tokens;
+    a.seg_len = pkv::speculative_segment_len(vocab);
+    a.num_seqs = num_seqs;
+    a.k = draft_tokens;
+    a.vocab = vocab;
+    return hip_status(pkv::launch_speculative_accept(a, static_cast<hipStream_t>(stream)));
+}
+
 pkv_status paged_attention_decode(const pkv_pool* pool, int32_t layer, const pkv_table* table, const void* dev_q,
                                   int32_t q_dtype, int32_t num_q_heads, float scale, void* dev_workspace,
                                   size_t workspace_bytes, void* dev_out, int32_t out_dtype, void* stream) {

@@ -116,6 +116,24 @@ struct PrefillArgs {
 // Launch the prefill kernel; kv_dtype is KV_BF16 or KV_FP8, head_dim 64 or 128.
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, hipStream_t stream);
 
+// Exact speculative acceptance (see speculative.hip).
+struct SpecArgs {
+    const float* p;              // [B][K+1][V] target probabilities
+    const float* q;              // [B][K][V] draft probabilities
+    const int32_t* draft;        // [B][K] drafted tokens
+    const float* u_accept;       // [B][K] uniforms of the acceptance tests
+    const float* u_sample;       // [B] uniform of the emitted draw
+    int32_t* num_accepted;       // [B] out
+    int32_t* tokens;             // [B][K+1] out: accepted drafts, the draw, then -1
+    int64_t seg_len;             // weights per wave segment (speculative_segment_len)
+    int32_t num_seqs;
+    int32_t k;
+    int32_t vocab;
+};
+
+hipError_t launch_speculative_accept(const SpecArgs& a, hipStream_t stream);
+int64_t speculative_segment_len(int64_t vocab);
+
 struct CacheArgs {
     uint8_t* pool;
     const float* k_scale;

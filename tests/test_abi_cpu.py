@@ -143,6 +143,9 @@ def test_calls_without_handles_are_refused(pk):
     assert lib.paged_attention_decode(nul, 0, nul, nul, 1, 8, 1.0, nul, 0, nul, 1, nul) == -1
     assert lib.paged_attention_verify(nul, 0, nul, nul, 1, 2, 8, 1.0, nul, 0, nul, 1, nul) == -1
     assert lib.paged_attention_prefill(nul, 0, nul, nul, 1, 64, 8, 1.0, nul, 1, nul) == -1
+    assert lib.speculative_accept(nul, nul, nul, nul, nul, 4, 4, 1000, nul, nul, nul) == -1
+    assert lib.speculative_accept(nul, nul, nul, nul, nul, 4, 0, 1000, nul, nul, nul) == -1
+    assert lib.speculative_accept(nul, nul, nul, nul, nul, 0, 4, 1000, nul, nul, nul) == 0   # nothing to do
     assert lib.reshape_and_cache(nul, 0, nul, nul, 1, nul, 4, nul) == -1
     assert lib.slot_mapping_compute(nul, nul, nul, 4, nul, nul) == -1
     assert lib.paged_attention_workspace_bytes(nul, nul, 8, 1) == 0

@@ -354,3 +354,65 @@ def fill_pool_random(pool_u8, kv_dtype, seed, num_kv_heads=None):
             part.copy_(x.to(torch.float8_e4m3fn).view(torch.uint8))
     else:
         raise ValueError(kv_dtype)
+
+
+# ------------------------------------------------- speculative acceptance
+
+@dataclass
+class SpecWorkload:
+    """Inputs of one exact speculative-acceptance step (no method arithmetic:
+    seeded logits, their softmax, draft tokens drawn from q, and uniforms)."""
+    name: str
+    seed: int
+    p: np.ndarray          # float32 [B][K+1][V]
+    q: np.ndarray          # float32 [B][K][V]
+    draft: np.ndarray      # int32 [B][K]
+    u_accept: np.ndarray   # float32 [B][K]
+    u_sample: np.ndarray   # float32 [B]
+
+    @property
+    def batch(self):
+        return int(self.draft.shape[0])
+
+    @property
+    def k(self):
+        return int(self.draft.shape[1])
+
+    @property
+    def vocab(self):
+        return int(self.p.shape[2])
+
+
+def _softmax32(logits):
+    z = logits - logits.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return (e / e.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+
+def make_spec(name, seed=None, batch=None, k=None, vocab=None):
+    """sp: 128 sequences, 4 drafted tokens (+ the bonus row), Llama-3's
+    128,256-token vocabulary; sps: 7 sequences, vocabulary 1000.  Target
+    logits are N(0, 3^2); the draft's are the target's plus N(0, 0.7^2) noise,
+    so a drafted token is accepted about 70% of the time (page "LLM Inference
+    Optimization: KV Cache, Batching, and Speculative Decoding", section
+    "Speculative Decoding", puts good drafts at 60-80%).  Draft tokens are drawn
+    from q with the generator (an input of the step, not part of it)."""
+    seed = SEED_BASE + 7 if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, K, V = (128, 4, 128256) if name == "sp" else (7, 4, 1000)
+    B = batch or B
+    K = k or K
+    V = vocab or V
+    lp = rng.standard_normal((B, K + 1, V), dtype=np.float32) * np.float32(3.0)
+    lq = lp[:, :K] + rng.standard_normal((B, K, V), dtype=np.float32) * np.float32(0.7)
+    p = _softmax32(lp)
+    q = _softmax32(lq)
+    cq = np.cumsum(q.astype(np.float64), axis=-1)
+    r = rng.random((B, K))
+    draft = np.empty((B, K), dtype=np.int32)
+    for b in range(B):
+        for i in range(K):
+            draft[b, i] = min(int(np.searchsorted(cq[b, i], r[b, i] * cq[b, i, -1], side="right")), V - 1)
+    u_accept = rng.random((B, K), dtype=np.float32)
+    u_sample = rng.random(B, dtype=np.float32)
+    return SpecWorkload(name, seed, p, q, draft, u_accept, u_sample)
