@@ -58,6 +58,7 @@ typedef int32_t pkv_status;
 #define PKV_ERR_SEQ_LEN     (-4) /* seq_len < 1, > table capacity, or < rows   */
 #define PKV_ERR_WORKSPACE   (-5) /* device buffer or workspace too small       */
 #define PKV_ERR_HIP         (-6) /* the HIP runtime reported an error          */
+#define PKV_ERR_OUT_OF_BLOCKS (-7) /* block manager: not enough free blocks     */
 
 /* Element types. */
 #define PKV_F32      0  /* IEEE binary32                                        */
@@ -357,6 +358,88 @@ pkv_status speculative_accept(const float* dev_p, const float* dev_q, const int3
                               const float* dev_u_accept, const float* dev_u_sample, int32_t num_seqs,
                               int32_t draft_tokens, int32_t vocab, int32_t* dev_num_accepted,
                               int32_t* dev_tokens, void* stream);
+
+/*
+ * Block copies for copy-on-write (see the block manager below): for each pair
+ * (src, dst) of dev_pairs (int32 [num_pairs][2]), every layer's K and V tiles
+ * of physical block src, all KV heads, are copied to block dst.  Pairs with
+ * an id outside [0, num_blocks) or src == dst are skipped.  Pairs must not
+ * overlap (no block both written and read by the call).
+ */
+pkv_status kv_copy_blocks(const pkv_pool* pool, const int32_t* dev_pairs, int32_t num_pairs, void* stream);
+
+/*
+ * Block manager (host only, no device memory): hands out the pool's physical
+ * blocks (page "KV cache & continuous batching", section "Visual: the
+ * lifecycle of a request in continuous batching": 16-token blocks, a finished
+ * request frees its blocks at once; section "2. PagedAttention (vLLM)":
+ * blocks allocated on demand, one table per request; section "4. Prefix
+ * caching / prompt caching": prefix blocks hashed and reused across requests;
+ * page "LLM Serving - KV Cache, Batching, Speculative Decoding", section "KV
+ * memory, paging and prefix identity": shared physical blocks, reuse only for
+ * the exact token prefix, a salt separates tenants).
+ *   Reuse: a full block is registered under the chain of (previous block,
+ *   salt, its 16 token ids); a new request takes the longest run of leading
+ *   registered blocks that match exactly (token ids compared), but at most
+ *   len-1 tokens (its last prompt token is always computed).  Freed blocks
+ *   stay findable until handed out again; allocation takes the least
+ *   recently freed block first.
+ *   Forks share every block; an append into a partial block that another
+ *   sequence also holds moves the appending sequence to a fresh block first
+ *   and reports the (src, dst) pair for kv_copy_blocks, which the caller runs
+ *   before writing the new tokens.
+ * A manager is driven from one host thread.  Sequence ids are the caller's.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* A manager of num_blocks blocks (all free).  Errors: PKV_ERR_INVALID. */
+pkv_status block_manager_create(int32_t num_blocks, pkv_block_manager** out);
+pkv_status block_manager_destroy(pkv_block_manager* manager);
+
+/* Free blocks (registered or not), or -1 for a NULL manager. */
+int32_t block_manager_free_blocks(const pkv_block_manager* manager);
+
+/* Reference count of a physical block (sequences holding it), or -1. */
+int32_t block_manager_refcount(const pkv_block_manager* manager, int32_t block);
+
+/*
+ * A new sequence with its prompt tokens host_tokens[num_tokens] (token ids).
+ *   *out_cached_tokens  leading tokens whose K/V is already in the pool
+ *                       (a multiple of 16, < num_tokens);
+ *   out_slots           int64 [num_tokens - cached]: slots of the remaining
+ *                       tokens, for reshape_and_cache.
+ * Errors: PKV_ERR_INVALID (NULL, num_tokens < 1, seq_id in use),
+ * PKV_ERR_OUT_OF_BLOCKS (nothing changed).
+ */
+pkv_status block_manager_add(pkv_block_manager* manager, int64_t seq_id, const int32_t* host_tokens,
+                             int32_t num_tokens, uint64_t salt, int32_t* out_cached_tokens,
+                             int64_t* out_slots);
+
+/*
+ * Append num_tokens generated tokens: out_slots int64 [num_tokens]; if the
+ * sequence's partial last block is shared, *out_num_copies = 1 and
+ * out_copies[0..1] = (src, dst) (out_copies may be NULL only when no copy
+ * can arise); else *out_num_copies = 0.  Errors: PKV_ERR_INVALID,
+ * PKV_ERR_OUT_OF_BLOCKS (nothing changed).
+ */
+pkv_status block_manager_append(pkv_block_manager* manager, int64_t seq_id, const int32_t* host_tokens,
+                                int32_t num_tokens, int64_t* out_slots, int32_t* out_copies,
+                                int32_t* out_num_copies);
+
+/* A new sequence child_id sharing every block of parent_id. */
+pkv_status block_manager_fork(pkv_block_manager* manager, int64_t parent_id, int64_t child_id);
+
+/* Finish a sequence: its blocks' reference counts drop, blocks at 0 are free. */
+pkv_status block_manager_free(pkv_block_manager* manager, int64_t seq_id);
+
+/*
+ * The block-table batch of the given sequences, for block_table_upload:
+ * out_table int32 [num_seqs][max_blocks_per_seq] (unused entries -1),
+ * out_seq_lens int32 [num_seqs].  Errors: PKV_ERR_INVALID (unknown id),
+ * PKV_ERR_SEQ_LEN (a sequence needs more than max_blocks_per_seq blocks).
+ */
+pkv_status block_manager_table(const pkv_block_manager* manager, const int64_t* seq_ids, int32_t num_seqs,
+                               int32_t max_blocks_per_seq, int32_t* out_table, int32_t* out_seq_lens);
 
 #ifdef __cplusplus
 }

@@ -11,7 +11,7 @@ from ._lib import (  # noqa: F401
     BLOCK_SIZE, F32, BF16, FP8_E4M3, INT8, LIB_PATH, PagedKVError, lib,
 )
 from .api import (  # noqa: F401
-    BlockTable, KVPool, block_table_upload, kv_bytes_per_token, kv_pool_bytes,
+    BlockManager, BlockTable, KVPool, block_table_upload, kv_bytes_per_token, kv_copy_blocks, kv_pool_bytes,
     kv_pool_create, paged_attention_append, paged_attention_decode, paged_attention_prefill,
     paged_attention_verify,
     paged_attention_workspace_bytes, reshape_and_cache, slot_mapping_compute, speculative_accept,

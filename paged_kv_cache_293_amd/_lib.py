@@ -56,6 +56,16 @@ PROTOTYPES = {
     "paged_attention_prefill": (_c_int32, [_vp, _c_int32, _vp, _vp, _c_int32, _c_int32, _c_int32, ctypes.c_float,
                                            _vp, _c_int32, _vp]),
     "speculative_accept": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _vp, _vp, _vp]),
+    "kv_copy_blocks": (_c_int32, [_vp, _vp, _c_int32, _vp]),
+    "block_manager_create": (_c_int32, [_c_int32, ctypes.POINTER(_vp)]),
+    "block_manager_destroy": (_c_int32, [_vp]),
+    "block_manager_free_blocks": (_c_int32, [_vp]),
+    "block_manager_refcount": (_c_int32, [_vp, _c_int32]),
+    "block_manager_add": (_c_int32, [_vp, _c_int64, _vp, _c_int32, ctypes.c_uint64, ctypes.POINTER(_c_int32), _vp]),
+    "block_manager_append": (_c_int32, [_vp, _c_int64, _vp, _c_int32, _vp, _vp, ctypes.POINTER(_c_int32)]),
+    "block_manager_fork": (_c_int32, [_vp, _c_int64, _c_int64]),
+    "block_manager_free": (_c_int32, [_vp, _c_int64]),
+    "block_manager_table": (_c_int32, [_vp, _vp, _c_int32, _c_int32, _vp, _vp]),
 }
 
 

@@ -277,3 +277,73 @@ def speculative_accept(p, q, draft, u_accept, u_sample, num_accepted=None, token
         _ptr(p), _ptr(q), _ptr(draft), _ptr(u_accept), _ptr(u_sample), int(B), int(K), int(V),
         _ptr(num_accepted), _ptr(tokens), _stream(p.device)))
     return num_accepted, tokens
+
+
+def kv_copy_blocks(pool, pairs):
+    """Copy blocks (all layers, heads, K and V): pairs int32 CUDA tensor [n][2] of (src, dst)."""
+    assert pairs.is_cuda and pairs.dtype == torch.int32 and pairs.is_contiguous()
+    n = pairs.numel() // 2
+    _check("kv_copy_blocks", lib.kv_copy_blocks(pool.handle, _ptr(pairs), int(n), _stream(pairs.device)))
+
+
+def _np_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class BlockManager:
+    """Host block manager of a pool's physical blocks (see the C header for
+    the policy).  Token ids are int32; sequence ids are the caller's."""
+
+    def __init__(self, num_blocks):
+        h = ctypes.c_void_p()
+        _check("block_manager_create", lib.block_manager_create(int(num_blocks), ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = int(num_blocks)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib.block_manager_destroy(h)
+            self._h = None
+
+    @property
+    def free_blocks(self):
+        return int(lib.block_manager_free_blocks(self._h))
+
+    def refcount(self, block):
+        return int(lib.block_manager_refcount(self._h, int(block)))
+
+    def add(self, seq_id, tokens, salt=0):
+        """New sequence with its prompt; returns (cached_tokens, slots of the uncached tokens)."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = np.empty(t.size, dtype=np.int64)
+        cached = ctypes.c_int32()
+        _check("block_manager_add", lib.block_manager_add(self._h, int(seq_id), _np_ptr(t), int(t.size),
+                                                          ctypes.c_uint64(int(salt)), ctypes.byref(cached),
+                                                          _np_ptr(slots)))
+        return int(cached.value), slots[:t.size - cached.value].copy()
+
+    def append(self, seq_id, tokens):
+        """Append tokens; returns (slots, copies) with copies a list of (src, dst) block pairs."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = np.empty(max(t.size, 1), dtype=np.int64)
+        copies = np.empty(2, dtype=np.int32)
+        nc = ctypes.c_int32()
+        _check("block_manager_append", lib.block_manager_append(self._h, int(seq_id), _np_ptr(t), int(t.size),
+                                                                _np_ptr(slots), _np_ptr(copies), ctypes.byref(nc)))
+        return slots[:t.size].copy(), [tuple(int(x) for x in copies[2 * i:2 * i + 2]) for i in range(nc.value)]
+
+    def fork(self, parent_id, child_id):
+        _check("block_manager_fork", lib.block_manager_fork(self._h, int(parent_id), int(child_id)))
+
+    def free(self, seq_id):
+        _check("block_manager_free", lib.block_manager_free(self._h, int(seq_id)))
+
+    def table(self, seq_ids, max_blocks):
+        """(table int32 [n][max_blocks], seq_lens int32 [n]) for block_table_upload."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        tab = np.empty((ids.size, int(max_blocks)), dtype=np.int32)
+        lens = np.empty(ids.size, dtype=np.int32)
+        _check("block_manager_table", lib.block_manager_table(self._h, _np_ptr(ids), int(ids.size), int(max_blocks),
+                                                              _np_ptr(tab), _np_ptr(lens)))
+        return tab, lens

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libpagedkv.so")
-SOURCES = ["api.cpp", "attention.hip", "cache.hip", "prefill.hip", "speculative.hip"]
+SOURCES = ["api.cpp", "block_manager.cpp", "attention.hip", "cache.hip", "prefill.hip", "speculative.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

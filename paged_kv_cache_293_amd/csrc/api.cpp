@@ -242,6 +242,7 @@ const char* pkv_status_string(pkv_status s) {
         case PKV_ERR_SEQ_LEN: return "sequence length out of range";
         case PKV_ERR_WORKSPACE: return "device buffer or workspace too small";
         case PKV_ERR_HIP: return "HIP runtime error";
+        case PKV_ERR_OUT_OF_BLOCKS: return "not enough free blocks";
         default: return "unknown status";
     }
 }
@@ -612,6 +613,20 @@ pkv_status paged_attention_prefill(const pkv_pool* pool, int32_t layer, const pk
     a.score_scale = scale * 1.4426950408889634f;
     const int32_t kvt = kv;   // PKV_* element codes equal the kernels' KV_* codes
     return hip_status(pkv::launch_prefill(a, kvt, pool->desc.head_dim, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status kv_copy_blocks(const pkv_pool* pool, const int32_t* dev_pairs, int32_t num_pairs, void* stream) {
+    if (!pool || num_pairs < 0) return PKV_ERR_INVALID;
+    if (num_pairs == 0) return PKV_OK;
+    if (!dev_pairs) return PKV_ERR_INVALID;
+    pkv::CopyArgs a;
+    a.pool = pool->base;
+    a.pairs = dev_pairs;
+    a.num_pairs = num_pairs;
+    a.num_blocks = pool->desc.num_blocks;
+    a.num_layers = pool->desc.num_layers;
+    a.block_bytes = static_cast<int64_t>(pool->desc.num_kv_heads) * 2 * pool->tile_bytes;
+    return hip_status(pkv::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
 }
 
 pkv_status speculative_accept(const float* dev_p, const float* dev_q, const int32_t* dev_draft,

@@ -48,6 +48,18 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(SlotArgs a) {
     a.slots[t] = slot;
 }
 
+// Copy one block of one layer (all KV heads, K and V tiles: one contiguous run
+// of block_bytes) for the pair blockIdx.x, layer blockIdx.y.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
+    const int src = a.pairs[2 * blockIdx.x];
+    const int dst = a.pairs[2 * blockIdx.x + 1];
+    if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks || src == dst) return;
+    const int64_t layer_base = static_cast<int64_t>(blockIdx.y) * a.num_blocks * a.block_bytes;
+    const uint4* s = reinterpret_cast<const uint4*>(a.pool + layer_base + src * a.block_bytes);
+    uint4* d = reinterpret_cast<uint4*>(a.pool + layer_base + dst * a.block_bytes);
+    for (int64_t i = threadIdx.x; i < a.block_bytes / 16; i += blockDim.x) d[i] = s[i];
+}
+
 template <int KVT, int IN>
 hipError_t launch_cache_dim(const CacheArgs& a, hipStream_t stream) {
     if (a.head_dim == 128)
@@ -68,6 +80,12 @@ hipError_t launch_reshape_and_cache(const CacheArgs& a, int kv_dtype, int in_dty
                                   : launch_cache_dim<KV_INT8, KV_BF16>(a, stream);
     if (in_dtype == KV_F32) return launch_cache_dim<KV_FP8, KV_F32>(a, stream);
     return launch_cache_dim<KV_FP8, KV_BF16>(a, stream);
+}
+
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream) {
+    if (a.num_pairs <= 0) return hipSuccess;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(a.num_pairs, a.num_layers), dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_slot_mapping(const SlotArgs& a, hipStream_t stream) {

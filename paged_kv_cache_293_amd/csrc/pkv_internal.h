@@ -166,4 +166,16 @@ struct SlotArgs {
 
 hipError_t launch_slot_mapping(const SlotArgs& a, hipStream_t stream);
 
+// Whole-block copies for copy-on-write: every layer of block src -> block dst.
+struct CopyArgs {
+    uint8_t* pool;
+    const int32_t* pairs;        // [n][2] (src, dst)
+    int64_t block_bytes;         // H_kv * 2 * tile bytes: one block of one layer
+    int32_t num_pairs;
+    int32_t num_blocks;
+    int32_t num_layers;
+};
+
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
+
 }  // namespace pkv

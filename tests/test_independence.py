@@ -28,7 +28,7 @@ def test_oracle_imports_no_product_code():
     used = _imports(os.path.join(ROOT, "oracle"))
     assert "paged_kv_cache_293_amd" not in used
     assert "workloads" not in used
-    assert used <= {"numpy", "math", "fractions"}
+    assert used <= {"numpy", "math", "fractions", "collections"}
 
 
 def test_product_imports_no_oracle():
