@@ -129,11 +129,54 @@ int32_t auto_unit_blocks(const std::vector<int32_t>& nblk, int32_t num_kv_heads)
     return std::min(hi, pkv::kAutoMaxBlocks);
 }
 
+// Unit order for a grid with one work-group per item.  Every work-group is
+// then resident from the start, and (measured on MI355X) work-groups w and
+// w + C, C the number of CUs, run on the same CU; a CU streams its
+// work-groups' blocks at about the same rate whatever their split, so the
+// kernel ends when the CU with the most blocks is done.  Units (given longest
+// first, sizes from nb(i)) are placed one by one, longest first, at the free
+// position whose items' CUs would carry the smallest maximum load: the
+// greedy longest-processing-time rule over CUs.  Returns order[position] =
+// unit; the identity when the items exceed the resident work-groups (the
+// work-groups then take items from the queue, longest first).
+template <class NB>
+std::vector<int32_t> place_on_cus(size_t num_units, int32_t num_kv_heads, NB nb) {
+    std::vector<int32_t> order(num_units);
+    for (size_t i = 0; i < num_units; ++i) order[i] = static_cast<int32_t>(i);
+    const int64_t cus = device_cu_count();
+    const int64_t items = static_cast<int64_t>(num_units) * num_kv_heads;
+    if (num_units < 2 || items > cus * pkv::kAutoWgsPerCu) return order;
+    const int U = static_cast<int>(num_units);
+    std::vector<int64_t> load(static_cast<size_t>(cus), 0);
+    std::vector<char> used(num_units, 0);
+    std::vector<int32_t> cu_of(num_units * static_cast<size_t>(num_kv_heads));
+    for (int p = 0; p < U; ++p)
+        for (int h = 0; h < num_kv_heads; ++h)
+            cu_of[static_cast<size_t>(p) * num_kv_heads + h] =
+                static_cast<int32_t>(pkv::item_of(p, h, U, num_kv_heads) % cus);
+    for (int i = 0; i < U; ++i) {
+        const int64_t w = nb(static_cast<size_t>(i));
+        int best = -1;
+        int64_t best_max = 0;
+        for (int p = 0; p < U; ++p) {
+            if (used[p]) continue;
+            int64_t m = 0;
+            for (int h = 0; h < num_kv_heads; ++h) m = std::max(m, load[cu_of[static_cast<size_t>(p) * num_kv_heads + h]]);
+            if (best < 0 || m < best_max) { best = p; best_max = m; }
+        }
+        used[best] = 1;
+        order[best] = i;
+        for (int h = 0; h < num_kv_heads; ++h) load[cu_of[static_cast<size_t>(best) * num_kv_heads + h]] += w;
+    }
+    return order;
+}
+
 // Build the plan.  partition_tokens > 0: fixed partitions of that many tokens
 // (the last one of a sequence shorter); 0: one partition per sequence; -1:
 // balanced, every sequence cut into near-equal parts of about
 // auto_unit_blocks() blocks (no part under 2 * kAutoMinItemBlocks when the
-// batch alone fills the device).  Units are ordered longest first.
+// batch alone fills the device).  Units are ordered longest first, or placed
+// by place_on_cus() when the grid has a work-group per item.
 bool build_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, int32_t partition_tokens,
                 int32_t num_kv_heads, Plan* P) {
     if (num_seqs < 1 || max_blocks < 1) return false;
@@ -187,6 +230,12 @@ bool build_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, i
         }
     }
     std::stable_sort(us.begin(), us.end(), [](const U& x, const U& y) { return x.nb > y.nb; });
+    const std::vector<int32_t> order = place_on_cus(us.size(), num_kv_heads, [&](size_t i) { return us[i].nb; });
+    {
+        std::vector<U> placed(us.size());
+        for (size_t pos = 0; pos < us.size(); ++pos) placed[pos] = us[order[pos]];
+        us.swap(placed);
+    }
     P->num_units = static_cast<int32_t>(us.size());
     P->units.assign(static_cast<size_t>(P->num_units) * pkv::kUnitInts, 0);
     for (size_t i = 0; i < us.size(); ++i) {

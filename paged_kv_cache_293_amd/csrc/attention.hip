@@ -402,54 +402,57 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     __syncthreads();
     if (*ticket_s != parts - 1) return;
     const int64_t sl0 = static_cast<int64_t>(h) * a.num_split_slots + (slot - ud[kUnitPart]);
-    float* Mr = m_s;          // [R] reused: the common max of each row
-    float* Lr = m_s + R;      // [R] and its sum
+    // The partials' (m, l) go to LDS in one parallel pass (every load in
+    // flight at once: these loads travel to the coherent level, so a chain of
+    // them would cost a round trip each); acc_s is free now and holds
+    // 2 * parts * R <= R * (D + 1) floats for parts <= kFuseMaxParts.
+    float* pm = acc_s;                // [parts][R] maxima, then the partition weights
+    float* pw = acc_s + parts * R;    // [parts][R] sums
+    float* Lr = m_s;                  // [R] common sum of each row
+    for (int e = tid; e < parts * R; e += 64 * kWaves) {
+        pm[e] = xwg_load(a.part_m + sl0 * R + e);
+        pw[e] = xwg_load(a.part_l + sl0 * R + e);
+    }
+    __syncthreads();
     for (int r = tid; r < R; r += 64 * kWaves) {
         float M = neg_inf();
-        for (int q = 0; q < parts; ++q) M = fmaxf(M, xwg_load(a.part_m + (sl0 + q) * R + r));
+        for (int q = 0; q < parts; ++q) M = fmaxf(M, pm[q * R + r]);
         float L = 0.f;
-        for (int q = 0; q < parts; ++q)
-            L += xwg_load(a.part_l + (sl0 + q) * R + r) * fast_exp2(xwg_load(a.part_m + (sl0 + q) * R + r) - M);
-        Mr[r] = M;
+        for (int q = 0; q < parts; ++q) {
+            const float wq = fast_exp2(pm[q * R + r] - M);
+            L += pw[q * R + r] * wq;
+            pm[q * R + r] = wq;       // weight of partition q for row r
+        }
         Lr[r] = L;
     }
     __syncthreads();
     for (int e = tid; e < R * D; e += 64 * kWaves) {
         const int r = e / D;
         const int d = e % D;
-        const float M = Mr[r];
         float O = 0.f;
-        for (int q = 0; q < parts; ++q)
-            O += xwg_load(a.part_o + ((sl0 + q) * R + r) * D + d) * fast_exp2(xwg_load(a.part_m + (sl0 + q) * R + r) - M);
+        for (int q0 = 0; q0 < parts; q0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = q0 + u < parts ? xwg_load(a.part_o + ((sl0 + q0 + u) * R + r) * D + d) : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (q0 + u < parts) O += v[u] * pm[(q0 + u) * R + r];
+        }
         store_out(a, seq, h, r, d, O / Lr[r] * vscale);
     }
     if (tid == 0)   // ready for the next call
         __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Item i -> (unit, KV head).  Items come in groups of kXcds units x H_kv heads
-// (the last group may hold fewer units); within a group the unit is the
-// fastest index.  Work-groups are handed to the XCDs round-robin by index, so
-// in the first round every head of a unit runs on the same XCD, which then
-// reads the unit's blocks whole (all heads of a block are adjacent) and
-// touches fewer pages.  Units are numbered longest first, and so are groups.
-constexpr int kXcds = 8;
-__device__ __forceinline__ void item_coords(int item, int num_units, int hkv, int& unit, int& h) {
-    const int group = item / (kXcds * hkv);
-    const int r = item - group * kXcds * hkv;
-    const int in_group = min(kXcds, num_units - group * kXcds);
-    h = r / in_group;
-    unit = group * kXcds + (r - h * in_group);
-}
-
 // Persistent work-groups: work-group b first takes item b, then items
 // gridDim.x, gridDim.x + 1, ... in the order they are claimed from the
 // queue, until none is left; a work-group claims its next item when it has
-// read all blocks of the current one.  Items are ordered longest unit first.  Every
-// work-group leaves the loop after exactly one claim past the end; the last
-// to leave sets both queue counters back to zero for the next call.  When the
-// grid has a work-group per item nothing is claimed and the queue is not
-// touched.  No work-group ever waits for another.
+// read all blocks of the current one.  Every work-group leaves the loop
+// after exactly one claim past the end; the last to leave sets both queue
+// counters back to zero for the next call.  When the grid has a work-group
+// per item nothing is claimed and the queue is not touched.  No work-group
+// ever waits for another.
 template <int KVT, int D, int NT>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NT == 1 ? (KVT == KV_F32 ? 1 : 3) : (NT == 2 && KVT != KV_F32 ? 2 : 1))))
 void attn_partition_kernel(AttnArgs a) {
@@ -479,11 +482,15 @@ void attn_partition_kernel(AttnArgs a) {
         int tid = wave_s * 64 + static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
         asm volatile("" : "+v"(tid));
         attend_item<KVT, D, NT>(ia, unit, h, smem, &ticket, claimed, tid);
-        if (threadIdx.x == 0) next_item = static_cast<int>(gridDim.x) + claimed;
+        if (tid == 0) next_item = static_cast<int>(gridDim.x) + claimed;
         __syncthreads();   // next_item visible; this item's LDS reads are done
         item = next_item;
     }
-    if (threadIdx.x == 0 && a.num_items > static_cast<int>(gridDim.x)) {
+    // Thread 0 found again from the wave index and the lane, so the thread
+    // index is not held across the loop.
+    const bool first_thread =
+        wave_s == 0 && __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) == 0;
+    if (first_thread && a.num_items > static_cast<int>(gridDim.x)) {
         // The claim that ended the loop has returned before this add is issued,
         // so when the last work-group counts itself no claim is outstanding.
         const int left = __hip_atomic_fetch_add(a.queue + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

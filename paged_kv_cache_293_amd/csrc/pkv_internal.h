@@ -43,6 +43,28 @@ constexpr int kAutoMinItemBlocks = PKV_AUTO_MIN_ITEM_BLOCKS;
 constexpr int kAutoMinBlocks = 8;
 constexpr int kAutoMaxBlocks = 256;
 
+// Item i -> (unit, KV head).  Items come in groups of kXcds units x H_kv heads
+// (the last group may hold fewer units); within a group the unit is the
+// fastest index.  Work-groups are handed to the XCDs round-robin by index, so
+// in the first round every head of a unit runs on the same XCD, which then
+// reads the unit's blocks whole (all heads of a block are adjacent) and
+// touches fewer pages.
+constexpr int kXcds = 8;
+__host__ __device__ inline void item_coords(int item, int num_units, int hkv, int& unit, int& h) {
+    const int group = item / (kXcds * hkv);
+    const int r = item - group * kXcds * hkv;
+    const int in_group = num_units - group * kXcds < kXcds ? num_units - group * kXcds : kXcds;
+    h = r / in_group;
+    unit = group * kXcds + (r - h * in_group);
+}
+
+// The inverse: the item of (unit, KV head).
+__host__ __device__ inline int item_of(int unit, int h, int num_units, int hkv) {
+    const int group = unit / kXcds;
+    const int in_group = num_units - group * kXcds < kXcds ? num_units - group * kXcds : kXcds;
+    return group * kXcds * hkv + h * in_group + (unit - group * kXcds);
+}
+
 // Everything the attention kernel reads; built by the host per call.
 struct AttnArgs {
     const uint8_t* pool;         // pool base

@@ -57,3 +57,25 @@ def test_append_full_size_bench_configuration(name):
     s, ref, got, fused_store = _both_routes(w, P=-1, poison=False)
     assert torch.equal(fused_store, s.pool.storage)
     assert torch.equal(got, ref)
+
+
+# Appends spanning several blocks and unit boundaries, every pool type, and
+# row counts on both sides of 32 (up to 32 rows the appended positions fall in
+# each wave's first tile; beyond, any tile may hold them).  Sequence lengths
+# put the first appended position at offsets 0, 1, 15 of a block, and the
+# 32-token partitions cut several sequences into units.
+@pytest.mark.parametrize("kv,k,Hq,Hkv,d", [
+    ("bf16", 1, 8, 2, 128), ("bf16", 8, 16, 4, 128), ("bf16", 9, 32, 8, 128),
+    ("bf16", 33, 8, 8, 64), ("fp8", 17, 8, 4, 128), ("int8", 12, 32, 8, 64),
+    ("f32", 6, 8, 2, 128), ("f32", 20, 4, 2, 64),
+])
+def test_append_multi_block_rows(kv, k, Hq, Hkv, d):
+    log(f"append multi-block kv={kv} k={k} {Hq}/{Hkv} d{d}")
+    lens = [k, k + 1, k + 15, 16 + k, 17 + k, 47 + k, 200, 321]
+    w = workloads.custom(4100 + 7 * k + d, lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, kv_dtype=kv,
+                         k_rows=k, partition_tokens=32)
+    for P in (32, -1, 0):
+        s, ref, got, fused_store = _both_routes(w, P=P)
+        assert torch.equal(fused_store, s.pool.storage), f"pool bytes differ (P={P})"
+        assert torch.equal(got, ref), f"outputs differ (P={P})"
+    assert_close(out_values(got), s.oracle(), kv, f"append multi-block {kv} k={k}")
