@@ -101,10 +101,10 @@ int device_cu_count() {
 }
 
 // Blocks per unit for the balanced plan: the smallest unit size whose plan has
-// at most kAutoWgsPerCu work-groups per CU over all KV heads, kept within
+// at most wgs_per_cu work-groups per CU over all KV heads, kept within
 // [kAutoMinBlocks, kAutoMaxBlocks].
-int32_t auto_unit_blocks(const std::vector<int32_t>& nblk, int32_t num_kv_heads) {
-    const int64_t slots = static_cast<int64_t>(device_cu_count()) * pkv::kAutoWgsPerCu;
+int32_t auto_unit_blocks(const std::vector<int32_t>& nblk, int32_t num_kv_heads, int32_t wgs_per_cu) {
+    const int64_t slots = static_cast<int64_t>(device_cu_count()) * wgs_per_cu;
     int64_t total = 0;
     for (int32_t b : nblk) total += b;
     total *= std::max(1, num_kv_heads);
@@ -140,12 +140,12 @@ int32_t auto_unit_blocks(const std::vector<int32_t>& nblk, int32_t num_kv_heads)
 // unit; the identity when the items exceed the resident work-groups (the
 // work-groups then take items from the queue, longest first).
 template <class NB>
-std::vector<int32_t> place_on_cus(size_t num_units, int32_t num_kv_heads, NB nb) {
+std::vector<int32_t> place_on_cus(size_t num_units, int32_t num_kv_heads, int32_t wgs_per_cu, NB nb) {
     std::vector<int32_t> order(num_units);
     for (size_t i = 0; i < num_units; ++i) order[i] = static_cast<int32_t>(i);
     const int64_t cus = device_cu_count();
     const int64_t items = static_cast<int64_t>(num_units) * num_kv_heads;
-    if (num_units < 2 || items > cus * pkv::kAutoWgsPerCu) return order;
+    if (num_units < 2 || items > cus * wgs_per_cu) return order;
     const int U = static_cast<int>(num_units);
     std::vector<int64_t> load(static_cast<size_t>(cus), 0);
     std::vector<char> used(num_units, 0);
@@ -178,7 +178,7 @@ std::vector<int32_t> place_on_cus(size_t num_units, int32_t num_kv_heads, NB nb)
 // batch alone fills the device).  Units are ordered longest first, or placed
 // by place_on_cus() when the grid has a work-group per item.
 bool build_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, int32_t partition_tokens,
-                int32_t num_kv_heads, Plan* P) {
+                int32_t num_kv_heads, int32_t wgs_per_cu, Plan* P) {
     if (num_seqs < 1 || max_blocks < 1) return false;
     if (partition_tokens < -1 || (partition_tokens > 0 && partition_tokens % PKV_BLOCK_SIZE)) return false;
     std::vector<int32_t> nblk(num_seqs);
@@ -192,12 +192,12 @@ bool build_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, i
     if (partition_tokens > 0) unit_blocks = partition_tokens / PKV_BLOCK_SIZE;
     else if (partition_tokens == 0) unit_blocks = max_blocks;
     else {
-        unit_blocks = auto_unit_blocks(nblk, num_kv_heads);
+        unit_blocks = auto_unit_blocks(nblk, num_kv_heads, wgs_per_cu);
         // When whole sequences already give every resident work-group an item,
         // cutting them further only balances the long ones: parts stay at
         // 2 * kAutoMinItemBlocks or more (each part costs a partial result and
         // its merge, more so with many query rows).
-        const int64_t slots = static_cast<int64_t>(device_cu_count()) * pkv::kAutoWgsPerCu;
+        const int64_t slots = static_cast<int64_t>(device_cu_count()) * wgs_per_cu;
         if (static_cast<int64_t>(num_seqs) * num_kv_heads >= slots) min_part = 2 * pkv::kAutoMinItemBlocks;
     }
 
@@ -230,7 +230,8 @@ bool build_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, i
         }
     }
     std::stable_sort(us.begin(), us.end(), [](const U& x, const U& y) { return x.nb > y.nb; });
-    const std::vector<int32_t> order = place_on_cus(us.size(), num_kv_heads, [&](size_t i) { return us[i].nb; });
+    const std::vector<int32_t> order =
+        place_on_cus(us.size(), num_kv_heads, wgs_per_cu, [&](size_t i) { return us[i].nb; });
     {
         std::vector<U> placed(us.size());
         for (size_t pos = 0; pos < us.size(); ++pos) placed[pos] = us[order[pos]];
@@ -343,7 +344,8 @@ size_t block_table_device_bytes(const pkv_pool* pool, const int32_t* host_seq_le
     try {
         if (!pool || !host_seq_lens) return 0;
         Plan P;
-        if (!build_plan(host_seq_lens, num_seqs, max_blocks_per_seq, partition_tokens, pool->desc.num_kv_heads, &P))
+        if (!build_plan(host_seq_lens, num_seqs, max_blocks_per_seq, partition_tokens, pool->desc.num_kv_heads,
+                        pkv::decode_wgs_per_cu(pool->desc.kv_dtype, pool->desc.head_dim), &P))
             return 0;
         return table_layout(num_seqs, max_blocks_per_seq, pool->desc.num_kv_heads, P).total;
     } catch (...) {
@@ -381,7 +383,8 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
             }
         }
         Plan P;
-        if (!build_plan(host_seq_lens, num_seqs, max_blocks_per_seq, partition_tokens, hkv, &P))
+        if (!build_plan(host_seq_lens, num_seqs, max_blocks_per_seq, partition_tokens, hkv,
+                        pkv::decode_wgs_per_cu(pool->desc.kv_dtype, pool->desc.head_dim), &P))
             return PKV_ERR_INVALID;
         const TableLayout L = table_layout(num_seqs, max_blocks_per_seq, hkv, P);
         if (dev_buffer_bytes < L.total) return PKV_ERR_WORKSPACE;

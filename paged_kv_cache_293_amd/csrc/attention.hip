@@ -306,15 +306,35 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             return tile_rsrc(head_base + static_cast<int64_t>(pid) * block_stride, valid ? a.tile_bytes : 0);
         };
         TileRegs<KVT, D> ta, tb;
-        ta.load(rsrc(0, true), koff, voff);
-        int i = 0;
-        for (; i + 1 < cnt; i += 2) {
-            tb.load(rsrc(i + 1, true), koff, voff);
-            process(ta, logical(base + kWaves * i));
-            ta.load(rsrc(i + 2, i + 2 < cnt), koff, voff);
-            process(tb, logical(base + kWaves * (i + 1)));
+        if constexpr (NT == 1 && decode_depth(KVT, D) == 2) {
+            // Three buffers: while a wave processes one block the next two
+            // are in flight.
+            TileRegs<KVT, D> tc;
+            ta.load(rsrc(0, true), koff, voff);
+            tb.load(rsrc(1, cnt > 1), koff, voff);
+            int i = 0;
+            for (; i + 2 < cnt; i += 3) {
+                tc.load(rsrc(i + 2, true), koff, voff);
+                process(ta, logical(base + kWaves * i));
+                ta.load(rsrc(i + 3, i + 3 < cnt), koff, voff);
+                process(tb, logical(base + kWaves * (i + 1)));
+                tb.load(rsrc(i + 4, i + 4 < cnt), koff, voff);
+                process(tc, logical(base + kWaves * (i + 2)));
+            }
+            if (i < cnt) process(ta, logical(base + kWaves * i));
+            if (i + 1 < cnt) process(tb, logical(base + kWaves * (i + 1)));
+        } else {
+            // Two buffers: one block in flight while the other is processed.
+            ta.load(rsrc(0, true), koff, voff);
+            int i = 0;
+            for (; i + 1 < cnt; i += 2) {
+                tb.load(rsrc(i + 1, true), koff, voff);
+                process(ta, logical(base + kWaves * i));
+                ta.load(rsrc(i + 2, i + 2 < cnt), koff, voff);
+                process(tb, logical(base + kWaves * (i + 1)));
+            }
+            if (i < cnt) process(ta, logical(base + kWaves * i));
         }
-        if (i < cnt) process(ta, logical(base + kWaves * i));
     }
 
     // This work-group's blocks are read: claim its next item now, while the
@@ -454,7 +474,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
 // per item nothing is claimed and the queue is not touched.  No work-group
 // ever waits for another.
 template <int KVT, int D, int NT>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NT == 1 ? (KVT == KV_F32 ? 1 : 3) : (NT == 2 && KVT != KV_F32 ? 2 : 1))))
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NT == 1 ? decode_wgs_per_cu(KVT, D) : (NT == 2 && KVT != KV_F32 ? 2 : 1))))
 void attn_partition_kernel(AttnArgs a) {
     extern __shared__ float smem[];
     __shared__ int ticket;

@@ -26,7 +26,7 @@ constexpr int kUnitInts = 8;
 constexpr int kFuseMaxParts = 32;
 
 // Balanced plan: units sized so the batch gives up to kAutoItemsPerWg
-// (unit, KV head) items per resident work-group (kAutoWgsPerCu per CU), as
+// (unit, KV head) items per resident work-group (decode_wgs_per_cu() per CU), as
 // many as keep units at kAutoMinItemBlocks blocks or more, with units of
 // kAutoMinBlocks .. kAutoMaxBlocks blocks.  The attention kernel's
 // work-groups take items from a queue, so work-groups that drain early (the
@@ -37,7 +37,14 @@ constexpr int kFuseMaxParts = 32;
 #ifndef PKV_AUTO_MIN_ITEM_BLOCKS
 #define PKV_AUTO_MIN_ITEM_BLOCKS 96
 #endif
-constexpr int kAutoWgsPerCu = 3;
+// Decode-kernel instances with one row tile (R <= 16), per KV dtype (PKV_*
+// code) and head dim: the prefetch depth (tiles a wave has in flight while it
+// processes one) and the waves per SIMD it is built for, which is also its
+// resident work-groups per CU (a work-group is one wave on each SIMD).  At
+// d = 128 a deeper pipeline with two waves per SIMD streams faster than three
+// waves with one tile in flight each.
+constexpr int decode_depth(int kv, int d) { return kv != 0 && d == 128 ? 2 : 1; }
+constexpr int decode_wgs_per_cu(int kv, int d) { return kv == 0 ? 1 : (d == 128 ? 2 : 3); }
 constexpr int kAutoItemsPerWg = PKV_AUTO_ITEMS_PER_WG;
 constexpr int kAutoMinItemBlocks = PKV_AUTO_MIN_ITEM_BLOCKS;
 constexpr int kAutoMinBlocks = 8;
