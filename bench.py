@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1, "int4": 0.5}   # bytes per stored element
 METRIC = "paged decode attention KV GB/s (% HBM peak) + seqs/s, Llama-3-8B GQA shapes"
 WORKLOAD_NAMES = {
     "c2": "llama3-8b-decode-layer bf16 kv, 32q/8kv heads, d128, block16, batch64, ctx U[512,4096]",
@@ -42,6 +43,8 @@ WORKLOAD_NAMES = {
     "c4": "long-context split-kv bf16 kv, 32q/8kv heads, d128, block16, batch4, ctx 131072, 512-token partitions",
     "c2i8": "llama3-8b-decode-layer int8 kv (per-head scales), 32q/8kv heads, d128, block16, batch64, "
             "ctx U[512,4096]",
+    "c2i4": "llama3-8b-decode-layer int4 kv (per-head scales, 2 codes/byte), 32q/8kv heads, d128, block16, "
+            "batch64, ctx U[512,4096]",
     "c5": "speculative verify fp8 kv, 32q/8kv heads, d128, block16, batch128, k=5 rows, "
           "2048-token shared prefix + U[64,1024] private",
     "pf": "llama3-8b chunked-prefill layer bf16 kv, 32q/8kv heads, d128, block16, batch8, "
@@ -71,8 +74,8 @@ def parse():
 
 
 def kv_bytes(w):
-    elem = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[w.kv_dtype]
-    return int(w.seq_lens.astype("int64").sum()) * 2 * w.num_kv_heads * w.head_dim * elem
+    elem = ELEM_BYTES[w.kv_dtype]
+    return int(int(w.seq_lens.astype("int64").sum()) * 2 * w.num_kv_heads * w.head_dim * elem)
 
 
 def cpu_baseline(w, pool_image, budget_s):
@@ -95,8 +98,8 @@ def cpu_baseline(w, pool_image, budget_s):
             if time.perf_counter() - t0 > budget_s:
                 break
         dt = time.perf_counter() - t0
-    elem = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[w.kv_dtype]
-    nbytes = tokens * 2 * w.num_kv_heads * w.head_dim * elem
+    elem = ELEM_BYTES[w.kv_dtype]
+    nbytes = int(tokens * 2 * w.num_kv_heads * w.head_dim * elem)
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seqs_per_s": round(done / dt, 3),
             "sample": f"float64 numpy oracle {'decode' if w.k_rows == 1 else f'{w.k_rows}-row verify'} "
@@ -129,7 +132,7 @@ def main():
     P = w.partition_tokens if args.partition is None else args.partition
 
     ks = vs = None
-    if w.kv_dtype in ("fp8", "int8"):
+    if w.kv_dtype in ("fp8", "int8", "int4"):
         ks = torch.from_numpy(w.k_scale).to(dev)
         vs = torch.from_numpy(w.v_scale).to(dev)
     pools = []
@@ -229,8 +232,8 @@ def main():
                    "step": "slot_mapping_compute + reshape_and_cache + paged_attention_decode" if args.separate
                            else "paged_attention_append (slot mapping, append and attention in one launch)",
                    "tokens": int(w.seq_lens.sum()), "query_rows": kq, "partition_tokens": P,
-                   "unique_kv_bytes": int(w.info["blocks_used"]) * 16 * 2 * w.num_kv_heads * w.head_dim
-                                      * {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[w.kv_dtype],
+                   "unique_kv_bytes": int(int(w.info["blocks_used"]) * 16 * 2 * w.num_kv_heads * w.head_dim
+                                          * ELEM_BYTES[w.kv_dtype]),
                    "pools_rotated": len(pools), "work_units": info["num_units"]},
         "seqs_per_s": round(w.batch / (ms_step * 1e-3), 1),
         "pct_hbm_peak_step": round(100.0 * value / HBM_PEAK_GBS, 2),

@@ -70,13 +70,20 @@ typedef int32_t pkv_status;
                            f32(x) * f32(1 / scale))), NaN written as 0 (page "KV cache &
                            continuous batching", section "KV cache memory math": one
                            byte per element for fp8 or int8) */
+#define PKV_INT4     4  /* symmetric int4 code in [-7, 7] times a float32 scale per
+                           (layer, KV head); written as sat7(round-half-even(
+                           f32(x) * f32(1 / scale))), NaN written as 0; two codes per
+                           byte, low nibble first, two's complement (page "LLM
+                           Inference Optimization: KV Cache, Batching, and
+                           Speculative Decoding", section "Memory Bandwidth
+                           Optimization": int4 KV at half a byte per element) */
 
 /*
  * Pool geometry.
  *
  * The pool is one caller-owned device buffer of kv_pool_bytes(desc) bytes,
  * i.e. num_blocks * 16 token slots times the per-token size
- * 2 * num_layers * num_kv_heads * head_dim * b (b = 4, 2, 1 bytes), which is
+ * 2 * num_layers * num_kv_heads * head_dim * b (b = 4, 2, 1, 1/2 bytes), which is
  * the page-1 formula of section "KV cache memory math" applied to the pool's
  * capacity.
  *
@@ -89,9 +96,15 @@ typedef int32_t pkv_status;
  *        ((i / X) * 16 + o) * X + (i % X),   X = 16 / b,
  * i.e. 16-byte chunks of X consecutive dims, chunk-major then token.  Inside a
  * V tile, element (o, i) is element number  i * 16 + o  (V stored transposed).
+ * PKV_INT4 tiles are instead nibble arrays (nibble N = byte N / 2, low nibble
+ * when N is even), laid out so that no byte holds codes of two tokens and each
+ * of the attention kernel's 64 lanes reads one contiguous run; with
+ * W = head_dim / 4 nibbles per run:
+ *   K (o, i), i = 32 s + 8 g + e (e < 8, g < 4):   N = (g * 16 + o) * W + 8 s + e
+ *   V (o, i), o = 4 g + t, i = 16 m + c (c < 16):  N = (g * 16 + c) * W + t * (head_dim / 16) + m
  * Token position t of a sequence with block table row `bt` lives at block
  * bt[t / 16], offset t % 16; its flat slot is bt[t / 16] * 16 + t % 16.
- * For PKV_FP8_E4M3 and PKV_INT8 the stored code c of head h in layer l stands for the value
+ * For PKV_FP8_E4M3, PKV_INT8 and PKV_INT4 the stored code c of head h in layer l stands for the value
  * decode(c) * scale[l][h], with separate K and V scale arrays.
  */
 typedef struct pkv_pool_desc {
@@ -100,7 +113,7 @@ typedef struct pkv_pool_desc {
     int32_t num_kv_heads;  /* >= 1                                    */
     int32_t head_dim;      /* 64 or 128                               */
     int32_t block_size;    /* must be PKV_BLOCK_SIZE (16)             */
-    int32_t kv_dtype;      /* PKV_F32, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 */
+    int32_t kv_dtype;      /* PKV_F32, PKV_BF16, PKV_FP8_E4M3, PKV_INT8, PKV_INT4 */
 } pkv_pool_desc;
 
 typedef struct pkv_pool pkv_pool;
@@ -128,7 +141,7 @@ int64_t kv_pool_bytes(const pkv_pool_desc* desc);
  * Wrap a caller-allocated pool buffer in a handle.
  *   dev_base   device buffer of at least kv_pool_bytes(desc) bytes, 256-byte aligned.
  *   dev_k_scale, dev_v_scale  float32 [num_layers][num_kv_heads] device arrays;
- *              required (non-NULL) for PKV_FP8_E4M3 and PKV_INT8, ignored otherwise.
+ *              required (non-NULL) for PKV_FP8_E4M3, PKV_INT8 and PKV_INT4, ignored otherwise.
  * Errors: PKV_ERR_INVALID (null, short or misaligned buffer, bad counts),
  *         PKV_ERR_UNSUPPORTED (block_size != 16, head_dim not 64/128, dtype).
  * The buffer contents are not touched.
@@ -214,12 +227,13 @@ pkv_status slot_mapping_compute(const pkv_table* table, const int32_t* dev_seq_i
  * scheduling oracles").
  *   dev_k_new, dev_v_new  [num_tokens][num_kv_heads][head_dim], element type in_dtype.
  *   in_dtype     PKV_F32 for an F32 pool, PKV_BF16 for a BF16 pool, PKV_F32 or
- *                PKV_BF16 for an FP8 pool.
+ *                PKV_BF16 for an FP8, INT8 or INT4 pool.
  *   dev_slot_mapping  int64 [num_tokens]; a slot outside [0, num_blocks * 16)
  *                (e.g. -1) skips its token.  Two tokens with the same slot race.
  * F32 and BF16 pools store the input bits unchanged.  FP8 pools store
  *   e4m3( sat448( f32(x) * f32(1 / scale[layer][h]) ) )
- * with round-to-nearest-even, saturation to +-448 and NaN kept NaN.
+ * with round-to-nearest-even, saturation to +-448 and NaN kept NaN; INT8 and
+ * INT4 pools the codes their element types define.
  */
 pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, const void* dev_k_new,
                              const void* dev_v_new, int32_t in_dtype,
@@ -242,14 +256,15 @@ size_t paged_attention_workspace_bytes(const pkv_pool* pool, const pkv_table* ta
  * with K_s, V_s read from `layer` of the pool through the table's block list.
  *   dev_q    [num_seqs][num_q_heads][head_dim], q_dtype.
  *   dev_out  [num_seqs][num_q_heads][head_dim], out_dtype.
- *   q_dtype  PKV_F32 with an F32 pool; PKV_BF16 with BF16 and FP8 pools.
+ *   q_dtype  PKV_F32 with an F32 pool; PKV_BF16 with BF16, FP8, INT8 and INT4 pools.
  *   out_dtype  PKV_F32 or PKV_BF16 (round to nearest even).
  *   scale    softmax scale (typically 1/sqrt(head_dim)).
  *   dev_workspace  >= paged_attention_workspace_bytes(pool, table, num_q_heads, 1)
  *            bytes (may be NULL when that is 0); no initial contents needed.
  * num_q_heads must be a multiple of num_kv_heads with at most 64 query heads
- * per KV head.  Accumulation is float32; bf16/fp8 operands go through the
- * matrix cores with float32 accumulation, probabilities rounded to bfloat16.
+ * per KV head.  Accumulation is float32; bf16 operands (fp8, int8 and int4
+ * codes convert to bf16 exactly) go through the matrix cores with float32
+ * accumulation, probabilities rounded to bfloat16.
  * Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_BLOCK_RANGE (the table's
  * entries do not fit this pool), PKV_ERR_WORKSPACE, PKV_ERR_HIP.
  */
@@ -317,7 +332,8 @@ pkv_status paged_attention_append(const pkv_pool* pool, int32_t layer, const pkv
  * visible K/V blocks through LDS, bound by the matrix cores.
  *   dev_q    [num_seqs][C][num_q_heads][head_dim] bfloat16.
  *   dev_out  [num_seqs][C][num_q_heads][head_dim], out_dtype PKV_BF16 or PKV_F32.
- *   Pools: PKV_BF16, PKV_FP8_E4M3 or PKV_INT8 (PKV_F32 pools: PKV_ERR_UNSUPPORTED).
+ *   Pools: PKV_BF16, PKV_FP8_E4M3 or PKV_INT8 (PKV_F32 and PKV_INT4 pools:
+ *   PKV_ERR_UNSUPPORTED).
  * No workspace.  The table's split-KV plan is not used (any partition_tokens).
  * Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_SEQ_LEN (a sequence
  * shorter than C), PKV_ERR_BLOCK_RANGE, PKV_ERR_HIP.

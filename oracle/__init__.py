@@ -35,6 +35,7 @@ Modules
 ``kv_math``   byte and block arithmetic the pages print (pinned by their numbers).
 ``fp8``       OCP E4M3 codec written from the format definition.
 ``int8``      symmetric int8 codec (round half to even, saturate to +-127).
+``int4``      symmetric int4 codec (saturate to +-7), two codes per byte.
 ``pool``      host model of the pool byte layout: slot mapping, cache write, gather.
 ``attention`` float64 softmax attention over gathered K/V: decode and k-row verify.
 
@@ -43,4 +44,4 @@ Pins (what ties each function to something other than itself) live in
 docstrings.
 """
 
-from . import kv_math, fp8, int8, pool, attention  # noqa: F401
+from . import kv_math, fp8, int8, int4, pool, attention  # noqa: F401

@@ -26,7 +26,12 @@ so the oracle reads the pool from the definition, not from library code):
   (dim-major: the V tile is stored transposed);
 * b = 4 (float32), 2 (bfloat16) or 1 (fp8 E4M3, or symmetric int8, with a
   float32 scale per (layer, KV head), separately for K and V; value = code *
-  scale).
+  scale);
+* int4 (b = 1/2, same scales) instead numbers the nibbles of a tile
+  (nibble N is byte N // 2, the low half when N is even) so that no byte
+  holds two tokens; with W = d // 4:
+  K (token o, dim i = 32 s + 8 g + e):  N = (g * 16 + o) * W + 8 s + e,
+  V (token o = 4 g + t, dim i = 16 m + c):  N = (g * 16 + c) * W + t * (d // 16) + m.
 
 Pins: the layout formula is checked against hand-computed offsets stored in
 ``tests/golden/pool_layout.txt``; the slot rule against the page-1 block-table
@@ -37,10 +42,11 @@ gather against each other and against brute-force loops in the tests.
 import numpy as np
 
 from . import fp8 as _fp8
+from . import int4 as _int4
 from . import int8 as _int8
 from .kv_math import BLOCK_SIZE, slot_of
 
-DTYPE_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}
+DTYPE_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1, "int4": 0.5}
 
 
 class PoolDesc:
@@ -61,7 +67,7 @@ class PoolDesc:
 
     @property
     def tile_bytes(self):
-        return BLOCK_SIZE * self.head_dim * self.elem_bytes
+        return int(BLOCK_SIZE * self.head_dim * self.elem_bytes)
 
     @property
     def total_bytes(self):
@@ -86,8 +92,30 @@ def v_element_in_tile(desc, token, dim):
     return dim * BLOCK_SIZE + token
 
 
+def k_nibble_in_tile(desc, token, dim):
+    """int4: nibble number of K(token, dim) inside its tile."""
+    w = desc.head_dim // 4
+    s, g, e = dim // 32, (dim // 8) % 4, dim % 8
+    return (g * BLOCK_SIZE + token) * w + 8 * s + e
+
+
+def v_nibble_in_tile(desc, token, dim):
+    """int4: nibble number of V(token, dim) inside its tile."""
+    w = desc.head_dim // 4
+    g, t = token // 4, token % 4
+    m, c = dim // 16, dim % 16
+    return (g * BLOCK_SIZE + c) * w + t * (desc.head_dim // 16) + m
+
+
+def element_nibble_offset(desc, layer, block, head, kv, token, dim):
+    """int4: nibble number of one K or V element in the pool."""
+    inner = (k_nibble_in_tile(desc, token, dim) if kv == 0
+             else v_nibble_in_tile(desc, token, dim))
+    return 2 * tile_byte_offset(desc, layer, block, head, kv) + inner
+
+
 def element_byte_offset(desc, layer, block, head, kv, token, dim):
-    """Byte offset of one K or V element in the pool."""
+    """Byte offset of one K or V element in the pool (byte element types)."""
     inner = (k_element_in_tile(desc, token, dim) if kv == 0
              else v_element_in_tile(desc, token, dim))
     return tile_byte_offset(desc, layer, block, head, kv) + inner * desc.elem_bytes
@@ -154,27 +182,53 @@ def gather_kv(desc, pool_u8, layer, table_row, n_tokens, head,
 
     For every logical position t < n the physical block table_row[t // 16] and
     offset t % 16 are located, and each element is read at its layout offset
-    and decoded exactly (fp8: code value times the float32 scale of
+    and decoded exactly (code types: code value times the float32 scale of
     (layer, head)).
     """
     d = desc.head_dim
-    eb = desc.elem_bytes
-    raw = _raw_view(desc, pool_u8)
     t = np.arange(n_tokens)
     blocks = np.asarray(table_row, dtype=np.int64)[t // BLOCK_SIZE]
     offs = t % BLOCK_SIZE
     dims = np.arange(d)
+    ks = None if k_scale is None else k_scale[layer][head]
+    vs = None if v_scale is None else v_scale[layer][head]
+    if desc.kv_dtype == "int4":
+        bb, oo, ii = blocks[:, None], offs[:, None], dims[None, :]
+        k_nib = element_nibble_offset(desc, layer, bb, head, 0, oo, ii)
+        v_nib = element_nibble_offset(desc, layer, bb, head, 1, oo, ii)
+        return (_int4.decode(_read_nibbles(pool_u8, k_nib), ks),
+                _int4.decode(_read_nibbles(pool_u8, v_nib), vs))
+    eb = desc.elem_bytes
+    raw = _raw_view(desc, pool_u8)
     k_base = np.array([tile_byte_offset(desc, layer, int(b), head, 0) for b in blocks],
                       dtype=np.int64)
     v_base = np.array([tile_byte_offset(desc, layer, int(b), head, 1) for b in blocks],
                       dtype=np.int64)
     k_idx = (k_base[:, None] // eb) + k_element_in_tile(desc, offs[:, None], dims[None, :])
     v_idx = (v_base[:, None] // eb) + v_element_in_tile(desc, offs[:, None], dims[None, :])
-    ks = None if k_scale is None else k_scale[layer][head]
-    vs = None if v_scale is None else v_scale[layer][head]
     K = _decode_raw(desc, raw[k_idx], ks)
     V = _decode_raw(desc, raw[v_idx], vs)
     return K, V
+
+
+def _read_nibbles(pool_u8, nib):
+    """Signed codes of the nibbles numbered `nib` (low half of byte N // 2 when N is even)."""
+    b = pool_u8[nib // 2].astype(np.int64)
+    n = np.where(nib % 2 == 0, b & 0xF, b >> 4)
+    return _int4.code_of(n)
+
+
+def _write_nibbles(pool_u8, nib, codes):
+    """Store codes into the nibbles numbered `nib` (all distinct) of a uint8
+    image, in place: first every low half, then every high half, so the two
+    halves of one byte never overwrite each other."""
+    nib = np.ravel(nib).astype(np.int64)
+    c = np.ravel(_int4.nibble_of(codes)).astype(np.uint8)
+    lo = nib % 2 == 0
+    b = nib[lo] // 2
+    pool_u8[b] = (pool_u8[b] & np.uint8(0xF0)) | c[lo]
+    b = nib[~lo] // 2
+    pool_u8[b] = (pool_u8[b] & np.uint8(0x0F)) | (c[~lo] << np.uint8(4))
 
 
 # ----------------------------------------------------------- cache write
@@ -187,7 +241,8 @@ def cache_write(desc, pool_u8, layer, k_new, v_new, in_dtype, slots,
     array) or "bf16" (uint16 bit patterns).  A slot < 0 skips its token.
     f32 and bf16 pools store the input bits unchanged (the input dtype must
     equal the pool dtype); fp8 pools store fp8.quantize(x, scale[layer][h]),
-    int8 pools int8.quantize(x, scale[layer][h]).
+    int8 pools int8.quantize(x, scale[layer][h]), int4 pools the nibbles of
+    int4.quantize(x, scale[layer][h]).
     Returns a new array; the input image is not modified.
     """
     pool = pool_u8.copy()
@@ -206,6 +261,14 @@ def cache_write(desc, pool_u8, layer, k_new, v_new, in_dtype, slots,
             continue
         blk, off = slot // BLOCK_SIZE, slot % BLOCK_SIZE
         for h in range(H):
+            if desc.kv_dtype == "int4":
+                kx = _input_to_f32(k_new[t, h], in_dtype)
+                vx = _input_to_f32(v_new[t, h], in_dtype)
+                k_nib = element_nibble_offset(desc, layer, blk, h, 0, off, dims)
+                v_nib = element_nibble_offset(desc, layer, blk, h, 1, off, dims)
+                _write_nibbles(pool, k_nib, _int4.quantize(kx, k_scale[layer][h]))
+                _write_nibbles(pool, v_nib, _int4.quantize(vx, v_scale[layer][h]))
+                continue
             k_at = (tile_byte_offset(desc, layer, blk, h, 0) // eb
                     + k_element_in_tile(desc, off, dims))
             v_at = (tile_byte_offset(desc, layer, blk, h, 1) // eb

@@ -8,7 +8,7 @@ the import fails loudly: there is no fallback.
 """
 
 from ._lib import (  # noqa: F401
-    BLOCK_SIZE, F32, BF16, FP8_E4M3, INT8, LIB_PATH, PagedKVError, lib,
+    BLOCK_SIZE, F32, BF16, FP8_E4M3, INT4, INT8, LIB_PATH, PagedKVError, lib,
 )
 from .api import (  # noqa: F401
     BlockManager, BlockTable, KVPool, block_table_upload, kv_bytes_per_token, kv_copy_blocks, kv_pool_bytes,

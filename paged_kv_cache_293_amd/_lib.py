@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "lib", "libpagedkv.so")
 
 BLOCK_SIZE = 16
-F32, BF16, FP8_E4M3, INT8 = 0, 1, 2, 3
+F32, BF16, FP8_E4M3, INT8, INT4 = 0, 1, 2, 3, 4
 
 _c_int32 = ctypes.c_int32
 _c_int64 = ctypes.c_int64

@@ -12,10 +12,10 @@ import math
 import numpy as np
 import torch
 
-from ._lib import BF16, BLOCK_SIZE, F32, FP8_E4M3, INT8, PagedKVError, PoolDesc, lib
+from ._lib import BF16, BLOCK_SIZE, F32, FP8_E4M3, INT4, INT8, PagedKVError, PoolDesc, lib
 
-_KV_DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "int8": INT8, F32: F32, BF16: BF16,
-              FP8_E4M3: FP8_E4M3, INT8: INT8}
+_KV_DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "int8": INT8, "int4": INT4, F32: F32, BF16: BF16,
+              FP8_E4M3: FP8_E4M3, INT8: INT8, INT4: INT4}
 _TORCH_CODE = {torch.float32: F32, torch.bfloat16: BF16}
 _CODE_TORCH = {F32: torch.float32, BF16: torch.bfloat16}
 
@@ -79,7 +79,7 @@ def kv_pool_create(num_layers, num_blocks, num_kv_heads, head_dim, kv_dtype, sto
     """Wrap (or allocate, when storage is None) a device pool buffer.
 
     storage: uint8 CUDA tensor of at least kv_pool_bytes(...) bytes.
-    k_scale, v_scale: float32 CUDA tensors [num_layers][num_kv_heads] (fp8 and int8 only).
+    k_scale, v_scale: float32 CUDA tensors [num_layers][num_kv_heads] (fp8, int8 and int4 only).
     """
     desc = _desc(num_layers, num_blocks, num_kv_heads, head_dim, kv_dtype)
     nbytes = int(lib.kv_pool_bytes(ctypes.byref(desc)))

@@ -52,22 +52,27 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-int elem_bytes(int32_t dtype) {
+// Bits per stored element (0: not a pool element type).
+int elem_bits(int32_t dtype) {
     switch (dtype) {
-        case PKV_F32: return 4;
-        case PKV_BF16: return 2;
-        case PKV_FP8_E4M3: return 1;
-        case PKV_INT8: return 1;
+        case PKV_F32: return 32;
+        case PKV_BF16: return 16;
+        case PKV_FP8_E4M3: return 8;
+        case PKV_INT8: return 8;
+        case PKV_INT4: return 4;
         default: return 0;
     }
 }
+
+// Element types stored as codes with a float32 scale per (layer, KV head).
+bool scaled_dtype(int32_t dtype) { return dtype == PKV_FP8_E4M3 || dtype == PKV_INT8 || dtype == PKV_INT4; }
 
 pkv_status check_desc(const pkv_pool_desc* d) {
     if (!d) return PKV_ERR_INVALID;
     if (d->num_layers < 1 || d->num_blocks < 1 || d->num_kv_heads < 1) return PKV_ERR_INVALID;
     if (d->block_size != PKV_BLOCK_SIZE) return PKV_ERR_UNSUPPORTED;
     if (d->head_dim != 64 && d->head_dim != 128) return PKV_ERR_UNSUPPORTED;
-    if (elem_bytes(d->kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
+    if (elem_bits(d->kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
     return PKV_OK;
 }
 
@@ -298,9 +303,9 @@ const char* pkv_status_string(pkv_status s) {
 }
 
 int64_t kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim, int32_t kv_dtype) {
-    const int b = elem_bytes(kv_dtype);
-    if (num_layers < 1 || num_kv_heads < 1 || head_dim < 1 || b == 0) return -1;
-    return 2LL * num_layers * num_kv_heads * head_dim * b;
+    const int bits = elem_bits(kv_dtype);
+    if (num_layers < 1 || num_kv_heads < 1 || head_dim < 1 || bits == 0) return -1;
+    return 2LL * num_layers * num_kv_heads * head_dim * bits / 8;
 }
 
 int64_t kv_pool_bytes(const pkv_pool_desc* desc) {
@@ -318,7 +323,7 @@ pkv_status kv_pool_create(const pkv_pool_desc* desc, void* dev_base, size_t dev_
         if (st != PKV_OK) return st;
         if (!dev_base || reinterpret_cast<uintptr_t>(dev_base) % kAlign) return PKV_ERR_INVALID;
         if (dev_bytes < static_cast<size_t>(kv_pool_bytes(desc))) return PKV_ERR_INVALID;
-        const bool scaled = desc->kv_dtype == PKV_FP8_E4M3 || desc->kv_dtype == PKV_INT8;
+        const bool scaled = scaled_dtype(desc->kv_dtype);
         if (scaled && (!dev_k_scale || !dev_v_scale)) return PKV_ERR_INVALID;
         pkv_pool* p = new pkv_pool;
         p->desc = *desc;
@@ -326,7 +331,7 @@ pkv_status kv_pool_create(const pkv_pool_desc* desc, void* dev_base, size_t dev_
         p->bytes = dev_bytes;
         p->k_scale = scaled ? dev_k_scale : nullptr;
         p->v_scale = scaled ? dev_v_scale : nullptr;
-        p->tile_bytes = static_cast<int64_t>(PKV_BLOCK_SIZE) * desc->head_dim * elem_bytes(desc->kv_dtype);
+        p->tile_bytes = static_cast<int64_t>(PKV_BLOCK_SIZE) * desc->head_dim * elem_bits(desc->kv_dtype) / 8;
         *out = p;
         return PKV_OK;
     } catch (...) {
@@ -493,7 +498,7 @@ pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, const void* de
     if (layer < 0 || layer >= pool->desc.num_layers) return PKV_ERR_INVALID;
     const int32_t kv = pool->desc.kv_dtype;
     const bool ok = (kv == PKV_F32 && in_dtype == PKV_F32) || (kv == PKV_BF16 && in_dtype == PKV_BF16) ||
-                    ((kv == PKV_FP8_E4M3 || kv == PKV_INT8) && (in_dtype == PKV_F32 || in_dtype == PKV_BF16));
+                    (scaled_dtype(kv) && (in_dtype == PKV_F32 || in_dtype == PKV_BF16));
     if (!ok) return PKV_ERR_UNSUPPORTED;
     if (num_tokens == 0) return PKV_OK;
     if (!dev_k_new || !dev_v_new || !dev_slot_mapping) return PKV_ERR_INVALID;
@@ -558,7 +563,7 @@ pkv_status attention_call(const pkv_pool* pool, int32_t layer, const pkv_table* 
     if (k_new || v_new) {
         if (!k_new || !v_new) return PKV_ERR_INVALID;
         const bool ok = (kv == PKV_F32 && in_dtype == PKV_F32) || (kv == PKV_BF16 && in_dtype == PKV_BF16) ||
-                        ((kv == PKV_FP8_E4M3 || kv == PKV_INT8) && (in_dtype == PKV_F32 || in_dtype == PKV_BF16));
+                        (scaled_dtype(kv) && (in_dtype == PKV_F32 || in_dtype == PKV_BF16));
         if (!ok) return PKV_ERR_UNSUPPORTED;
     }
 

@@ -95,6 +95,31 @@ __device__ __forceinline__ void accumulate_pv(const TileRegs<KV_INT8, D>& t, con
 }
 
 template <int D, int NT>
+__device__ __forceinline__ void accumulate_pv(const TileRegs<KV_INT4, D>& t, const f32x4 (&p)[NT],
+                                              f32x4 (&o)[NT][D / 16]) {
+    s16x4 pb[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+        pb[c] = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[c][0], p[c][1]), pack_bf16x2(p[c][2], p[c][3])});
+    }
+    constexpr int M = D / 16;                    // nibbles per token in a lane's V run
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        unsigned b[4];                           // tokens 4 (lane / 16) + t, dim 16 m + lane % 16
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int nib = tt * M + m;
+            b[tt] = i4_to_bf16(t.v[nib / 8], nib % 8);
+        }
+        const u32x2 vb = {b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+        const s16x4 a = __builtin_bit_cast(s16x4, vb);
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+            o[c][m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb[c], o[c][m], 0, 0, 0);
+    }
+}
+
+template <int D, int NT>
 __device__ __forceinline__ void accumulate_pv(const TileRegs<KV_F32, D>& t, const f32x4 (&p)[NT],
                                               f32x4 (&o)[NT][D / 16]) {
 #pragma unroll
@@ -648,6 +673,9 @@ hipError_t launch_attention(const AttnArgs& a, int kv_dtype, int head_dim, int n
     if (kv_dtype == KV_INT8)
         return head_dim == 128 ? launch_rows<KV_INT8, 128>(a, num_units, stream)
                                : launch_rows<KV_INT8, 64>(a, num_units, stream);
+    if (kv_dtype == KV_INT4)
+        return head_dim == 128 ? launch_rows<KV_INT4, 128>(a, num_units, stream)
+                               : launch_rows<KV_INT4, 64>(a, num_units, stream);
     return head_dim == 128 ? launch_rows<KV_F32, 128>(a, num_units, stream)
                            : launch_rows<KV_F32, 64>(a, num_units, stream);
 }

@@ -78,6 +78,9 @@ hipError_t launch_reshape_and_cache(const CacheArgs& a, int kv_dtype, int in_dty
     if (kv_dtype == KV_INT8)
         return in_dtype == KV_F32 ? launch_cache_dim<KV_INT8, KV_F32>(a, stream)
                                   : launch_cache_dim<KV_INT8, KV_BF16>(a, stream);
+    if (kv_dtype == KV_INT4)
+        return in_dtype == KV_F32 ? launch_cache_dim<KV_INT4, KV_F32>(a, stream)
+                                  : launch_cache_dim<KV_INT4, KV_BF16>(a, stream);
     if (in_dtype == KV_F32) return launch_cache_dim<KV_FP8, KV_F32>(a, stream);
     return launch_cache_dim<KV_FP8, KV_BF16>(a, stream);
 }

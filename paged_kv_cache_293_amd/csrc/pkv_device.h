@@ -6,10 +6,10 @@
 
 namespace pkv {
 
-enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_INT8 = 3 };
+enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_INT8 = 3, KV_INT4 = 4 };
 
-// One-byte element types carry a float32 scale per (layer, KV head).
-template <int KVT> constexpr bool kv_scaled() { return KVT == KV_FP8 || KVT == KV_INT8; }
+// Code element types carry a float32 scale per (layer, KV head).
+template <int KVT> constexpr bool kv_scaled() { return KVT == KV_FP8 || KVT == KV_INT8 || KVT == KV_INT4; }
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -33,9 +33,19 @@ __device__ __forceinline__ unsigned quantize_i8(float x, float inv) {
     return static_cast<unsigned>(static_cast<int>(y)) & 0xffu;
 }
 
+// Symmetric int4 code (the low nibble of the result): as int8, saturated to
+// +-7 (the code -8 is never written).
+__device__ __forceinline__ unsigned quantize_i4(float x, float inv) {
+    float y = __fmul_rn(x, inv);
+    y = (y == y) ? y : 0.f;
+    y = __builtin_rintf(fminf(fmaxf(y, -7.f), 7.f));
+    return static_cast<unsigned>(static_cast<int>(y)) & 0xfu;
+}
+
 template <int KVT>
 __device__ __forceinline__ unsigned quantize_code(float x, float inv) {
     if constexpr (KVT == KV_INT8) return quantize_i8(x, inv);
+    else if constexpr (KVT == KV_INT4) return quantize_i4(x, inv);
     else return quantize_e4m3(x, inv);
 }
 
@@ -58,7 +68,72 @@ __device__ __forceinline__ float load_in(const void* p, int64_t i) {
 template <int KVT, int IN, int D>
 __device__ __forceinline__ void write_token(uint8_t* blk, int64_t tile_bytes, int off, const void* k_row,
                                             const void* v_row, int h0, int nh, const float* k_scale,
+                                            const float* v_scale, int tid, int nthr);
+
+// Nibbles [n0, n0 + 8) of an int4 run as one 32-bit word, code j = value
+// index `first + stride * j` of the row (low nibble first).
+template <int IN>
+__device__ __forceinline__ unsigned pack8_i4(const void* row, int64_t first, int stride, float inv) {
+    unsigned w = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w |= quantize_i4(load_in<IN>(row, first + stride * j), inv) << (4 * j);
+    return w;
+}
+
+// int4 pools (layout in the library header): per token, K is four runs of
+// D / 4 nibbles (lane groups g), V sixteen partial runs of D / 16 nibbles
+// (columns c); every byte written belongs to this token alone.
+template <int IN, int D>
+__device__ __forceinline__ void write_token_i4(uint8_t* blk, int64_t tile_bytes, int off, const void* k_row,
+                                               const void* v_row, int h0, int nh, const float* k_scale,
+                                               const float* v_scale, int tid, int nthr) {
+    constexpr int W = D / 4;                 // nibbles per lane run
+    for (int it = tid; it < nh * 4; it += nthr) {          // K: run (g, off)
+        const int h = h0 + it / 4;
+        const int g = it % 4;
+        const float inv = 1.0f / k_scale[h];
+        uint8_t* run = blk + static_cast<int64_t>(h) * 2 * tile_bytes + (g * 16 + off) * (W / 2);
+        const int64_t src = static_cast<int64_t>(h) * D;
+        // dims 32 s + 8 g + e at nibble 8 s + e
+        if constexpr (D == 128) {
+            u32x4_t w;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) w[st] = pack8_i4<IN>(k_row, src + 32 * st + 8 * g, 1, inv);
+            *reinterpret_cast<u32x4_t*>(run) = w;
+        } else {
+            const unsigned w0 = pack8_i4<IN>(k_row, src + 8 * g, 1, inv);
+            const unsigned w1 = pack8_i4<IN>(k_row, src + 32 + 8 * g, 1, inv);
+            reinterpret_cast<unsigned*>(run)[0] = w0;
+            reinterpret_cast<unsigned*>(run)[1] = w1;
+        }
+    }
+    const int g = off / 4, t = off % 4;
+    for (int it = tid; it < nh * 16; it += nthr) {         // V: column c of run (g, c)
+        const int h = h0 + it / 16;
+        const int c = it % 16;
+        const float inv = 1.0f / v_scale[h];
+        uint8_t* run = blk + (static_cast<int64_t>(h) * 2 + 1) * tile_bytes + (g * 16 + c) * (W / 2);
+        const int64_t src = static_cast<int64_t>(h) * D + c;
+        // dims 16 m + c at nibble t * (D / 16) + m
+        if constexpr (D == 128) {
+            reinterpret_cast<unsigned*>(run)[t] = pack8_i4<IN>(v_row, src, 16, inv);
+        } else {
+            unsigned w = 0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) w |= quantize_i4(load_in<IN>(v_row, src + 16 * m), inv) << (4 * m);
+            reinterpret_cast<uint16_t*>(run)[t] = static_cast<uint16_t>(w);
+        }
+    }
+}
+
+template <int KVT, int IN, int D>
+__device__ __forceinline__ void write_token(uint8_t* blk, int64_t tile_bytes, int off, const void* k_row,
+                                            const void* v_row, int h0, int nh, const float* k_scale,
                                             const float* v_scale, int tid, int nthr) {
+    if constexpr (KVT == KV_INT4) {
+        write_token_i4<IN, D>(blk, tile_bytes, off, k_row, v_row, h0, nh, k_scale, v_scale, tid, nthr);
+        return;
+    }
     constexpr int EB = KVT == KV_F32 ? 4 : (KVT == KV_BF16 ? 2 : 1);
     constexpr int X = 16 / EB;
     constexpr int CH = D / X;

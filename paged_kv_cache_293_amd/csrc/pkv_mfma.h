@@ -143,6 +143,66 @@ template <int D> struct TileRegs1B {
 template <int D> struct TileRegs<KV_FP8, D> : TileRegs1B<D> {};
 template <int D> struct TileRegs<KV_INT8, D> : TileRegs1B<D> {};
 
+// int4 tiles: each lane reads its own run of D / 4 nibbles from the K and the
+// V tile (layout in the library header), so koff = lane * D / 8 and
+// voff = TILE + lane * D / 8 with TILE = 8 * D.  K nibble 8 s + e holds dim
+// 32 s + 8 (lane / 16) + e of token lane % 16; V nibble t * (D / 16) + m holds
+// dim 16 m + lane % 16 of token 4 (lane / 16) + t.
+template <int D> struct TileRegs<KV_INT4, D> {
+    unsigned k[D / 32];
+    unsigned v[D / 32];
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int koff, int voff) {
+        const int kb = (koff >> 4) * (D / 8);   // koff = lane * 16 by the caller's convention
+        if constexpr (D == 128) {
+            const u32x4 a = bload<u32x4>(r, kb, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            const u32x4 b = bload<u32x4>(r, voff, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { k[j] = a[j]; v[j] = b[j]; }
+        } else {
+            const u32x2 a = bload<u32x2>(r, kb, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            const u32x2 b = bload<u32x2>(r, voff, 0);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) { k[j] = a[j]; v[j] = b[j]; }
+        }
+    }
+    static constexpr int kTile = 8 * D;
+    __device__ static int v_offset(int lane) { return kTile + lane * (D / 8); }
+    // zero V of tokens >= nvalid among this lane's four (codes 0 stand for 0)
+    __device__ __forceinline__ void zero_v_from(int nvalid) {
+        if (nvalid >= 4) return;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t < nvalid) continue;
+            constexpr int M = D / 16;            // nibbles per token
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const int nib = t * M + m;
+                v[nib / 8] &= ~(0xfu << (4 * (nib % 8)));
+            }
+        }
+    }
+};
+
+// Signed value of nibble j of w (shift it to the top, then arithmetic shift down).
+__device__ __forceinline__ int i4_code(unsigned w, int j) {
+    return static_cast<int>(w << (28 - 4 * j)) >> 28;
+}
+
+// Two int4 codes (nibbles j, j + 1 of w, j even) -> two exact bf16 values
+// (|code| <= 8 converts to float32 exactly, and so does its upper half).
+__device__ __forceinline__ unsigned i4x2_to_bf16x2(unsigned w, int j) {
+    const float f0 = static_cast<float>(i4_code(w, j));
+    const float f1 = static_cast<float>(i4_code(w, j + 1));
+    return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+}
+
+// One int4 code (nibble j of w) -> bf16 bits in the low half.
+__device__ __forceinline__ unsigned i4_to_bf16(unsigned w, int j) {
+    return __float_as_uint(static_cast<float>(i4_code(w, j))) >> 16;
+}
+
 template <int D> struct TileRegs<KV_F32, D> {
     f32x4 k[D / 16];   // 4 f32: token lane%16, dims of chunk 4r + lane/16
     f32x4 v[D / 16];   // 4 f32: dim 16m + lane%16, tokens 4*(lane/16) .. +3
@@ -196,6 +256,8 @@ template <int D> struct QRegs1B {
 };
 template <int D> struct QRegs<KV_FP8, D> : QRegs1B<D> {};
 template <int D> struct QRegs<KV_INT8, D> : QRegs1B<D> {};
+// int4 K runs hold dims 32 s + 8 (lane / 16) + e per step s: the bf16 order.
+template <int D> struct QRegs<KV_INT4, D> : QRegs<KV_BF16, D> {};
 
 template <int D> struct QRegs<KV_F32, D> {
     f32x4 q[D / 16];    // r: dims (4r + lane/16) * 4 .. +4, one MFMA per element
@@ -241,6 +303,18 @@ __device__ __forceinline__ f32x4 scores(const TileRegs<KV_FP8, D>& t, const QReg
 template <int D>
 __device__ __forceinline__ f32x4 scores(const TileRegs<KV_INT8, D>& t, const QRegs<KV_INT8, D>& q) {
     return scores_1b<KV_INT8, D>(t, q);
+}
+
+template <int D>
+__device__ __forceinline__ f32x4 scores(const TileRegs<KV_INT4, D>& t, const QRegs<KV_INT4, D>& q) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+        const unsigned w = t.k[s];
+        const u32x4 kb = {i4x2_to_bf16x2(w, 0), i4x2_to_bf16x2(w, 2), i4x2_to_bf16x2(w, 4), i4x2_to_bf16x2(w, 6)};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb), q.q[s], acc, 0, 0, 0);
+    }
+    return acc;
 }
 
 template <int D>

@@ -48,7 +48,7 @@ def out_values(t):
 
 def tolerance(kv_dtype):
     """Max-abs error bound for unit-scale outputs: 1e-5 (float32 KV) or 1e-2
-    (bf16 / fp8 / int8 KV); for outputs above 1 in magnitude the bound scales with
+    (bf16 / fp8 / int8 / int4 KV); for outputs above 1 in magnitude the bound scales with
     them (the bf16 output itself carries a relative rounding of 2^-9)."""
     return 1e-5 if kv_dtype == "f32" else 1e-2
 
@@ -76,7 +76,7 @@ class Setup:
         P = w.partition_tokens if partition_tokens is None else partition_tokens
         self.partition_tokens = P
         ks = vs = None
-        if w.kv_dtype in ("fp8", "int8"):
+        if w.kv_dtype in ("fp8", "int8", "int4"):
             ks = torch.from_numpy(np.ascontiguousarray(w.k_scale, np.float32)).to(DEV)
             vs = torch.from_numpy(np.ascontiguousarray(w.v_scale, np.float32)).to(DEV)
         nbytes = pk.kv_pool_bytes(w.num_layers, w.num_blocks, w.num_kv_heads, w.head_dim, w.kv_dtype)

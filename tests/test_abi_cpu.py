@@ -55,7 +55,8 @@ def test_abi_version_and_status_strings(pk):
 
 @pytest.mark.parametrize("L,H,d,dt,b", [(80, 8, 128, "bf16", 2), (32, 8, 128, "bf16", 2),
                                          (32, 32, 128, "bf16", 2), (1, 8, 128, "fp8", 1),
-                                         (1, 2, 64, "f32", 4), (80, 8, 128, "int8", 1)])
+                                         (1, 2, 64, "f32", 4), (80, 8, 128, "int8", 1),
+                                         (32, 8, 128, "int4", 0.5)])
 def test_bytes_per_token_matches_oracle(pk, L, H, d, dt, b):
     assert pk.kv_bytes_per_token(L, H, d, dt) == kv_math.kv_bytes_per_token(L, H, d, b)
 
@@ -68,7 +69,7 @@ def test_pages_per_token_figures_through_the_library(pk):
     assert pk.kv_bytes_per_token(32, 32, 128, "bf16") == 524288
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16", "fp8", "int8"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "fp8", "int8", "int4"])
 def test_pool_bytes_match_oracle_layout(pk, dt):
     for L, NB, H, d in [(1, 128, 2, 64), (2, 3, 2, 64), (1, 12188, 8, 128)]:
         assert pk.kv_pool_bytes(L, NB, H, d, dt) == opool.PoolDesc(L, NB, H, d, dt).total_bytes
@@ -88,7 +89,7 @@ def test_pool_create_validation(pk):
                               ctypes.byref(out)) == -1
     for bad in (PoolDesc(1, 4, 2, 96, 16, 1), PoolDesc(1, 4, 2, 64, 32, 1), PoolDesc(1, 4, 2, 64, 16, 7)):
         assert lib.kv_pool_create(ctypes.byref(bad), fake, 1 << 30, None, None, ctypes.byref(out)) == -2
-    for scaled in (2, 3):                     # fp8 and int8 pools need their scale arrays
+    for scaled in (2, 3, 4):                  # fp8, int8 and int4 pools need their scale arrays
         d8 = PoolDesc(1, 4, 2, 64, 16, scaled)
         assert lib.kv_pool_create(ctypes.byref(d8), fake, 1 << 30, None, None, ctypes.byref(out)) == -1
         assert lib.kv_pool_create(ctypes.byref(d8), fake, 1 << 30, fake, fake, ctypes.byref(out)) == 0

@@ -102,6 +102,62 @@ def test_pool_layout_hand_offsets(dtype):
     assert seen == 2
 
 
+def test_int4_pool_layout_hand_offsets():
+    rows = golden_lines("pool_layout.txt")
+    desc = opool.PoolDesc(num_layers=2, num_blocks=3, num_kv_heads=2, head_dim=64, kv_dtype="int4")
+    seen = 0
+    for row in rows:
+        if row[0] == "SIZE":
+            if row[1] == "int4":
+                assert desc.total_bytes == int(row[2])
+                assert desc.total_bytes == kv_math.pool_bytes(2, 3, 2, 64, opool.DTYPE_BYTES["int4"])
+            continue
+        dt, kv, layer, block, head, tok, dim, expected = row
+        if dt != "int4":
+            continue
+        seen += 1
+        got = opool.element_nibble_offset(desc, int(layer), int(block), int(head),
+                                          0 if kv == "K" else 1, int(tok), int(dim))
+        assert got == int(expected)
+    assert seen == 4
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_int4_layout_is_a_bijection_and_keeps_tokens_apart(d):
+    # every element gets its own nibble, and the two nibbles of a byte always
+    # belong to the same token (so tokens can be written independently)
+    desc = opool.PoolDesc(num_layers=1, num_blocks=2, num_kv_heads=2, head_dim=d, kv_dtype="int4")
+    owner = np.full(2 * desc.total_bytes, -1, dtype=np.int64)
+    for blk in range(2):
+        for h in range(2):
+            for kv in range(2):
+                for t in range(16):
+                    for i in range(d):
+                        n = opool.element_nibble_offset(desc, 0, blk, h, kv, t, i)
+                        assert owner[n] == -1
+                        owner[n] = ((blk * 2 + h) * 2 + kv) * 16 + t
+    assert (owner >= 0).all()
+    assert np.array_equal(owner[0::2], owner[1::2])
+
+
+def test_int4_cache_write_then_gather_round_trips():
+    rng = np.random.default_rng(11)
+    desc = opool.PoolDesc(1, 6, 2, 64, "int4")
+    table = rng.permutation(6)[:4].astype(np.int32)[None, :]
+    n = 53
+    k = (rng.standard_normal((n, 2, 64)) * 3).astype(np.float32)
+    v = (rng.standard_normal((n, 2, 64)) * 3).astype(np.float32)
+    ks = np.array([[0.5, 0.75]], np.float32)
+    vs = np.array([[1.0, 0.25]], np.float32)
+    slots = opool.slot_mapping(table, [0] * n, list(range(n)), 6)
+    img = opool.cache_write(desc, opool.empty_pool(desc, 0), 0, k, v, "f32", slots, ks, vs)
+    for h in range(2):
+        K, V = opool.gather_kv(desc, img, 0, table[0], n, h, ks, vs)
+        from oracle import int4
+        assert np.array_equal(K, int4.decode(int4.quantize(k[:, h], ks[0][h]), ks[0][h]))
+        assert np.array_equal(V, int4.decode(int4.quantize(v[:, h], vs[0][h]), vs[0][h]))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
 def test_pool_layout_is_a_bijection(dtype):
     # every (layer, block, head, kv, token, dim) element gets its own byte range

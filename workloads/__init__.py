@@ -45,11 +45,12 @@ Conventions (readings recorded in the design notes):
 * draw order: lengths, placement, Q, prefill K/V (materialised workloads
   only), new-token K/V;
 * softmax scale 1/sqrt(d);
-* fp8 / int8 scales: materialised workloads use amax/448 (amax/127 for int8)
-  of each head's prefilled values (K and V separately); full-size workloads
-  whose pool is filled on the device use (4/448) * (1 + h/8) (int8:
-  (4/127) * (1 + h/8)) for head h with codes drawn as e4m3(x*448/4) (int8:
-  round(x*127/4) saturated to +-127).
+* fp8 / int8 / int4 scales: materialised workloads use amax/448 (amax/127
+  for int8, amax/7 for int4) of each head's prefilled values (K and V
+  separately); full-size workloads whose pool is filled on the device use
+  (4/448) * (1 + h/8) (int8: (4/127) * (1 + h/8), int4: (4/7) * (1 + h/8))
+  for head h with codes drawn as e4m3(x*448/4) (int8: round(x*127/4)
+  saturated to +-127; int4: round(x*7/4) saturated to +-7, two per byte).
 
 Seeds: 293000 + config number (c1 -> 293001, ...; pf, pfs -> 293006).
 """
@@ -71,7 +72,7 @@ class Workload:
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
-    kv_dtype: str                 # "f32" | "bf16" | "fp8" | "int8"
+    kv_dtype: str                 # "f32" | "bf16" | "fp8" | "int8" | "int4"
     q_dtype: str                  # "f32" | "bf16"
     out_dtype: str                # "f32" | "bf16"
     k_rows: int                   # query rows per sequence (1 = decode)
@@ -92,7 +93,7 @@ class Workload:
     pre_positions: Optional[np.ndarray] = None
     k_pre: Optional[np.ndarray] = None
     v_pre: Optional[np.ndarray] = None
-    k_scale: Optional[np.ndarray] = None   # float32 [L][H_kv] (fp8 and int8 only)
+    k_scale: Optional[np.ndarray] = None   # float32 [L][H_kv] (fp8, int8 and int4 only)
     v_scale: Optional[np.ndarray] = None
     shared_prefix_tokens: int = 0
     info: dict = field(default_factory=dict)
@@ -197,8 +198,8 @@ def build(name, seed, rng, seq_lens, *, num_q_heads, num_kv_heads, head_dim, kv_
     v_new = _cast(rng.standard_normal((T_new, Hkv, d), dtype=np.float32), in_dtype)
 
     k_scale = v_scale = None
-    if kv_dtype in ("fp8", "int8"):
-        qmax = np.float32(448.0 if kv_dtype == "fp8" else 127.0)
+    if kv_dtype in ("fp8", "int8", "int4"):
+        qmax = np.float32({"fp8": 448.0, "int8": 127.0, "int4": 7.0}[kv_dtype])
         if materialize:
             kv = values_f32(k_pre, in_dtype) if k_pre.shape[0] else np.ones((1, Hkv, d), np.float32)
             vv = values_f32(v_pre, in_dtype) if v_pre.shape[0] else np.ones((1, Hkv, d), np.float32)
@@ -233,12 +234,12 @@ def _uniform(rng, lo, hi, size):
 def make(name, materialize=None, seed=None, kv_dtype=None):
     """Build workload `name` (c1..c5 full size, c2s..c5s reduced; pf / pfs:
     chunked prefill, full size / reduced; a trailing "i8" (c2i8, c5si8, ...)
-    keeps the config but stores the KV cache as int8)."""
+    or "i4" keeps the config but stores the KV cache as int8 or int4)."""
     if name in ("pf", "pfs"):
         return _make_prefill(name, materialize, seed)
-    if name.endswith("i8"):
-        # int8 KV variant of a config: same seed, lengths and placement
-        return make(name[:-2], materialize, seed, kv_dtype="int8")
+    if name.endswith("i8") or name.endswith("i4"):
+        # int8 / int4 KV variant of a config: same seed, lengths and placement
+        return make(name[:-2], materialize, seed, kv_dtype="int8" if name.endswith("i8") else "int4")
     num = int(name[1])
     seed = SEED_BASE + num if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -323,7 +324,8 @@ def fill_pool_random(pool_u8, kv_dtype, seed, num_kv_heads=None):
     bf16/f32 pools get N(0, 1) in every element.  fp8 pools get
     e4m3(x * 448 / 4) codes of N(0, 1) draws, i.e. values x * scale / (4/448)
     under the per-head scales ``build`` assigns to unmaterialised workloads;
-    int8 pools get round(x * 127 / 4) saturated to +-127.
+    int8 pools get round(x * 127 / 4) saturated to +-127, int4 pools
+    round(x * 7 / 4) saturated to +-7, two codes per byte.
     Used for full-size workloads whose prefilled cache is too large to draw on
     the host; the oracle reads the filled pool back.
     """
@@ -343,6 +345,15 @@ def fill_pool_random(pool_u8, kv_dtype, seed, num_kv_heads=None):
                             dtype=torch.float32) * (127.0 / 4.0)
             x = torch.round(x).clamp(-127.0, 127.0)
             part.copy_(x.to(torch.int8).view(torch.uint8))
+    elif kv_dtype == "int4":
+        chunk = 1 << 26
+        flat = pool_u8.view(-1)
+        for start in range(0, flat.numel(), chunk):
+            part = flat[start:start + chunk]
+            x = torch.randn(2 * part.numel(), generator=g, device=pool_u8.device,
+                            dtype=torch.float32) * (7.0 / 4.0)
+            c = torch.round(x).clamp(-7.0, 7.0).to(torch.int32) & 0xF
+            part.copy_((c[0::2] | (c[1::2] << 4)).to(torch.uint8))
     elif kv_dtype == "fp8":
         chunk = 1 << 26
         flat = pool_u8.view(-1)
