@@ -94,6 +94,7 @@ __device__ __forceinline__ void accumulate_pv(const TileRegs<KV_INT8, D>& t, con
     accumulate_pv_1b<KV_INT8, D, NT>(t, p, o);
 }
 
+// Biased: the caller subtracts kI4Bias times the row's probability sum.
 template <int D, int NT>
 __device__ __forceinline__ void accumulate_pv(const TileRegs<KV_INT4, D>& t, const f32x4 (&p)[NT],
                                               f32x4 (&o)[NT][D / 16]) {
@@ -103,15 +104,21 @@ __device__ __forceinline__ void accumulate_pv(const TileRegs<KV_INT4, D>& t, con
         pb[c] = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[c][0], p[c][1]), pack_bf16x2(p[c][2], p[c][3])});
     }
     constexpr int M = D / 16;                    // nibbles per token in a lane's V run
+    constexpr int WPT = M / 8 > 0 ? M / 8 : 1;   // dwords per token (D = 128: 1; D = 64: half of one)
+    unsigned ev[4], od[4];                       // per token t: biased nibbles by parity
+    if constexpr (M == 8) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) i4_split(t.v[tt * WPT], ev[tt], od[tt]);
+    } else {
+        // D = 64: token t's 4 nibbles are the (t % 2) half of dword t / 2
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) i4_split(t.v[tt / 2] >> (16 * (tt % 2)), ev[tt], od[tt]);
+    }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-        unsigned b[4];                           // tokens 4 (lane / 16) + t, dim 16 m + lane % 16
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int nib = tt * M + m;
-            b[tt] = i4_to_bf16(t.v[nib / 8], nib % 8);
-        }
-        const u32x2 vb = {b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+        // tokens 4 (lane / 16) + t, dim 16 m + lane % 16: nibble m of token t
+        const unsigned* src = (m % 2) ? od : ev;
+        const u32x2 vb = {i4_pair(src[0], src[1], m / 2), i4_pair(src[2], src[3], m / 2)};
         const s16x4 a = __builtin_bit_cast(s16x4, vb);
 #pragma unroll
         for (int c = 0; c < NT; ++c)
@@ -208,6 +215,13 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
         qr[c].load(qrow, valid, lane);
         lim[c] = valid ? n - (kq - 1 - jr) : n;
     }
+    // int4: scores come out biased by kI4Bias times the sum of the query row
+    float qbias[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+        if constexpr (KVT == KV_INT4) qbias[c] = kI4Bias * query_row_sum<D>(qr[c])[0];
+        else qbias[c] = 0.f;
+    }
     const int mask_from = n - kq + 1;
 
     f32x4 o[NT][D / 16];
@@ -230,7 +244,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
         for (int c = 0; c < NT; ++c) {
             s[c] = scores<D>(tr, qr[c]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[c][i] *= sscale;
+            for (int i = 0; i < 4; ++i) s[c][i] = (s[c][i] - qbias[c]) * sscale;
         }
         const int tok0 = blk * kBlock + 4 * lg;
         if (blk * kBlock + kBlock > mask_from) {
@@ -331,7 +345,26 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             return tile_rsrc(head_base + static_cast<int64_t>(pid) * block_stride, valid ? a.tile_bytes : 0);
         };
         TileRegs<KVT, D> ta, tb;
-        if constexpr (NT == 1 && decode_depth(KVT, D) == 2) {
+        if constexpr (NT == 1 && decode_depth(KVT, D) == 3) {
+            TileRegs<KVT, D> tc, td;
+            ta.load(rsrc(0, true), koff, voff);
+            tb.load(rsrc(1, cnt > 1), koff, voff);
+            tc.load(rsrc(2, cnt > 2), koff, voff);
+            int i = 0;
+            for (; i + 3 < cnt; i += 4) {
+                td.load(rsrc(i + 3, true), koff, voff);
+                process(ta, logical(base + kWaves * i));
+                ta.load(rsrc(i + 4, i + 4 < cnt), koff, voff);
+                process(tb, logical(base + kWaves * (i + 1)));
+                tb.load(rsrc(i + 5, i + 5 < cnt), koff, voff);
+                process(tc, logical(base + kWaves * (i + 2)));
+                tc.load(rsrc(i + 6, i + 6 < cnt), koff, voff);
+                process(td, logical(base + kWaves * (i + 3)));
+            }
+            if (i < cnt) process(ta, logical(base + kWaves * i));
+            if (i + 1 < cnt) process(tb, logical(base + kWaves * (i + 1)));
+            if (i + 2 < cnt) process(tc, logical(base + kWaves * (i + 2)));
+        } else if constexpr (NT == 1 && decode_depth(KVT, D) == 2) {
             // Three buffers: while a wave processes one block the next two
             // are in flight.
             TileRegs<KVT, D> tc;
@@ -359,6 +392,19 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
                 process(tb, logical(base + kWaves * (i + 1)));
             }
             if (i < cnt) process(ta, logical(base + kWaves * i));
+        }
+    }
+
+    // int4: the output came out biased by kI4Bias times the row's probability
+    // sum (the whole wave's: summed over the four lane groups).
+    if constexpr (KVT == KV_INT4) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            float l = l_run[c];
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+#pragma unroll
+            for (int m = 0; m < D / 16; ++m) o[c][m] -= kI4Bias * l;
         }
     }
 

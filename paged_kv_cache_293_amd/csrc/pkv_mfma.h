@@ -148,6 +148,13 @@ template <int D> struct TileRegs<KV_INT8, D> : TileRegs1B<D> {};
 // voff = TILE + lane * D / 8 with TILE = 8 * D.  K nibble 8 s + e holds dim
 // 32 s + 8 (lane / 16) + e of token lane % 16; V nibble t * (D / 16) + m holds
 // dim 16 m + lane % 16 of token 4 (lane / 16) + t.
+//
+// Codes enter the matrix cores biased: flipping a nibble's top bit turns the
+// code c into u = c + 8 in [0, 15], and the bf16 bits 0x4300 | u are exactly
+// 128 + u = c + kI4Bias.  Two codes become one bf16 pair with a byte permute
+// and an OR.  The bias is taken out of the scores (kI4Bias * sum of the query
+// row) and of the output (kI4Bias * the row's probability sum) by the caller.
+// Every nibble pattern is a finite value, so no V row needs zeroing.
 template <int D> struct TileRegs<KV_INT4, D> {
     unsigned k[D / 32];
     unsigned v[D / 32];
@@ -169,38 +176,25 @@ template <int D> struct TileRegs<KV_INT4, D> {
     }
     static constexpr int kTile = 8 * D;
     __device__ static int v_offset(int lane) { return kTile + lane * (D / 8); }
-    // zero V of tokens >= nvalid among this lane's four (codes 0 stand for 0)
-    __device__ __forceinline__ void zero_v_from(int nvalid) {
-        if (nvalid >= 4) return;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if (t < nvalid) continue;
-            constexpr int M = D / 16;            // nibbles per token
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const int nib = t * M + m;
-                v[nib / 8] &= ~(0xfu << (4 * (nib % 8)));
-            }
-        }
-    }
+    // probabilities of tokens past the end are 0 and every code is finite
+    __device__ __forceinline__ void zero_v_from(int) {}
 };
 
-// Signed value of nibble j of w (shift it to the top, then arithmetic shift down).
-__device__ __forceinline__ int i4_code(unsigned w, int j) {
-    return static_cast<int>(w << (28 - 4 * j)) >> 28;
+constexpr float kI4Bias = 136.f;
+
+// Biased nibbles of w split by parity: byte k of `even` holds u of nibble
+// 2k, byte k of `odd` that of nibble 2k + 1.
+__device__ __forceinline__ void i4_split(unsigned w, unsigned& even, unsigned& odd) {
+    const unsigned x = w ^ 0x88888888u;
+    even = x & 0x0f0f0f0fu;
+    odd = (x >> 4) & 0x0f0f0f0fu;
 }
 
-// Two int4 codes (nibbles j, j + 1 of w, j even) -> two exact bf16 values
-// (|code| <= 8 converts to float32 exactly, and so does its upper half).
-__device__ __forceinline__ unsigned i4x2_to_bf16x2(unsigned w, int j) {
-    const float f0 = static_cast<float>(i4_code(w, j));
-    const float f1 = static_cast<float>(i4_code(w, j + 1));
-    return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
-}
-
-// One int4 code (nibble j of w) -> bf16 bits in the low half.
-__device__ __forceinline__ unsigned i4_to_bf16(unsigned w, int j) {
-    return __float_as_uint(static_cast<float>(i4_code(w, j))) >> 16;
+// bf16 pair (byte k of lo -> low half, byte k of hi -> high half), biased.
+__device__ __forceinline__ unsigned i4_pair(unsigned lo, unsigned hi, int k) {
+    // result bytes: [lo.k, 0, hi.k, 0]; selector 0x0c yields a zero byte
+    const unsigned sel = static_cast<unsigned>(k) | (0x0cu << 8) | ((4u + k) << 16) | (0x0cu << 24);
+    return __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
 }
 
 template <int D> struct TileRegs<KV_F32, D> {
@@ -305,15 +299,29 @@ __device__ __forceinline__ f32x4 scores(const TileRegs<KV_INT8, D>& t, const QRe
     return scores_1b<KV_INT8, D>(t, q);
 }
 
+// Biased scores: the caller subtracts kI4Bias times the query row's sum.
 template <int D>
 __device__ __forceinline__ f32x4 scores(const TileRegs<KV_INT4, D>& t, const QRegs<KV_INT4, D>& q) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
-        const unsigned w = t.k[s];
-        const u32x4 kb = {i4x2_to_bf16x2(w, 0), i4x2_to_bf16x2(w, 2), i4x2_to_bf16x2(w, 4), i4x2_to_bf16x2(w, 6)};
+        unsigned ev, od;
+        i4_split(t.k[s], ev, od);
+        const u32x4 kb = {i4_pair(ev, od, 0), i4_pair(ev, od, 1), i4_pair(ev, od, 2), i4_pair(ev, od, 3)};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb), q.q[s], acc, 0, 0, 0);
     }
+    return acc;
+}
+
+// Sum of a query row over all dims, for every lane of its column: the score
+// MFMA against a tile of bf16 ones.
+template <int D>
+__device__ __forceinline__ f32x4 query_row_sum(const QRegs<KV_BF16, D>& q) {
+    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones), q.q[s], acc, 0, 0, 0);
     return acc;
 }
 
