@@ -26,6 +26,7 @@ import argparse
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -60,6 +61,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--ceiling", action="store_true",
+                    help="run the standalone HBM read-ceiling probe (random and streaming tile reads) and exit")
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--partition", type=int, default=-1, help="split-KV partition tokens (-1: balanced plan)")
     ap.add_argument("--rotate", type=int, default=3, help="independent pools cycled through")
@@ -115,6 +118,11 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.ceiling:
+        probe = os.path.join(ROOT, "paged_kv_cache_293_amd", "lib", "read_ceiling")
+        if not os.path.exists(probe):
+            sys.exit(f"{probe} is missing: build first (python -m paged_kv_cache_293_amd.build)")
+        sys.exit(subprocess.run([probe]).returncode)
     if args.workload == "pf":
         return run_prefill(args)
     if args.workload == "sp":

@@ -345,26 +345,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             return tile_rsrc(head_base + static_cast<int64_t>(pid) * block_stride, valid ? a.tile_bytes : 0);
         };
         TileRegs<KVT, D> ta, tb;
-        if constexpr (NT == 1 && decode_depth(KVT, D) == 3) {
-            TileRegs<KVT, D> tc, td;
-            ta.load(rsrc(0, true), koff, voff);
-            tb.load(rsrc(1, cnt > 1), koff, voff);
-            tc.load(rsrc(2, cnt > 2), koff, voff);
-            int i = 0;
-            for (; i + 3 < cnt; i += 4) {
-                td.load(rsrc(i + 3, true), koff, voff);
-                process(ta, logical(base + kWaves * i));
-                ta.load(rsrc(i + 4, i + 4 < cnt), koff, voff);
-                process(tb, logical(base + kWaves * (i + 1)));
-                tb.load(rsrc(i + 5, i + 5 < cnt), koff, voff);
-                process(tc, logical(base + kWaves * (i + 2)));
-                tc.load(rsrc(i + 6, i + 6 < cnt), koff, voff);
-                process(td, logical(base + kWaves * (i + 3)));
-            }
-            if (i < cnt) process(ta, logical(base + kWaves * i));
-            if (i + 1 < cnt) process(tb, logical(base + kWaves * (i + 1)));
-            if (i + 2 < cnt) process(tc, logical(base + kWaves * (i + 2)));
-        } else if constexpr (NT == 1 && decode_depth(KVT, D) == 2) {
+        if constexpr (NT == 1 && decode_depth(KVT, D) == 2) {
             // Three buffers: while a wave processes one block the next two
             // are in flight.
             TileRegs<KVT, D> tc;

@@ -43,14 +43,8 @@ constexpr int kFuseMaxParts = 32;
 // resident work-groups per CU (a work-group is one wave on each SIMD).  At
 // d = 128 a deeper pipeline with two waves per SIMD streams faster than three
 // waves with one tile in flight each.
-#ifndef PKV_I4_DEPTH
-#define PKV_I4_DEPTH 2
-#endif
-#ifndef PKV_I4_WGS
-#define PKV_I4_WGS 2
-#endif
-constexpr int decode_depth(int kv, int d) { return kv == 4 && d == 128 ? PKV_I4_DEPTH : (kv != 0 && d == 128 ? 2 : 1); }
-constexpr int decode_wgs_per_cu(int kv, int d) { return kv == 4 && d == 128 ? PKV_I4_WGS : (kv == 0 ? 1 : (d == 128 ? 2 : 3)); }
+constexpr int decode_depth(int kv, int d) { return kv != 0 && d == 128 ? 2 : 1; }
+constexpr int decode_wgs_per_cu(int kv, int d) { return kv == 0 ? 1 : (d == 128 ? 2 : 3); }
 constexpr int kAutoItemsPerWg = PKV_AUTO_ITEMS_PER_WG;
 constexpr int kAutoMinItemBlocks = PKV_AUTO_MIN_ITEM_BLOCKS;
 constexpr int kAutoMinBlocks = 8;
