@@ -304,8 +304,10 @@ pkv_status paged_attention_verify(const pkv_pool* pool, int32_t layer, const pkv
  *                 in_dtype (as reshape_and_cache): row j of sequence s is the
  *                 token at position seq_len[s] - query_rows + j.
  *   other arguments as paged_attention_verify.
- * The tokens are written by the work-group that attends over their block,
- * before it reads any block.  Errors as paged_attention_verify, plus
+ * The work-group that attends over a token's block writes the token; its own
+ * attention takes the token's K/V codes from on-chip memory, so the write
+ * completes by the end of the call but is not waited for before the blocks
+ * are read.  Errors as paged_attention_verify, plus
  * PKV_ERR_INVALID for null token pointers and PKV_ERR_UNSUPPORTED for an
  * in_dtype the pool does not take.
  */

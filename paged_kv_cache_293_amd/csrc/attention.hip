@@ -157,6 +157,22 @@ __device__ __forceinline__ void store_out(const AttnArgs& a, int seq, int h, int
         reinterpret_cast<float*>(a.out)[oi] = val;
 }
 
+// Bytes one appended token occupies in the LDS staging area: its K then its
+// V elements in dim order, in the pool's element encoding (int4: one code per
+// byte).
+template <int KVT, int D> constexpr int stage_token_bytes() {
+    return 2 * D * (KVT == KV_F32 ? 4 : (KVT == KV_BF16 ? 2 : 1));
+}
+
+// Floats of the LDS area at the start of the dynamic LDS: the waves' merged
+// output, or (before the merge) the staged appended tokens followed by the
+// ids of the blocks they go to (at most k / 16 + 2 blocks).
+__host__ __device__ inline int acc_area_floats(int rows, int d, int k_rows, int stage_bytes) {
+    const int a = rows * (d + 1);
+    const int b = k_rows * stage_bytes / 4 + k_rows / 16 + 2;
+    return a > b ? a : b;
+}
+
 // ------------------------------------------------------- partition kernel
 // One (unit, KV head) item: attend over the unit's blocks with the work-group's
 // four waves, merge the waves, then write the output (unsplit sequence) or the
@@ -166,12 +182,14 @@ template <int KVT, int D, int NT>
 __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, const int h, float* smem,
                                             int* ticket_s, int& claimed, const int tid) {
     const int R = a.rows;
+    constexpr int STOK = stage_token_bytes<KVT, D>();
     float* acc_s = smem;                       // [R][D + 1] merged unnormalised output
-    float* m_s = smem + R * (D + 1);           // [W][R]
+    uint8_t* stage = reinterpret_cast<uint8_t*>(smem);   // appended tokens, during the block walk
+    float* m_s = smem + acc_area_floats(R, D, a.k_rows, STOK);   // [W][R]
     float* l_s = m_s + kWaves * R;             // [W][R]
 
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lg = lane >> 4;                  // lane group: tokens 4*lg .. +3
     const int col = lane & 15;                 // column within a row tile
     // Unit descriptor (see the plan built by block_table_upload) and, loaded
@@ -190,7 +208,6 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     const int G = a.group;
     const int kq = a.k_rows;
 
-    for (int e = tid; e < R * (D + 1); e += 64 * kWaves) acc_s[e] = 0.f;
 
     float sscale = a.score_scale;
     float vscale = 1.f;
@@ -238,7 +255,27 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     const uint8_t* head_base = a.pool +
         static_cast<int64_t>(a.layer) * a.num_blocks * block_stride + static_cast<int64_t>(h) * 2 * a.tile_bytes;
 
+    // Appended positions [lo, hi) of this unit (fused append): their K/V are
+    // staged in LDS and substituted into the tile registers, so the tiles are
+    // read without waiting for the pool write.
+    int lo = 0, hi = 0;
+    if (a.k_new != nullptr) {
+        lo = max(n - kq, b0 * kBlock);
+        hi = min(n, (b0 + nb) * kBlock);
+    }
+    const bool appends = lo < hi;
+
+    const int koff = lane * 16;
+    const int voff = TileRegs<KVT, D>::v_offset(lane);
+    const int blk_lo = lo / kBlock;
+    int* pid_s = reinterpret_cast<int*>(stage + kq * STOK);   // block ids of the appended positions
+
     auto process = [&](TileRegs<KVT, D>& tr, int blk) {
+        if (appends && blk * kBlock + kBlock > lo && blk * kBlock < hi) {
+            const int t0 = max(lo, blk * kBlock);
+            const int t1 = min(hi, blk * kBlock + kBlock);
+            for (int t = t0; t < t1; ++t) tr.put_token(t - blk * kBlock, stage + (t - lo) * STOK, lane);
+        }
         f32x4 s[NT];
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
@@ -285,72 +322,136 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
         accumulate_pv<D, NT>(tr, p, o);
     };
 
-    // Fused append (paged_attention_append): the k newest positions
-    // n-k .. n-1 of the sequence are written into the pool, for this KV head,
-    // by the work-group whose unit holds them, before any tile is read.
-    if (a.k_new != nullptr) {
-        const int first_new = n - kq;
-        const int lo = max(first_new, b0 * kBlock);
-        const int hi = min(n, (b0 + nb) * kBlock);
-        if (lo < hi) {
-            const int ib = a.append_in_f32 ? 4 : 2;
-            for (int t = lo; t < hi; ++t) {
-                int j = t / kBlock - b0 - rot;
-                if (j < 0) j += nb;
-                const int pid = min(max(uids[j], 0), a.num_blocks - 1);
-                uint8_t* blk = const_cast<uint8_t*>(a.pool) +
-                    (static_cast<int64_t>(a.layer) * a.num_blocks + pid) * block_stride;
-                const int64_t row = ((static_cast<int64_t>(seq) * kq + (t - first_new)) * a.num_kv_heads) * D * ib;
-                const uint8_t* kr = reinterpret_cast<const uint8_t*>(a.k_new) + row;
-                const uint8_t* vr = reinterpret_cast<const uint8_t*>(a.v_new) + row;
-                const float* ks = a.k_scale ? a.k_scale + a.layer * a.num_kv_heads : nullptr;
-                const float* vs = a.v_scale ? a.v_scale + a.layer * a.num_kv_heads : nullptr;
-                if constexpr (kv_scaled<KVT>()) {
-                    if (a.append_in_f32)
-                        write_token<KVT, KV_F32, D>(blk, a.tile_bytes, t % kBlock, kr, vr, h, 1, ks, vs,
-                                                    tid, 64 * kWaves);
-                    else
-                        write_token<KVT, KV_BF16, D>(blk, a.tile_bytes, t % kBlock, kr, vr, h, 1, ks, vs,
-                                                     tid, 64 * kWaves);
-                } else {
-                    write_token<KVT, KVT, D>(blk, a.tile_bytes, t % kBlock, kr, vr, h, 1, ks, vs,
-                                             tid, 64 * kWaves);
-                }
-            }
-            __builtin_amdgcn_s_waitcnt(0);   // this thread's stores have completed
-            __syncthreads();                 // and every thread's, before the tiles are read
-        }
-    }
-
-    const int koff = lane * 16;
-    const int voff = TileRegs<KVT, D>::v_offset(lane);
     // The unit's ids are stored in walking order j = 0 .. nb-1, which visits
     // logical block b0 + (j + rot) mod nb: sequences that share physical
     // blocks (a common prefix) start their walk at different blocks instead of
-    // all reading the same block at the same moment.
+    // all reading the same block at the same moment.  A wave walks j = wave,
+    // wave + 4, ... in chunks of up to 64 blocks (one block id per lane).
     auto logical = [&](int j) { const int x = j + rot; return b0 + (x >= nb ? x - nb : x); };
-    for (int base = wave; base < nb; base += 64 * kWaves) {
-        const int cnt = min(64, (nb - base + kWaves - 1) / kWaves);
-        int id = id0;
+    constexpr bool deep = NT == 1 && decode_depth(KVT, D) == 2;
+    int base = wave;
+    int cnt = 0;
+    int id = 0;
+    // The next block's loads are issued unconditionally so the wait counts
+    // stay static; past the last block they go through a zero-sized
+    // resource (no memory traffic, zeros returned).
+    auto rsrc = [&](int i, bool valid) {
+        const int pid = __builtin_amdgcn_readlane(id, min(i, 63));
+        return tile_rsrc(head_base + static_cast<int64_t>(pid) * block_stride, valid ? a.tile_bytes : 0);
+    };
+    TileRegs<KVT, D> ta, tb, tc;
+    // First loads of a chunk: one block in flight, two with three buffers.
+    // A wave without blocks (cnt = 0) issues them through zero-sized
+    // resources, so the first chunk's loads are issued on every path.
+    auto begin_chunk = [&]() {
+        cnt = min(64, (nb - base + kWaves - 1) / kWaves);
+        id = id0;
         if (base != wave) {
             id = 0;
             if (base + kWaves * lane < a.unit_stride) id = uids[base + kWaves * lane];
         }
         id = min(max(id, 0), a.num_blocks - 1);
-        // The next block's loads are issued unconditionally so the wait counts
-        // stay static; past the last block they go through a zero-sized
-        // resource (no memory traffic, zeros returned).
-        auto rsrc = [&](int i, bool valid) {
-            const int pid = __builtin_amdgcn_readlane(id, min(i, 63));
-            return tile_rsrc(head_base + static_cast<int64_t>(pid) * block_stride, valid ? a.tile_bytes : 0);
-        };
-        TileRegs<KVT, D> ta, tb;
-        if constexpr (NT == 1 && decode_depth(KVT, D) == 2) {
+        ta.load(rsrc(0, cnt > 0), koff, voff);
+        if constexpr (deep) tb.load(rsrc(1, cnt > 1), koff, voff);
+    };
+    // Fused append (paged_attention_append): the k newest positions n-k ..
+    // n-1 of the sequence are written into the pool, for this KV head, by the
+    // work-group whose unit holds them.  Their codes are staged in LDS and
+    // take the place of what the tile loads return for those positions, so
+    // no tile read waits for a pool write (the writes, issued after the walk,
+    // complete by the end of the kernel, before any later call reads the
+    // pool).  The inputs, the
+    // block ids and the scales are loaded before the first tile loads are
+    // issued: vector loads complete in issue order, so loading them later
+    // would hold the wave until its first tiles had arrived.
+    constexpr int kPre = 8;                       // input elements per thread per batch
+    constexpr int kBatch = 64 * kWaves * kPre;    // elements per batch (whole tokens)
+    static_assert(kBatch % (2 * D) == 0, "a batch holds whole tokens");
+    const int first_new = n - kq;
+    const int ib = a.append_in_f32 ? 4 : 2;       // input element bytes
+    const int n_elem = (hi - lo) * 2 * D;         // staged elements: K then V of each token
+    unsigned xin[kPre];
+    float k_sc = 1.f, v_sc = 1.f;                 // scales of code pools
+    // Buffer resources over the unit's appended input rows of KV head h (K
+    // and V; element (t, i) at ((t - lo) * H_kv * D + i) * ib).  They are
+    // zero-sized when nothing is appended, so the loads below are issued on
+    // every path, without branches, and read nothing then.
+    const int64_t row0 = (static_cast<int64_t>(seq) * kq + (lo - first_new)) * a.num_kv_heads + h;
+    const int in_span = appends ? ((hi - lo - 1) * a.num_kv_heads * D + D) * ib : 0;
+    const uint8_t* kin = appends ? reinterpret_cast<const uint8_t*>(a.k_new) + row0 * D * ib : a.pool;
+    const uint8_t* vin = appends ? reinterpret_cast<const uint8_t*>(a.v_new) + row0 * D * ib : a.pool;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kin), 0, in_span, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vin), 0, in_span, 0x00020000);
+    // Element e = e0 + tid + 64 W r of a batch: token lo + e / 2D, element
+    // e % 2D of its K (< D) or V row.  2D is a multiple of 64, so K or V is
+    // the same for a whole wave.  One dword load per element (a bf16 input
+    // takes its half; row lengths are even, so the dword stays in the span);
+    // elements past the end lie past the span and read as zero.
+    auto load_batch = [&](int e0) {
+#pragma unroll
+        for (int r = 0; r < kPre; ++r) {
+            const int eb = e0 + 64 * kWaves * r + 64 * wave;   // uniform
+            const int tt = eb / (2 * D);
+            const int iw = eb % (2 * D);
+            const bool isv = iw >= D;
+            const int off = (tt * a.num_kv_heads * D + (isv ? iw - D : iw) + lane) * ib;
+            const unsigned raw = __builtin_amdgcn_raw_buffer_load_b32(isv ? vrs : krs, off & ~3, 0, 0);
+            xin[r] = ib == 4 ? raw : ((raw >> ((off & 2) * 8)) & 0xffffu);
+        }
+    };
+    auto stage_batch = [&](int e0) {
+        float kinv = 1.f, vinv = 1.f;
+        if constexpr (kv_scaled<KVT>()) {
+            kinv = 1.0f / k_sc;
+            vinv = 1.0f / v_sc;
+        }
+#pragma unroll
+        for (int r = 0; r < kPre; ++r) {
+            const int e = e0 + tid + 64 * kWaves * r;
+            if (e < n_elem) {
+                const int i = e % (2 * D);
+                uint8_t* st = stage + (e / (2 * D)) * STOK;
+                if constexpr (kv_scaled<KVT>()) {
+                    const float x = ib == 4 ? __uint_as_float(xin[r]) : __uint_as_float(xin[r] << 16);
+                    st[i] = static_cast<uint8_t>(quantize_code<KVT>(x, i < D ? kinv : vinv));
+                } else if constexpr (KVT == KV_BF16) {
+                    reinterpret_cast<uint16_t*>(st)[i] = static_cast<uint16_t>(xin[r]);
+                } else {
+                    reinterpret_cast<unsigned*>(st)[i] = xin[r];
+                }
+            }
+        }
+    };
+    // Block ids of the appended positions (lanes past them load the last
+    // one's; without appended positions, entry 0) and the scales.
+    int pid_r;
+    {
+        int j = appends ? blk_lo + min(tid, (hi - 1) / kBlock - blk_lo) - b0 - rot : 0;
+        if (j < 0) j += nb;
+        pid_r = uids[j];
+    }
+    if constexpr (kv_scaled<KVT>()) {
+        k_sc = a.k_scale[a.layer * a.num_kv_heads + h];
+        v_sc = a.v_scale[a.layer * a.num_kv_heads + h];
+    }
+    load_batch(0);
+
+    begin_chunk();
+
+    if (appends) {
+        stage_batch(0);
+        for (int e0 = kBatch; e0 < n_elem; e0 += kBatch) {   // more than a batch: loaded here
+            load_batch(e0);
+            stage_batch(e0);
+        }
+        if (tid < (hi - 1) / kBlock - blk_lo + 1) pid_s[tid] = pid_r;   // clamped where it is read
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+
+    while (base < nb) {
+        if constexpr (deep) {
             // Three buffers: while a wave processes one block the next two
             // are in flight.
-            TileRegs<KVT, D> tc;
-            ta.load(rsrc(0, true), koff, voff);
-            tb.load(rsrc(1, cnt > 1), koff, voff);
             int i = 0;
             for (; i + 2 < cnt; i += 3) {
                 tc.load(rsrc(i + 2, true), koff, voff);
@@ -364,7 +465,6 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             if (i + 1 < cnt) process(tb, logical(base + kWaves * (i + 1)));
         } else {
             // Two buffers: one block in flight while the other is processed.
-            ta.load(rsrc(0, true), koff, voff);
             int i = 0;
             for (; i + 1 < cnt; i += 2) {
                 tb.load(rsrc(i + 1, true), koff, voff);
@@ -373,6 +473,66 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
                 process(tb, logical(base + kWaves * (i + 1)));
             }
             if (i < cnt) process(ta, logical(base + kWaves * i));
+        }
+        base += 64 * kWaves;
+        if (base < nb) begin_chunk();
+    }
+
+    // Pool writes of the appended positions, from the staged codes (tile
+    // layouts in the library header: K in 16-byte chunks of consecutive
+    // dims, V transposed).  They are issued after the walk, so no tile load
+    // of the walk waits behind them (measured: issued before the walk they
+    // cost the c2 step about 2 us more).
+    if (appends) {
+        for (int t = lo; t < hi; ++t) {
+            const int o = t % kBlock;
+            const int pid = min(max(pid_s[t / kBlock - blk_lo], 0), a.num_blocks - 1);
+            uint8_t* tk = const_cast<uint8_t*>(head_base) + static_cast<int64_t>(pid) * block_stride;
+            uint8_t* tv = tk + a.tile_bytes;
+            const uint8_t* st = stage + (t - lo) * STOK;
+            if constexpr (KVT == KV_INT4) {
+                // K: run (g, o) holds dims 32 s + 8 g + e at nibble 8 s + e;
+                // V: run (o / 4, c) holds dims 16 m + c of token o at nibble
+                // (o % 4) * (D / 16) + m.
+                for (int w = tid; w < 4 + 16; w += 64 * kWaves) {
+                    if (w < 4) {
+                        unsigned wd[D / 32];
+#pragma unroll
+                        for (int q = 0; q < D / 32; ++q) {
+                            unsigned x = 0;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) x |= (static_cast<unsigned>(st[32 * q + 8 * w + e]) & 0xfu) << (4 * e);
+                            wd[q] = x;
+                        }
+                        uint8_t* run = tk + (w * 16 + o) * (D / 8);
+                        if constexpr (D == 128) *reinterpret_cast<u32x4*>(run) = u32x4{wd[0], wd[1], wd[2], wd[3]};
+                        else *reinterpret_cast<u32x2*>(run) = u32x2{wd[0], wd[1]};
+                    } else {
+                        const int c = w - 4;
+                        uint8_t* run = tv + ((o / 4) * 16 + c) * (D / 8);
+                        unsigned x = 0;
+#pragma unroll
+                        for (int m = 0; m < D / 16; ++m) x |= (static_cast<unsigned>(st[D + 16 * m + c]) & 0xfu) << (4 * m);
+                        if constexpr (D == 128) reinterpret_cast<unsigned*>(run)[o % 4] = x;
+                        else reinterpret_cast<uint16_t*>(run)[o % 4] = static_cast<uint16_t>(x);
+                    }
+                }
+            } else {
+                constexpr int EB = KVT == KV_F32 ? 4 : (KVT == KV_BF16 ? 2 : 1);
+                constexpr int CH = D * EB / 16;   // 16-byte K chunks per token
+                for (int w = tid; w < CH + D; w += 64 * kWaves) {
+                    if (w < CH) {
+                        *reinterpret_cast<u32x4*>(tk + (w * kBlock + o) * 16) =
+                            *reinterpret_cast<const u32x4*>(st + w * 16);
+                    } else {
+                        const int i = w - CH;
+                        uint8_t* dst = tv + (i * kBlock + o) * EB;
+                        if constexpr (EB == 4) *reinterpret_cast<unsigned*>(dst) = reinterpret_cast<const unsigned*>(st)[D + i];
+                        else if constexpr (EB == 2) *reinterpret_cast<uint16_t*>(dst) = reinterpret_cast<const uint16_t*>(st)[D + i];
+                        else *dst = st[D + i];
+                    }
+                }
+            }
         }
     }
 
@@ -427,10 +587,12 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
                 const int row = 16 * c + col;
                 if (row >= R) continue;
                 float* dst = acc_s + row * (D + 1) + 4 * lg;
+                // wave 0 overwrites (the area held the staged tokens)
 #pragma unroll
                 for (int m = 0; m < D / 16; ++m)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dst[16 * m + i] += o[c][m][i] * f[c];
+                    for (int i = 0; i < 4; ++i)
+                        dst[16 * m + i] = (w == 0 ? 0.f : dst[16 * m + i]) + o[c][m][i] * f[c];
             }
         }
         __syncthreads();
@@ -528,7 +690,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
 template <int KVT, int D, int NT>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NT == 1 ? decode_wgs_per_cu(KVT, D) : (NT == 2 && KVT != KV_F32 ? 2 : 1))))
 void attn_partition_kernel(AttnArgs a) {
-    extern __shared__ float smem[];
+    extern __shared__ __attribute__((aligned(16))) float smem[];
     __shared__ int ticket;
     __shared__ int next_item;
     const int wave_s = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -649,7 +811,9 @@ template <int KVT, int D, int NT>
 int resident_work_groups() {
     static int per_cu = 0;   // same for every device of one architecture
     if (per_cu == 0) {
-        constexpr size_t lds_max = (static_cast<size_t>(16 * NT) * (D + 1) + 2 * kWaves * 16 * NT) * sizeof(float);
+        constexpr int rows = 16 * NT;   // at most rows appended tokens per sequence (G = 1)
+        const size_t lds_max = (static_cast<size_t>(acc_area_floats(rows, D, rows, stage_token_bytes<KVT, D>())) +
+                                2 * kWaves * rows) * sizeof(float);
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_partition_kernel<KVT, D, NT>, 64 * kWaves,
                                                          lds_max) != hipSuccess || n < 1)
@@ -666,7 +830,8 @@ int resident_work_groups() {
 template <int KVT, int D, int NT>
 hipError_t launch_instance(const AttnArgs& a, int num_units, hipStream_t stream) {
     (void)num_units;
-    const size_t lds = (static_cast<size_t>(a.rows) * (D + 1) + 2 * kWaves * a.rows) * sizeof(float);
+    const size_t lds = (static_cast<size_t>(acc_area_floats(a.rows, D, a.k_rows, stage_token_bytes<KVT, D>())) +
+                        2 * kWaves * a.rows) * sizeof(float);
     const int grid = std::min(a.num_items, resident_work_groups<KVT, D, NT>());
     hipLaunchKernelGGL((attn_partition_kernel<KVT, D, NT>), dim3(grid), dim3(64 * kWaves), lds, stream, a);
     hipError_t err = hipGetLastError();

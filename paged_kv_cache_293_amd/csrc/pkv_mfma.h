@@ -117,6 +117,27 @@ template <int D> struct TileRegs<KV_BF16, D> {
 #pragma unroll
         for (int m = 0; m < D / 16; ++m) { v[m][0] &= m0; v[m][1] &= m1; }
     }
+    // Token o of the tile takes the values staged in LDS at st: its K
+    // elements in dim order, then its V elements (the bytes the pool write
+    // stores for it).  Only lanes that hold a part of token o change.
+    __device__ __forceinline__ void put_token(int o, const uint8_t* st, int lane) {
+        const uint16_t* ks = reinterpret_cast<const uint16_t*>(st);
+        if ((lane & 15) == o) {
+#pragma unroll
+            for (int s = 0; s < D / 32; ++s) k[s] = *reinterpret_cast<const u32x4*>(ks + (4 * s + (lane >> 4)) * 8);
+        }
+        if ((lane >> 4) == (o >> 2)) {
+            const int e = o & 3;
+            const unsigned sh = 16 * (e & 1);
+            const unsigned keep = ~(0xffffu << sh);
+#pragma unroll
+            for (int m = 0; m < D / 16; ++m) {
+                const unsigned x = static_cast<unsigned>(ks[D + 16 * m + (lane & 15)]) << sh;
+                if (e < 2) v[m][0] = (v[m][0] & keep) | x;
+                else v[m][1] = (v[m][1] & keep) | x;
+            }
+        }
+    }
 };
 
 template <int D> struct TileRegs1B {
@@ -137,6 +158,21 @@ template <int D> struct TileRegs1B {
         const unsigned msk = nvalid <= 0 ? 0u : (0xffffffffu >> (8 * (4 - nvalid)));
 #pragma unroll
         for (int m = 0; m < D / 16; ++m) v[m] &= msk;
+    }
+    // Token o takes the codes staged in LDS at st (K codes in dim order, then
+    // V codes); only lanes holding a part of token o change.
+    __device__ __forceinline__ void put_token(int o, const uint8_t* st, int lane) {
+        if ((lane & 15) == o) {
+#pragma unroll
+            for (int q = 0; q < D / 64; ++q) k[q] = *reinterpret_cast<const u32x4*>(st + (4 * q + (lane >> 4)) * 16);
+        }
+        if ((lane >> 4) == (o >> 2)) {
+            const unsigned sh = 8 * (o & 3);
+            const unsigned keep = ~(0xffu << sh);
+#pragma unroll
+            for (int m = 0; m < D / 16; ++m)
+                v[m] = (v[m] & keep) | (static_cast<unsigned>(st[D + 16 * m + (lane & 15)]) << sh);
+        }
     }
 };
 // fp8 and int8 tiles share the byte layout; only the code conversion differs.
@@ -178,6 +214,45 @@ template <int D> struct TileRegs<KV_INT4, D> {
     __device__ static int v_offset(int lane) { return kTile + lane * (D / 8); }
     // probabilities of tokens past the end are 0 and every code is finite
     __device__ __forceinline__ void zero_v_from(int) {}
+    // Token o takes the codes staged in LDS at st, one code per byte (low
+    // nibble): K codes in dim order, then V codes.  Only lanes holding a part
+    // of token o change.
+    __device__ __forceinline__ void put_token(int o, const uint8_t* st, int lane) {
+        if ((lane & 15) == o) {
+#pragma unroll
+            for (int s = 0; s < D / 32; ++s) {
+                unsigned w = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w |= (static_cast<unsigned>(st[32 * s + 8 * (lane >> 4) + e]) & 0xfu) << (4 * e);
+                k[s] = w;
+            }
+        }
+        if ((lane >> 4) == (o >> 2)) {
+            const int t = o & 3;
+            const int c = lane & 15;
+            if constexpr (D == 128) {
+                unsigned w = 0;
+#pragma unroll
+                for (int m = 0; m < 8; ++m) w |= (static_cast<unsigned>(st[D + 16 * m + c]) & 0xfu) << (4 * m);
+                // per-lane selects: with a uniform index the compiler would
+                // address v[] dynamically and move the tile to scratch
+                int tv = t;
+                asm volatile("" : "+v"(tv));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = (j == tv) ? w : v[j];
+            } else {
+                unsigned w = 0;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) w |= (static_cast<unsigned>(st[D + 16 * m + c]) & 0xfu) << (4 * m);
+                const unsigned sh = 16 * (t & 1);
+                const unsigned keep = ~(0xffffu << sh);
+                int tv = t >> 1;
+                asm volatile("" : "+v"(tv));
+#pragma unroll
+                for (int j = 0; j < 2; ++j) v[j] = (j == tv) ? ((v[j] & keep) | (w << sh)) : v[j];
+            }
+        }
+    }
 };
 
 constexpr float kI4Bias = 136.f;
@@ -217,6 +292,24 @@ template <int D> struct TileRegs<KV_F32, D> {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (e >= nvalid) v[m][e] = 0.f;
+    }
+    // Token o takes the values staged in LDS at st (K in dim order, then V);
+    // only lanes holding a part of token o change.
+    __device__ __forceinline__ void put_token(int o, const uint8_t* st, int lane) {
+        const float* fs = reinterpret_cast<const float*>(st);
+        if ((lane & 15) == o) {
+#pragma unroll
+            for (int q = 0; q < D / 16; ++q) k[q] = *reinterpret_cast<const f32x4*>(fs + (4 * q + (lane >> 4)) * 4);
+        }
+        if ((lane >> 4) == (o >> 2)) {
+#pragma unroll
+            for (int m = 0; m < D / 16; ++m) {
+                const float x = fs[D + 16 * m + (lane & 15)];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (e == (o & 3)) v[m][e] = x;
+            }
+        }
     }
 };
 
