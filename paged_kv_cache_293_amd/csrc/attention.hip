@@ -445,7 +445,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             stage_batch(e0);
         }
         if (tid < (hi - 1) / kBlock - blk_lo + 1) pid_s[tid] = pid_r;   // clamped where it is read
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        lds_barrier();   // the tile loads stay in flight
     }
 
     while (base < nb) {
@@ -566,7 +566,9 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             l_s[wave * R + row] = l;
         }
     }
-    __syncthreads();
+    // The merge exchanges data through LDS only; the pool writes of appended
+    // tokens stay in flight.
+    lds_barrier();
     // Waves add their rescaled outputs one after another (fixed order, so the
     // result does not depend on scheduling).
     float f[NT];
@@ -595,7 +597,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
                         dst[16 * m + i] = (w == 0 ? 0.f : dst[16 * m + i]) + o[c][m][i] * f[c];
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     const bool split = parts > 1;
@@ -717,7 +719,7 @@ void attn_partition_kernel(AttnArgs a) {
         asm volatile("" : "+v"(tid));
         attend_item<KVT, D, NT>(ia, unit, h, smem, &ticket, claimed, tid);
         if (tid == 0) next_item = static_cast<int>(gridDim.x) + claimed;
-        __syncthreads();   // next_item visible; this item's LDS reads are done
+        lds_barrier();   // next_item visible; this item's LDS reads are done
         item = next_item;
     }
     // Thread 0 found again from the wave index and the lane, so the thread

@@ -92,6 +92,15 @@ __device__ __forceinline__ unsigned byte2_to_bf16x2(unsigned w) {
     else return fp8x2_to_bf16x2<HI>(w);
 }
 
+// Work-group barrier that orders LDS accesses only.  The plain barrier's
+// fence also waits for every global load and store the thread has in flight;
+// this one leaves them in flight (for data exchanged through LDS alone).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ------------------------------------------------------------------ tiles
 // Per-lane registers of one block's K and V tiles, and their loads.
 template <int KVT, int D> struct TileRegs;
