@@ -164,11 +164,12 @@ template <int KVT, int D> constexpr int stage_token_bytes() {
     return 2 * D * (KVT == KV_F32 ? 4 : (KVT == KV_BF16 ? 2 : 1));
 }
 
-// Floats of the LDS area at the start of the dynamic LDS: the waves' merged
-// output, or (before the merge) the staged appended tokens followed by the
-// ids of the blocks they go to (at most k / 16 + 2 blocks).
-__host__ __device__ inline int acc_area_floats(int rows, int d, int k_rows, int stage_bytes) {
-    const int a = rows * (d + 1);
+// Floats of the LDS area at the start of the dynamic LDS: the waves' outputs
+// (one [rows][d + 1] copy per wave when `copies` = kWaves, one shared copy
+// otherwise), or (before the merge) the staged appended tokens followed by
+// the ids of the blocks they go to (at most k / 16 + 2 blocks).
+__host__ __device__ inline int acc_area_floats(int rows, int d, int k_rows, int stage_bytes, int copies) {
+    const int a = copies * rows * (d + 1);
     const int b = k_rows * stage_bytes / 4 + k_rows / 16 + 2;
     return a > b ? a : b;
 }
@@ -185,7 +186,9 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     constexpr int STOK = stage_token_bytes<KVT, D>();
     float* acc_s = smem;                       // [R][D + 1] merged unnormalised output
     uint8_t* stage = reinterpret_cast<uint8_t*>(smem);   // appended tokens, during the block walk
-    float* m_s = smem + acc_area_floats(R, D, a.k_rows, STOK);   // [W][R]
+    // One-row-tile instances give every wave its own output copy to merge.
+    constexpr int kCopies = NT == 1 ? kWaves : 1;
+    float* m_s = smem + acc_area_floats(R, D, a.k_rows, STOK, kCopies);   // [W][R]
     float* l_s = m_s + kWaves * R;             // [W][R]
 
     const int lane = tid & 63;
@@ -582,22 +585,35 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
         }
         f[c] = (row >= R || M == neg_inf()) ? 0.f : fast_exp2(m_run[c] - M);
     }
-    for (int w = 0; w < kWaves; ++w) {
-        if (wave == w) {
+    if constexpr (kCopies == kWaves) {
+        // Every wave writes its rescaled output to its own copy; the output
+        // loop adds the copies in wave order.
+        if (col < R) {
+            float* dst = acc_s + (wave * R + col) * (D + 1) + 4 * lg;
 #pragma unroll
-            for (int c = 0; c < NT; ++c) {
-                const int row = 16 * c + col;
-                if (row >= R) continue;
-                float* dst = acc_s + row * (D + 1) + 4 * lg;
-                // wave 0 overwrites (the area held the staged tokens)
+            for (int m = 0; m < D / 16; ++m)
 #pragma unroll
-                for (int m = 0; m < D / 16; ++m)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        dst[16 * m + i] = (w == 0 ? 0.f : dst[16 * m + i]) + o[c][m][i] * f[c];
-            }
+                for (int i = 0; i < 4; ++i) dst[16 * m + i] = o[0][m][i] * f[0];
         }
         lds_barrier();
+    } else {
+        for (int w = 0; w < kWaves; ++w) {
+            if (wave == w) {
+#pragma unroll
+                for (int c = 0; c < NT; ++c) {
+                    const int row = 16 * c + col;
+                    if (row >= R) continue;
+                    float* dst = acc_s + row * (D + 1) + 4 * lg;
+                    // wave 0 overwrites (the area held the staged tokens)
+#pragma unroll
+                    for (int m = 0; m < D / 16; ++m)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            dst[16 * m + i] = (w == 0 ? 0.f : dst[16 * m + i]) + o[c][m][i] * f[c];
+                }
+            }
+            lds_barrier();
+        }
     }
 
     const bool split = parts > 1;
@@ -612,7 +628,11 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) L += l_s[w * R + r] * fast_exp2(m_s[w * R + r] - M);
         }
-        const float O = acc_s[r * (D + 1) + d];
+        float O = acc_s[r * (D + 1) + d];
+        if constexpr (kCopies == kWaves) {
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) O += acc_s[(w * R + r) * (D + 1) + d];
+        }
         if (!split) {
             store_out(a, seq, h, r, d, O / L * vscale);
         } else {
@@ -814,7 +834,8 @@ int resident_work_groups() {
     static int per_cu = 0;   // same for every device of one architecture
     if (per_cu == 0) {
         constexpr int rows = 16 * NT;   // at most rows appended tokens per sequence (G = 1)
-        const size_t lds_max = (static_cast<size_t>(acc_area_floats(rows, D, rows, stage_token_bytes<KVT, D>())) +
+        const size_t lds_max = (static_cast<size_t>(acc_area_floats(rows, D, rows, stage_token_bytes<KVT, D>(),
+                                                                    NT == 1 ? kWaves : 1)) +
                                 2 * kWaves * rows) * sizeof(float);
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_partition_kernel<KVT, D, NT>, 64 * kWaves,
@@ -832,7 +853,8 @@ int resident_work_groups() {
 template <int KVT, int D, int NT>
 hipError_t launch_instance(const AttnArgs& a, int num_units, hipStream_t stream) {
     (void)num_units;
-    const size_t lds = (static_cast<size_t>(acc_area_floats(a.rows, D, a.k_rows, stage_token_bytes<KVT, D>())) +
+    const size_t lds = (static_cast<size_t>(acc_area_floats(a.rows, D, a.k_rows, stage_token_bytes<KVT, D>(),
+                                                            NT == 1 ? kWaves : 1)) +
                         2 * kWaves * a.rows) * sizeof(float);
     const int grid = std::min(a.num_items, resident_work_groups<KVT, D, NT>());
     hipLaunchKernelGGL((attn_partition_kernel<KVT, D, NT>), dim3(grid), dim3(64 * kWaves), lds, stream, a);
