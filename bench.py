@@ -17,11 +17,14 @@ new tokens are shared.
 
 Printed: one JSON line.  ``value`` is KV bytes attended per second over the
 whole step (GB/s = 1e9 B/s), from K steps launched back to back between two
-events; ``seqs_per_s`` is sequences decoded per second; ``roofline`` rates
-the attention call alone (algorithmic KV bytes / its average duration,
-measured with events around each call on the stream it runs on, in a second
-pass of K steps) against the 8 TB/s HBM peak; ``cpu_baseline`` is the float64
-oracle on a bounded sample.
+events on the stream the library launches on; ``seqs_per_s`` is sequences
+decoded per second; ``roofline`` rates the attention kernel (algorithmic KV
+bytes / its average launch duration) against the 8 TB/s HBM peak.  The fused
+step is one launch of that kernel, so its duration is the timed region's
+time per step; with --separate it comes from events around each attention
+call.  A second pass of K steps with events around each call gives
+``attention_ms`` and its p10/p90 (these include each launch's dispatch gap).
+``cpu_baseline`` is the float64 oracle on a bounded sample.
 """
 
 import argparse
@@ -218,7 +221,12 @@ def main():
 
     nbytes = kv_bytes(w)
     value = nbytes / (ms_step * 1e-3) / 1e9
-    achieved = nbytes / (attn_avg * 1e-3) / 1e9
+    # The attention kernel's average launch duration: in the fused step the
+    # timed region is K launches of that one kernel back to back (per-call
+    # events would add each launch's dispatch gap); with --separate the
+    # events around each attention call.
+    kernel_ms = attn_avg if args.separate else ms_step
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     info = table.info()
 
     kernel_label = ("attn_partition_kernel (split-KV merge inside)" if info["max_parts"] <= 32
