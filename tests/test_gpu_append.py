@@ -67,7 +67,7 @@ def test_append_full_size_bench_configuration(name):
 @pytest.mark.parametrize("kv,k,Hq,Hkv,d", [
     ("bf16", 1, 8, 2, 128), ("bf16", 8, 16, 4, 128), ("bf16", 9, 32, 8, 128),
     ("bf16", 33, 8, 8, 64), ("fp8", 17, 8, 4, 128), ("int8", 12, 32, 8, 64),
-    ("f32", 6, 8, 2, 128), ("f32", 20, 4, 2, 64),
+    ("f32", 6, 8, 2, 128), ("f32", 20, 4, 2, 64), ("int4", 17, 8, 4, 128), ("int4", 33, 8, 8, 64),
 ])
 def test_append_multi_block_rows(kv, k, Hq, Hkv, d):
     log(f"append multi-block kv={kv} k={k} {Hq}/{Hkv} d{d}")
