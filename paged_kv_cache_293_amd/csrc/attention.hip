@@ -44,6 +44,7 @@ namespace pkv {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr float kLazyMax = 8.f;   // exp2 units the running max may lag behind a row's scores
 
 // O^T[dim tile m] += V^T tile . P^T for one column tile; p holds this lane's
 // probabilities of tokens 4*(lane/16) .. +3.
@@ -303,9 +304,14 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             float mx = fmaxf(fmaxf(s[c][0], s[c][1]), fmaxf(s[c][2], s[c][3]));
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(m_run[c], mx);
+            // The running max is a lagging reference: it moves only when a
+            // score exceeds it by more than kLazyMax, so probabilities stay
+            // <= 2^kLazyMax and the accumulators are rescaled on few blocks.
+            // O and l share the reference, so O / l does not depend on it.
+            const bool grow = mx > m_run[c] + kLazyMax;   // a row's first finite score always grows it
+            const float mnew = grow ? mx : m_run[c];
             const float muse = (mnew == neg_inf()) ? 0.f : mnew;
-            alpha[c] = fast_exp2(m_run[c] - muse);
+            alpha[c] = grow ? fast_exp2(m_run[c] - muse) : 1.f;
             float psum = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -314,7 +320,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             }
             l_run[c] = l_run[c] * alpha[c] + psum;
             m_run[c] = mnew;
-            rescale |= alpha[c] != 1.f;
+            rescale |= grow;
         }
         if (__ballot(rescale)) {
 #pragma unroll
