@@ -66,13 +66,13 @@ __device__ __forceinline__ T bload(__amdgpu_buffer_rsrc_t r, int voff, int imm) 
 }
 
 // Two fp8 E4M3 codes (bytes 0-1, or 2-3 when HI, of w) -> two bf16 values packed in one
-// dword.  The hardware conversion yields exact float32 values; their upper
-// halves are the exact bf16 values (E4M3 has 3 mantissa bits).
+// dword, in one gfx950 scaled conversion with scale 1: every E4M3 value
+// (3 mantissa bits, exponents 2^-9 .. 2^8) is exactly a bf16 value.
 template <bool HI>
 __device__ __forceinline__ unsigned fp8x2_to_bf16x2(unsigned w) {
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HI);
-    return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+    return __builtin_bit_cast(unsigned, b);
 }
 
 // Two int8 codes (bytes 0-1, or 2-3 when HI, of w) -> two bf16 values packed
