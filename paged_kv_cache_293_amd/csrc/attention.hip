@@ -75,7 +75,9 @@ __device__ __forceinline__ void accumulate_pv_1b(const TileRegs<KVT, D>& t, cons
     }
 #pragma unroll
     for (int m = 0; m < D / 16; ++m) {
-        const u32x2 vb = {byte2_to_bf16x2<KVT, false>(t.v[m]), byte2_to_bf16x2<KVT, true>(t.v[m])};
+        // int8: biased by kI8Bias (the caller subtracts kI8Bias times the
+        // row's probability sum)
+        const u32x2 vb = {decode_pair<KVT, false>(t.v[m]), decode_pair<KVT, true>(t.v[m])};
         const s16x4 a = __builtin_bit_cast(s16x4, vb);
 #pragma unroll
         for (int c = 0; c < NT; ++c)
@@ -236,11 +238,13 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
         qr[c].load(qrow, valid, lane);
         lim[c] = valid ? n - (kq - 1 - jr) : n;
     }
-    // int4: scores come out biased by kI4Bias times the sum of the query row
+    // int4 and int8: scores come out biased by the code bias times the sum of
+    // the query row
     float qbias[NT];
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
         if constexpr (KVT == KV_INT4) qbias[c] = kI4Bias * query_row_sum<D>(qr[c])[0];
+        else if constexpr (KVT == KV_INT8) qbias[c] = kI8Bias * query_row_sum<D>(qr[c])[0];
         else qbias[c] = 0.f;
     }
     const int mask_from = n - kq + 1;
@@ -283,7 +287,8 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
         f32x4 s[NT];
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
-            s[c] = scores<D>(tr, qr[c]);
+            if constexpr (KVT == KV_INT8) s[c] = scores_i8_biased<D>(tr, qr[c]);
+            else s[c] = scores<D>(tr, qr[c]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) s[c][i] = (s[c][i] - qbias[c]) * sscale;
         }
@@ -545,16 +550,18 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
         }
     }
 
-    // int4: the output came out biased by kI4Bias times the row's probability
-    // sum (the whole wave's: summed over the four lane groups).
-    if constexpr (KVT == KV_INT4) {
+    // int4 and int8: the output came out biased by the code bias times the
+    // row's probability sum (the whole wave's: summed over the four lane
+    // groups).
+    if constexpr (KVT == KV_INT4 || KVT == KV_INT8) {
+        constexpr float bias = KVT == KV_INT4 ? kI4Bias : kI8Bias;
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
             float l = l_run[c];
             l += __shfl_xor(l, 16);
             l += __shfl_xor(l, 32);
 #pragma unroll
-            for (int m = 0; m < D / 16; ++m) o[c][m] -= kI4Bias * l;
+            for (int m = 0; m < D / 16; ++m) o[c][m] -= bias * l;
         }
     }
 

@@ -4,6 +4,8 @@
 // the score product.  Not part of the public ABI.
 #pragma once
 
+#include <type_traits>
+
 #include "pkv_device.h"
 
 namespace pkv {
@@ -89,6 +91,28 @@ __device__ __forceinline__ unsigned i8x2_to_bf16x2(unsigned w) {
 template <int KVT, bool HI>
 __device__ __forceinline__ unsigned byte2_to_bf16x2(unsigned w) {
     if constexpr (KVT == KV_INT8) return i8x2_to_bf16x2<HI>(w);
+    else return fp8x2_to_bf16x2<HI>(w);
+}
+
+// Two int8 codes (bytes 0-1, or 2-3 when HI, of w) -> two bf16 values biased
+// by kI8Bias: flipping the sign bit turns code c into the byte c + 128, which
+// the byte-to-float converter takes exactly (8 significant bits fit bf16), and
+// one permute packs the pair.  The caller takes the bias out: kI8Bias times
+// the query row's sum from the scores, times the probability sum from the
+// output.
+constexpr float kI8Bias = 128.f;
+template <bool HI>
+__device__ __forceinline__ unsigned i8x2_to_bf16x2_biased(unsigned w) {
+    const unsigned x = w ^ 0x80808080u;
+    const float f0 = static_cast<float>((x >> (HI ? 16 : 0)) & 0xffu);
+    const float f1 = static_cast<float>((x >> (HI ? 24 : 8)) & 0xffu);
+    return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+}
+
+// Decode-kernel conversion of two one-byte codes: fp8 exact, int8 biased.
+template <int KVT, bool HI>
+__device__ __forceinline__ unsigned decode_pair(unsigned w) {
+    if constexpr (KVT == KV_INT8) return i8x2_to_bf16x2_biased<HI>(w);
     else return fp8x2_to_bf16x2<HI>(w);
 }
 
@@ -375,16 +399,21 @@ __device__ __forceinline__ f32x4 scores(const TileRegs<KV_BF16, D>& t, const QRe
     return acc;
 }
 
-template <int KVT, int D>
+template <int KVT, int D, bool BIASED = false>
 __device__ __forceinline__ f32x4 scores_1b(const TileRegs<KVT, D>& t, const QRegs<KVT, D>& q) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < D / 64; ++r) {
         const u32x4 w = t.k[r];
-        u32x4 lo = {byte2_to_bf16x2<KVT, false>(w[0]), byte2_to_bf16x2<KVT, true>(w[0]),
-                    byte2_to_bf16x2<KVT, false>(w[1]), byte2_to_bf16x2<KVT, true>(w[1])};
-        u32x4 hi = {byte2_to_bf16x2<KVT, false>(w[2]), byte2_to_bf16x2<KVT, true>(w[2]),
-                    byte2_to_bf16x2<KVT, false>(w[3]), byte2_to_bf16x2<KVT, true>(w[3])};
+        auto cv = [](unsigned x, auto hi_half) {
+            constexpr bool H = decltype(hi_half)::value;
+            if constexpr (BIASED) return decode_pair<KVT, H>(x);
+            else return byte2_to_bf16x2<KVT, H>(x);
+        };
+        using L = std::false_type;
+        using H = std::true_type;
+        u32x4 lo = {cv(w[0], L{}), cv(w[0], H{}), cv(w[1], L{}), cv(w[1], H{})};
+        u32x4 hi = {cv(w[2], L{}), cv(w[2], H{}), cv(w[3], L{}), cv(w[3], H{})};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo), q.q[2 * r], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi), q.q[2 * r + 1], acc, 0, 0, 0);
     }
@@ -399,6 +428,13 @@ __device__ __forceinline__ f32x4 scores(const TileRegs<KV_FP8, D>& t, const QReg
 template <int D>
 __device__ __forceinline__ f32x4 scores(const TileRegs<KV_INT8, D>& t, const QRegs<KV_INT8, D>& q) {
     return scores_1b<KV_INT8, D>(t, q);
+}
+
+// int8 scores for the decode kernel, biased: the caller subtracts kI8Bias
+// times the query row's sum.
+template <int D>
+__device__ __forceinline__ f32x4 scores_i8_biased(const TileRegs<KV_INT8, D>& t, const QRegs<KV_INT8, D>& q) {
+    return scores_1b<KV_INT8, D, true>(t, q);
 }
 
 // Biased scores: the caller subtracts kI4Bias times the query row's sum.
@@ -419,6 +455,16 @@ __device__ __forceinline__ f32x4 scores(const TileRegs<KV_INT4, D>& t, const QRe
 // MFMA against a tile of bf16 ones.
 template <int D>
 __device__ __forceinline__ f32x4 query_row_sum(const QRegs<KV_BF16, D>& q) {
+    const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones), q.q[s], acc, 0, 0, 0);
+    return acc;
+}
+
+template <int D>
+__device__ __forceinline__ f32x4 query_row_sum(const QRegs1B<D>& q) {
     const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
