@@ -141,13 +141,6 @@ __device__ __forceinline__ void accumulate_pv(const TileRegs<KV_F32, D>& t, cons
                 o[c][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.v[m][e], p[c][e], o[c][m], 0, 0, 0);
 }
 
-// The probability the normaliser adds up: what the PV product actually used.
-template <int KVT>
-__device__ __forceinline__ float as_used(float p) {
-    if constexpr (KVT == KV_F32) return p;
-    else return __uint_as_float(f32_to_bf16_rne(p) << 16);
-}
-
 // Final output element (row r of KV head h of sequence seq, dim d).
 __device__ __forceinline__ void store_out(const AttnArgs& a, int seq, int h, int r, int d, float val) {
     const int G = a.group;
@@ -249,15 +242,32 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     }
     const int mask_from = n - kq + 1;
 
+    // Row sums of the probabilities: float32 pools add them on the VALU per
+    // lane (l_run, four tokens per lane group); the others on the matrix
+    // cores, with the PV product's bf16 operand against a tile of ones
+    // (lacc: every element holds the row's sum of the values used).
     f32x4 o[NT][D / 16];
     float m_run[NT], l_run[NT];
+    f32x4 lacc[NT];
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
         m_run[c] = neg_inf();
         l_run[c] = 0.f;
+        lacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < D / 16; ++m) o[c][m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // Full row sum of column tile c for this lane's row.
+    auto row_sum = [&](int c) {
+        if constexpr (KVT == KV_F32) {
+            float l = l_run[c];
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+            return l;
+        } else {
+            return lacc[c][0];
+        }
+    };
 
     const int64_t block_stride = static_cast<int64_t>(a.num_kv_heads) * 2 * a.tile_bytes;
     const uint8_t* head_base = a.pool +
@@ -317,21 +327,33 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             const float mnew = grow ? mx : m_run[c];
             const float muse = (mnew == neg_inf()) ? 0.f : mnew;
             alpha[c] = grow ? fast_exp2(m_run[c] - muse) : 1.f;
-            float psum = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[c][i] = fast_exp2(s[c][i] - muse);
-                psum += as_used<KVT>(p[c][i]);
+            for (int i = 0; i < 4; ++i) p[c][i] = fast_exp2(s[c][i] - muse);
+            if constexpr (KVT == KV_F32) {
+                float psum = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) psum += p[c][i];
+                l_run[c] = l_run[c] * alpha[c] + psum;
             }
-            l_run[c] = l_run[c] * alpha[c] + psum;
             m_run[c] = mnew;
             rescale |= grow;
         }
         if (__ballot(rescale)) {
 #pragma unroll
-            for (int c = 0; c < NT; ++c)
+            for (int c = 0; c < NT; ++c) {
+                lacc[c] *= alpha[c];
 #pragma unroll
                 for (int m = 0; m < D / 16; ++m) o[c][m] *= alpha[c];
+            }
+        }
+        if constexpr (KVT != KV_F32) {
+            const s16x4 ones = __builtin_bit_cast(s16x4, u32x2{0x3f803f80u, 0x3f803f80u});
+#pragma unroll
+            for (int c = 0; c < NT; ++c) {
+                const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[c][0], p[c][1]),
+                                                                 pack_bf16x2(p[c][2], p[c][3])});
+                lacc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pb, lacc[c], 0, 0, 0);
+            }
         }
         accumulate_pv<D, NT>(tr, p, o);
     };
@@ -551,15 +573,12 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     }
 
     // int4 and int8: the output came out biased by the code bias times the
-    // row's probability sum (the whole wave's: summed over the four lane
-    // groups).
+    // row's probability sum (over all of the wave's tokens).
     if constexpr (KVT == KV_INT4 || KVT == KV_INT8) {
         constexpr float bias = KVT == KV_INT4 ? kI4Bias : kI8Bias;
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
-            float l = l_run[c];
-            l += __shfl_xor(l, 16);
-            l += __shfl_xor(l, 32);
+            const float l = row_sum(c);
 #pragma unroll
             for (int m = 0; m < D / 16; ++m) o[c][m] -= bias * l;
         }
@@ -573,9 +592,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     // Merge the waves: publish (m, l), rescale O to the common max, add in LDS.
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
-        float l = l_run[c];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        const float l = row_sum(c);
         const int row = 16 * c + col;
         if (lg == 0 && row < R) {
             m_s[wave * R + row] = m_run[c];
