@@ -34,9 +34,13 @@
 // transposed) makes every operand a plain vector load: each K load instruction
 // of a wave reads one contiguous KiB, each V load 16 dims x the tile row.
 //   bf16: v_mfma_f32_16x16x32_bf16 (QK), v_mfma_f32_16x16x16_bf16 (PV),
-//         probabilities rounded to bf16;
+//         probabilities rounded to bf16; their row sums come from one more
+//         16x16x16 MFMA against a tile of ones (the values PV used);
 //   fp8 : codes converted to bf16 in registers (exact), then as bf16; the K
 //         scale folds into the score scale, the V scale into the final divide;
+//   int8, int4: codes widened to bf16 with a bias (128, 136) that the kernel
+//         takes out of the scores (bias x the query row's sum) and of the
+//         output (bias x the probability sum); scales as fp8;
 //   f32 : v_mfma_f32_16x16x4_f32 for both products, probabilities in f32.
 #include "pkv_mfma.h"
 
