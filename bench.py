@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--ceiling", action="store_true",
                     help="run the standalone HBM read-ceiling probe (random and streaming tile reads) and exit")
+    ap.add_argument("--floor", action="store_true",
+                    help="run the standalone paged-read floor probe (the decode step's tile reads alone, "
+                         "8/4/2 KiB tiles) and exit")
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--partition", type=int, default=-1, help="split-KV partition tokens (-1: balanced plan)")
     ap.add_argument("--rotate", type=int, default=3, help="independent pools cycled through")
@@ -123,8 +126,8 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    if args.ceiling:
-        probe = os.path.join(ROOT, "paged_kv_cache_293_amd", "lib", "read_ceiling")
+    if args.ceiling or args.floor:
+        probe = os.path.join(ROOT, "paged_kv_cache_293_amd", "lib", "read_ceiling" if args.ceiling else "paged_read_floor")
         if not os.path.exists(probe):
             sys.exit(f"{probe} is missing: build first (python -m paged_kv_cache_293_amd.build)")
         sys.exit(subprocess.run([probe]).returncode)

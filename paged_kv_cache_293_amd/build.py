@@ -15,9 +15,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libpagedkv.so")
-# Standalone HBM read-ceiling probe (not part of the library; bench.py --ceiling runs it).
-PROBE_SRC = os.path.join(HERE, "probe", "read_ceiling.hip")
-PROBE_PATH = os.path.join(LIB_DIR, "read_ceiling")
+# Standalone probes (not part of the library): the HBM read ceiling
+# (bench.py --ceiling) and the paged-read floor at the decode kernel's shape
+# (bench.py --floor).
+PROBES = [("read_ceiling.hip", "read_ceiling"), ("paged_read_floor.hip", "paged_read_floor")]
 SOURCES = ["api.cpp", "block_manager.cpp", "attention.hip", "cache.hip", "prefill.hip", "speculative.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -49,12 +50,15 @@ def build(verbose=False):
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, LIB_PATH)
-    cmd = [HIPCC] + [f for f in FLAGS if f not in ("-shared", "-fPIC")] + [PROBE_SRC, "-o", PROBE_PATH + ".tmp"]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed on the read-ceiling probe:\n" +
-                           "\n".join(l for l in res.stderr.splitlines() if noise not in l))
-    os.replace(PROBE_PATH + ".tmp", PROBE_PATH)
+    for src, exe in PROBES:
+        out = os.path.join(LIB_DIR, exe)
+        cmd = [HIPCC] + [f for f in FLAGS if f not in ("-shared", "-fPIC")] + [os.path.join(HERE, "probe", src),
+                                                                             "-o", out + ".tmp"]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed on the probe {src}:\n" +
+                               "\n".join(l for l in res.stderr.splitlines() if noise not in l))
+        os.replace(out + ".tmp", out)
     return LIB_PATH
 
 
