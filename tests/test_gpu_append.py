@@ -54,7 +54,7 @@ def test_append_fp8_from_float32_inputs():
 def test_append_full_size_bench_configuration(name):
     log(f"append full size {name}")
     w = workloads.make(name, materialize=False)
-    s, ref, got, fused_store = _both_routes(w, P=-1, poison=False)
+    s, ref, got, fused_store = _both_routes(w, P=-1, poison=True)
     assert torch.equal(fused_store, s.pool.storage)
     assert torch.equal(got, ref)
 

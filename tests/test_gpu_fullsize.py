@@ -1,35 +1,58 @@
-"""GPU: full-size workloads in the launch configuration bench.py times, checked
-on sampled sequences against the float64 oracle (which reads the device pool
-back: at these sizes the prefilled cache comes from the seeded device RNG)."""
+"""GPU: the full-size workloads, every sequence against the float64 oracle.
+
+Each pool is filled by the seeded device RNG over the blocks the tables name;
+every other block holds the poison byte (NaN, or a code the cache write never
+stores), so a read outside a sequence's own blocks shows in its output.  The
+oracle reads the device pool back and runs over all sequences (spread over
+host threads).  Each workload runs in the launch configuration bench.py times
+(its default partition plan) and at the config's other plan: c4 at its stated
+512-token partitions (merged by the separate merge kernel) and at the balanced
+plan, the others at the balanced plan and at 512-token partitions.  Every
+output must be finite and meet the plain max-abs bound where |ref| <= 1 (and
+the bound scaled by |ref| above 1); the errors are logged per workload and plan.
+"""
+
+import time
 
 import numpy as np
 import pytest
 
 import workloads
-from gpu_setup import Setup, assert_close, log, out_values
+from gpu_setup import Setup, assert_close, error_stats, log, out_values
 
 pytestmark = pytest.mark.gpu
 
+CASES = [("c2", -1), ("c2", 512), ("c3", -1), ("c3", 512), ("c4", 512), ("c4", -1),
+         ("c5", -1), ("c5", 512), ("c2i8", -1), ("c2i8", 512), ("c2i4", -1), ("c2i4", 512)]
 
-def _sample(w, k_extra, seed):
-    lens = w.seq_lens
-    rng = np.random.default_rng(seed)
-    picks = {int(np.argmax(lens)), int(np.argmin(lens))}
-    picks.update(int(x) for x in rng.choice(w.batch, size=min(k_extra, w.batch), replace=False))
-    return sorted(picks)
+_cache = {}
 
 
-# P = -1 is the balanced plan bench.py times; the other value is the config's
-# own partition length (c4: 512-token partitions and a separate merge kernel).
-@pytest.mark.parametrize("name,extra,P", [("c2", 4, -1), ("c2", 4, 512), ("c3", 4, -1), ("c3", 4, 512),
-                                          ("c4", 1, 512), ("c4", 1, -1), ("c5", 4, -1), ("c5", 4, 512)])
-def test_full_size_sampled(name, extra, P):
+def _standing(name):
+    """The workload on the device and the oracle's output over every
+    sequence; one workload is kept at a time (c3's pool is 7.8 GB)."""
+    if name not in _cache:
+        _cache.clear()
+        w = workloads.make(name, materialize=False)
+        t0 = time.perf_counter()
+        s = Setup(w, partition_tokens=-1, poison=True)
+        ref = s.oracle_all()
+        log(f"  {name}: oracle over {w.batch} sequences ({int(w.seq_lens.sum())} tokens) "
+            f"in {time.perf_counter() - t0:.1f} s")
+        _cache[name] = (w, s, ref)
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name,P", CASES)
+def test_full_size_every_sequence(name, P):
     log(f"full size {name} P={P}")
-    w = workloads.make(name, materialize=False)
-    s = Setup(w, partition_tokens=P, poison=False)
-    got = out_values(s.run())
-    seqs = _sample(w, extra, 11)
-    ref = s.oracle(seqs=seqs)
-    err = assert_close(got[seqs], ref[seqs], w.kv_dtype, name)
-    log(f"  {name} P={P}: seqs {seqs} max abs err {err:.3e}; {s.table.info()}")
-    assert np.isfinite(got).all()
+    w, s, ref = _standing(name)
+    table = s.table if P == -1 else s.upload(P)
+    got = out_values(s.run(table=table))
+    err = assert_close(got, ref, w.kv_dtype, f"{name} P={P}")
+    e_unit, r_big, n_big = error_stats(got, ref)
+    log(f"  {name} P={P}: {w.batch} sequences, max abs err {err:.3e} (|ref| <= 1), "
+        f"max rel err {r_big:.3e} over {n_big} outputs with |ref| > 1; {table.info()}")
+    assert e_unit == err
+    if name == "c4" and P == 512:
+        assert table.info()["max_parts"] == 256   # 131072 / 512: the separate merge kernel runs

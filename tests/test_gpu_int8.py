@@ -119,13 +119,4 @@ def test_int8_prefill_and_fused_append():
     assert torch.equal(got, ref)
 
 
-def test_int8_full_size_decode_sampled():
-    log("int8 full-size c2i8")
-    w = workloads.make("c2i8", materialize=False)
-    s = Setup(w, partition_tokens=-1, poison=False)
-    got = out_values(s.run())
-    lens = w.seq_lens
-    seqs = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 7, 33})
-    ref = s.oracle(seqs=seqs)
-    err = assert_close(got[seqs], ref[seqs], "int8", "c2i8")
-    log(f"  max abs err {err:.3e}")
+# The full-size c2i8 workload is checked on every sequence in test_gpu_fullsize.py.
