@@ -23,8 +23,17 @@ bytes / its average launch duration) against the 8 TB/s HBM peak.  The fused
 step is one launch of that kernel, so its duration is the timed region's
 time per step; with --separate it comes from events around each attention
 call.  A second pass of K steps with events around each call gives
-``attention_ms`` and its p10/p90 (these include each launch's dispatch gap).
-``cpu_baseline`` is the float64 oracle on a bounded sample.
+``per_step_ms`` (median, p10, p90; these include each launch's dispatch gap),
+and a third pass of K steps back to back on one pool gives the warm time
+beside the flushed one (``flushed_vs_warm_ms_per_step``).  ``unique_kv_gbs``
+counts each physical block once (c5's shared prefix is read by every
+sequence).  ``cpu_baseline`` is the float64 oracle on a bounded sample, on
+one thread and on the host's cores (up to 16), with the host's core counts.
+
+Workloads: c2 (default), c3, c4 (512-token partitions, as the configuration
+states, merged by the reduction kernel), c4b (the same batch under the
+balanced plan), c5, c2i8, c2i4, pf (chunked prefill), sp (speculative
+acceptance).
 """
 
 import argparse
@@ -46,7 +55,10 @@ METRIC = "paged decode attention KV GB/s (% HBM peak) + seqs/s, Llama-3-8B GQA s
 WORKLOAD_NAMES = {
     "c2": "llama3-8b-decode-layer bf16 kv, 32q/8kv heads, d128, block16, batch64, ctx U[512,4096]",
     "c3": "llama3-70b-decode-layer bf16 kv, 64q/8kv heads, d128, block16, batch256, ctx 179xU[128,1024]+77xU[4096,32768]",
-    "c4": "long-context split-kv bf16 kv, 32q/8kv heads, d128, block16, batch4, ctx 131072, 512-token partitions",
+    "c4": "long-context split-kv bf16 kv, 32q/8kv heads, d128, block16, batch4, ctx 131072, "
+          "512-token partitions (256 per sequence) + reduction kernel",
+    "c4b": "long-context split-kv bf16 kv, 32q/8kv heads, d128, block16, batch4, ctx 131072, "
+           "balanced plan (near-equal partitions sized to the device, merged in the attention kernel)",
     "c2i8": "llama3-8b-decode-layer int8 kv (per-head scales), 32q/8kv heads, d128, block16, batch64, "
             "ctx U[512,4096]",
     "c2i4": "llama3-8b-decode-layer int4 kv (per-head scales, 2 codes/byte), 32q/8kv heads, d128, block16, "
@@ -72,9 +84,12 @@ def parse():
                     help="run the standalone paged-read floor probe (the decode step's tile reads alone, "
                          "8/4/2 KiB tiles) and exit")
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_NAMES))
-    ap.add_argument("--partition", type=int, default=-1, help="split-KV partition tokens (-1: balanced plan)")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="split-KV partition tokens (-1: balanced plan; default: the workload's own, "
+                         "512 for c4, -1 otherwise)")
     ap.add_argument("--rotate", type=int, default=3, help="independent pools cycled through")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="budget of each oracle sample (one thread, then all cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="run the step as three calls (slot mapping, append, attention) instead of one")
@@ -89,33 +104,60 @@ def kv_bytes(w):
     return int(int(w.seq_lens.astype("int64").sum()) * 2 * w.num_kv_heads * w.head_dim * elem)
 
 
+def host_cores():
+    """What the host offers the oracle: logical CPUs, the ones this process
+    may run on, and the BLAS thread pools numpy would use."""
+    from threadpoolctl import threadpool_info
+    blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")} for i in threadpool_info()]
+    return {"os_cpu_count": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)), "blas": blas}
+
+
 def cpu_baseline(w, pool_image, budget_s):
-    """The float64 oracle, single-threaded, on as many sequences as fit the budget."""
+    """The float64 oracle as it stands, timed on the host: first one thread
+    (one sequence after another), then every core of the process's affinity
+    (one oracle call per sequence on each thread, one BLAS thread each), each
+    on as many sequences as fit the budget."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     from threadpoolctl import threadpool_limits
     from oracle import attention as oatt
     from oracle import pool as opool
 
     desc = opool.PoolDesc(w.num_layers, w.num_blocks, w.num_kv_heads, w.head_dim, w.kv_dtype)
     q = opool.bf16_bits_to_float(w.q) if w.q_dtype == "bf16" else w.q.astype(np.float64)
-    done, tokens = 0, 0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        for s in range(w.batch):
-            oatt.verify(desc, pool_image, w.layer, w.block_tables, w.seq_lens, q, w.k_rows, w.scale,
-                        w.k_scale, w.v_scale, seqs=[s])
-            done += 1
-            tokens += int(w.seq_lens[s])
-            if time.perf_counter() - t0 > budget_s:
-                break
-        dt = time.perf_counter() - t0
     elem = ELEM_BYTES[w.kv_dtype]
-    nbytes = int(tokens * 2 * w.num_kv_heads * w.head_dim * elem)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seqs_per_s": round(done / dt, 3),
-            "sample": f"float64 numpy oracle {'decode' if w.k_rows == 1 else f'{w.k_rows}-row verify'} "
-                      f"of the first {done} of {w.batch} sequences "
-                      f"({tokens} tokens, {dt:.1f} s, one thread)"}
+    what = "decode" if w.k_rows == 1 else f"{w.k_rows}-row verify"
+
+    def one(s):
+        oatt.verify(desc, pool_image, w.layer, w.block_tables, w.seq_lens, q, w.k_rows, w.scale,
+                    w.k_scale, w.v_scale, seqs=[s])
+        return int(w.seq_lens[s])
+
+    def timed(threads):
+        done, tokens = 0, 0
+        with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=threads) as ex:
+            t0 = time.perf_counter()
+            while done < w.batch and time.perf_counter() - t0 < budget_s:
+                batch = list(range(done, min(w.batch, done + threads)))
+                tokens += sum(ex.map(one, batch))
+                done += len(batch)
+            dt = time.perf_counter() - t0
+        gbs = tokens * 2 * w.num_kv_heads * w.head_dim * elem / dt / 1e9
+        return done, tokens, dt, gbs
+
+    host = host_cores()
+    n1, t1, dt1, g1 = timed(1)
+    # at most 16 threads: the host's share for one GPU, whatever it reports
+    cores = max(1, min(16, host["affinity_cores"]))
+    na, ta, dta, ga = timed(cores)
+    return {"value": round(ga, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "seqs_per_s": round(na / dta, 3),
+            "sample": f"float64 numpy oracle {what} of the first {na} of {w.batch} sequences "
+                      f"({ta} tokens, {dta:.1f} s) on {cores} threads, one sequence per thread at a time, "
+                      f"one BLAS thread each",
+            "host": host,
+            "one_thread": {"value": round(g1, 4), "unit": "GB/s", "cores": 1, "seqs_per_s": round(n1 / dt1, 3),
+                           "sample": f"the first {n1} sequences ({t1} tokens, {dt1:.1f} s), one thread"}}
 
 
 def main():
@@ -144,8 +186,10 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    w = workloads.make(args.workload, materialize=False)
-    P = w.partition_tokens if args.partition is None else args.partition
+    w = workloads.make("c4" if args.workload == "c4b" else args.workload, materialize=False)
+    P = args.partition
+    if P is None:
+        P = 512 if args.workload == "c4" else -1
 
     ks = vs = None
     if w.kv_dtype in ("fp8", "int8", "int4"):
@@ -183,8 +227,8 @@ def main():
     K, W = args.steps, args.warmup
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
 
-    def step(i, timed):
-        pool = pools[i % len(pools)]
+    def step(i, timed, pool=None):
+        pool = pools[i % len(pools)] if pool is None else pool
         if args.separate:
             pk.slot_mapping_compute(table, sid, pos, out=slots)
             pk.reshape_and_cache(pool, w.layer, k_new, v_new, slots)
@@ -221,6 +265,17 @@ def main():
     torch.cuda.synchronize()
     attn_ms = [a.elapsed_time(b) for a, b in ev]
     attn_avg = sum(attn_ms) / len(attn_ms)
+    # Warm: K steps back to back on one pool, so part of each step's KV may
+    # still sit in the 256 MB Infinity Cache from the step before.
+    for i in range(W):
+        step(i, False, pools[0])
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(K):
+        step(i, False, pools[0])
+    t_stop.record()
+    torch.cuda.synchronize()
+    warm_ms = t_start.elapsed_time(t_stop) / K
 
     nbytes = kv_bytes(w)
     value = nbytes / (ms_step * 1e-3) / 1e9
@@ -232,6 +287,7 @@ def main():
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     info = table.info()
 
+    unique_bytes = int(int(w.info["blocks_used"]) * 16 * 2 * w.num_kv_heads * w.head_dim * ELEM_BYTES[w.kv_dtype])
     kernel_label = ("attn_partition_kernel (split-KV merge inside)" if info["max_parts"] <= 32
                     else "attn_partition_kernel + attn_merge_kernel")
     traffic = None
@@ -259,14 +315,24 @@ def main():
                    "step": "slot_mapping_compute + reshape_and_cache + paged_attention_decode" if args.separate
                            else "paged_attention_append (slot mapping, append and attention in one launch)",
                    "tokens": int(w.seq_lens.sum()), "query_rows": kq, "partition_tokens": P,
-                   "unique_kv_bytes": int(int(w.info["blocks_used"]) * 16 * 2 * w.num_kv_heads * w.head_dim
-                                          * ELEM_BYTES[w.kv_dtype]),
+                   "unique_kv_bytes": unique_bytes,
                    "pools_rotated": len(pools), "work_units": info["num_units"]},
         "seqs_per_s": round(w.batch / (ms_step * 1e-3), 1),
+        "unique_kv_gbs": round(unique_bytes / (ms_step * 1e-3) / 1e9, 2),
         "pct_hbm_peak_step": round(100.0 * value / HBM_PEAK_GBS, 2),
         "attention_ms": round(attn_avg, 5),
         "attention_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 5),
                                  round(float(np.percentile(attn_ms, 90)), 5)],
+        "per_step_ms": {"median": round(float(np.percentile(attn_ms, 50)), 5),
+                        "p10": round(float(np.percentile(attn_ms, 10)), 5),
+                        "p90": round(float(np.percentile(attn_ms, 90)), 5),
+                        "samples": len(attn_ms),
+                        "estimator": "numpy.percentile, linear interpolation between order statistics, "
+                                     "over per-step HIP-event times (events around each step)"},
+        "flushed_vs_warm_ms_per_step": {"flushed": round(ms_step, 5), "warm": round(warm_ms, 5),
+                                        "flushed_means": f"{len(pools)} independently filled pools rotated "
+                                                         "(each step's KV is not in the Infinity Cache)",
+                                        "warm_means": "one pool, steps back to back"},
         "kv_bytes_per_step": nbytes,
         "wall_s": round(wall, 3),
         "roofline": {"bound": "hbm", "kernel": kernel_label,

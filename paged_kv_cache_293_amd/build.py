@@ -36,7 +36,9 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
+def build(verbose=False, probes=True):
+    """Compile the library (errors raise), then the standalone probes, whose
+    failure is reported but does not fail the library build."""
     os.makedirs(LIB_DIR, exist_ok=True)
     tmp = LIB_PATH + ".tmp"
     cmd = [HIPCC] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
@@ -50,16 +52,27 @@ def build(verbose=False):
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, LIB_PATH)
+    if probes:
+        for src, ok, msg in build_probes():
+            if not ok:
+                print(f"warning: the probe {src} did not build (the library did):\n{msg}", file=sys.stderr)
+    return LIB_PATH
+
+
+def build_probes():
+    """Compile the standalone probes; returns (source, ok, compiler messages) per probe."""
+    noise = "is not a recognized feature for this target"
+    results = []
     for src, exe in PROBES:
         out = os.path.join(LIB_DIR, exe)
         cmd = [HIPCC] + [f for f in FLAGS if f not in ("-shared", "-fPIC")] + [os.path.join(HERE, "probe", src),
                                                                              "-o", out + ".tmp"]
         res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            raise RuntimeError(f"hipcc failed on the probe {src}:\n" +
-                               "\n".join(l for l in res.stderr.splitlines() if noise not in l))
-        os.replace(out + ".tmp", out)
-    return LIB_PATH
+        msg = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+        if res.returncode == 0:
+            os.replace(out + ".tmp", out)
+        results.append((src, res.returncode == 0, msg))
+    return results
 
 
 if __name__ == "__main__":

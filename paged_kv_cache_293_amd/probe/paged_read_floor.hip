@@ -1,16 +1,31 @@
-// Paged-read floor of this device at the decode kernel's shape: a standalone
-// program (not part of the library).  It reads 77,824 tiles (the (block, KV
-// head) tiles of a 64-sequence Llama-3-8B decode step) of one size, 8 KiB
-// (bf16 K+V at head dim 128), 4 KiB (fp8 / int8) or 2 KiB (int4), at random
-// positions of one of three 768 MiB regions taken in turn, so no launch finds
-// the previous launch's tiles in the 256 MB Infinity Cache.  Like the decode
-// kernel, each work-group of 4 waves takes an equal run of tiles, its waves
-// take them round robin, 16 bytes per lane per load, with 1 or 2 tiles in
-// flight per wave while one is consumed; the grid holds 2, 3 or 4 work-groups
-// per CU (set with the dynamic LDS size).  Every index is checked against the
-// region on the host.  Prints the median launch time over 30 launches and
-// the rate, per tile size and configuration.
+// Paged-read floor at the decode step's shape: a standalone program (not part
+// of the library).  It reads exactly the tiles a Llama-3-8B decode step reads
+// (64 sequences, lengths uniform in [512, 4096], 16-token blocks, 8 KV heads,
+// blocks placed by a random permutation over a pool of 1.25x the blocks in
+// use) and nothing else: no scores, no softmax, no output.  Pool layout as the
+// library's: the 8 KV heads' tiles of a block are adjacent, so one block is
+// 8 x S contiguous bytes (S = 8 KiB for bf16 K+V at head dim 128, 4 KiB for
+// one-byte codes, 2 KiB for int4).
+//
+// The tiles are listed in one of two orders and cut into equal runs, one run
+// per work-group; a work-group's 4 waves take its run's tiles round robin,
+// 16 bytes per lane per load (at 2 work-groups per CU with two tiles in flight
+// per wave while a third is consumed: the decode kernel's pipeline):
+//   head : sequence, then KV head, then block (the decode kernel's order: a
+//          work-group walks one head of one sequence, reading one S-byte tile
+//          of each 8 x S-byte block);
+//   block: sequence, then block, then KV head (a work-group's waves read the
+//          adjacent tiles of one block together: 8 x S contiguous bytes).
+// Three pool copies are read in turn, so no launch finds the previous one's
+// tiles in the 256 MB Infinity Cache.  Grids of 2, 4 and 8 work-groups per CU
+// (a work-group is one wave on each SIMD, so 2, 4 and 8 waves per SIMD); so
+// that every work-group of the grid is resident at once, the 4 per CU grid
+// keeps one tile per wave in flight while one is consumed, and the 8 per CU
+// grid one tile per wave (load, consume).  Every tile index is checked
+// against the pool on the host.
+// Prints the median launch time over 30 launches, p10 and p90, and the rate.
 #include <hip/hip_runtime.h>
+
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
@@ -20,13 +35,17 @@
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 #define CK(x) do { hipError_t e = (x); if (e != hipSuccess) { printf("HIP error %s at %d\n", hipGetErrorString(e), __LINE__); exit(1); } } while (0)
 
+constexpr int kHeads = 8;
+constexpr int kSeqs = 64;
+constexpr int kCopies = 3;
+
 template <int S> struct Tile { u32x4 w[S / 1024]; };   // 1 KiB per wave load
 
 template <int S>
-__device__ __forceinline__ void load_tile(Tile<S>& t, const unsigned char* buf, int id, bool valid, int lane) {
+__device__ __forceinline__ void load_tile(Tile<S>& t, const unsigned char* pool, long tile, bool valid, int lane) {
     // a zero-sized resource returns zeros without touching memory
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned char*>(buf + static_cast<long>(id) * S), 0, valid ? S : 0, 0x00020000);
+        const_cast<unsigned char*>(pool + tile * S), 0, valid ? S : 0, 0x00020000);
 #pragma unroll
     for (int s = 0; s < S / 1024; ++s)
         t.w[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 1024 * s, 0));
@@ -40,73 +59,129 @@ __device__ __forceinline__ unsigned fold(const Tile<S>& t) {
     return a;
 }
 
-// Work-group b reads tiles idx[b * per .. (b + 1) * per); wave w takes w, w + 4, ...
+// Work-group b reads tiles list[b * per .. b * per + run), run <= per (the
+// last runs may be shorter); wave w takes w, w + 4, ...  DEPTH 2: three tile
+// buffers (two tiles in flight while one is consumed); DEPTH 1: two buffers;
+// DEPTH 0: one buffer (load, consume, load).
 template <int S, int DEPTH>
-__global__ __launch_bounds__(256) void read_tiles(const unsigned char* buf, const int* idx, int per, unsigned* out) {
-    extern __shared__ int lds_pad[];
+__global__ __launch_bounds__(256) void read_tiles(const unsigned char* pool, const int* list, int per, int total,
+                                                  unsigned* out) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-    const int* my = idx + static_cast<long>(blockIdx.x) * per;
-    const int cnt = (per - wave + 3) / 4;
-    auto id = [&](int i) { return i < cnt ? my[wave + 4 * i] : 0; };
+    const int* my = list + static_cast<long>(blockIdx.x) * per;
+    const int run = max(0, min(per, total - static_cast<int>(blockIdx.x) * per));
+    const int cnt = (run - wave + 3) / 4;
+    auto id = [&](int i) { return i < cnt ? static_cast<long>(my[wave + 4 * i]) : 0L; };
     unsigned acc = 0;
-    Tile<S> ta, tb, tc;
-    load_tile<S>(ta, buf, id(0), cnt > 0, lane);
-    if (DEPTH == 2) load_tile<S>(tb, buf, id(1), cnt > 1, lane);
-    int i = 0;
-    if (DEPTH == 2) {
+    if constexpr (DEPTH == 2) {
+        Tile<S> ta, tb, tc;
+        load_tile<S>(ta, pool, id(0), cnt > 0, lane);
+        load_tile<S>(tb, pool, id(1), cnt > 1, lane);
+        int i = 0;
         for (; i + 2 < cnt; i += 3) {
-            load_tile<S>(tc, buf, id(i + 2), true, lane);
+            load_tile<S>(tc, pool, id(i + 2), true, lane);
             acc += fold<S>(ta);
-            load_tile<S>(ta, buf, id(i + 3), i + 3 < cnt, lane);
+            load_tile<S>(ta, pool, id(i + 3), i + 3 < cnt, lane);
             acc += fold<S>(tb);
-            load_tile<S>(tb, buf, id(i + 4), i + 4 < cnt, lane);
+            load_tile<S>(tb, pool, id(i + 4), i + 4 < cnt, lane);
             acc += fold<S>(tc);
         }
         if (i < cnt) acc += fold<S>(ta);
         if (i + 1 < cnt) acc += fold<S>(tb);
-    } else {
+    } else if constexpr (DEPTH == 1) {
+        Tile<S> ta, tb;
+        load_tile<S>(ta, pool, id(0), cnt > 0, lane);
+        int i = 0;
         for (; i + 1 < cnt; i += 2) {
-            load_tile<S>(tb, buf, id(i + 1), true, lane);
+            load_tile<S>(tb, pool, id(i + 1), true, lane);
             acc += fold<S>(ta);
-            load_tile<S>(ta, buf, id(i + 2), i + 2 < cnt, lane);
+            load_tile<S>(ta, pool, id(i + 2), i + 2 < cnt, lane);
             acc += fold<S>(tb);
         }
         if (i < cnt) acc += fold<S>(ta);
+    } else {
+        for (int i = 0; i < cnt; ++i) {
+            Tile<S> t;
+            load_tile<S>(t, pool, id(i), true, lane);
+            acc += fold<S>(t);
+        }
     }
-    if (acc == 0x12345678u) out[blockIdx.x] = acc + static_cast<unsigned>(lds_pad[0]);   // keeps the loads
+    if (acc == 0x12345678u) out[blockIdx.x] = acc;   // keeps the loads
 }
 
-constexpr long kRegionBytes = 768L << 20;
-constexpr int kRegions = 3;
-constexpr long kTiles = 77824;
+struct Step {
+    std::vector<int> lens;      // tokens per sequence
+    std::vector<std::vector<int>> table;   // physical block of each logical block
+    int num_blocks = 0;         // pool blocks
+};
+
+Step make_step(std::mt19937_64& rng) {
+    Step st;
+    std::uniform_int_distribution<int> len(512, 4096);
+    int used = 0;
+    for (int s = 0; s < kSeqs; ++s) {
+        st.lens.push_back(len(rng));
+        used += (st.lens.back() + 15) / 16;
+    }
+    st.num_blocks = (used * 5 + 3) / 4;
+    std::vector<int> perm(st.num_blocks);
+    for (int i = 0; i < st.num_blocks; ++i) perm[i] = i;
+    std::shuffle(perm.begin(), perm.end(), rng);
+    int cursor = 0;
+    for (int s = 0; s < kSeqs; ++s) {
+        const int nb = (st.lens[s] + 15) / 16;
+        st.table.emplace_back(perm.begin() + cursor, perm.begin() + cursor + nb);
+        cursor += nb;
+    }
+    return st;
+}
+
+// Tile index = block * kHeads + head, in the chosen order.
+std::vector<int> tile_list(const Step& st, bool block_major) {
+    std::vector<int> out;
+    for (int s = 0; s < kSeqs; ++s) {
+        const std::vector<int>& t = st.table[s];
+        if (block_major) {
+            for (int b : t)
+                for (int h = 0; h < kHeads; ++h) out.push_back(b * kHeads + h);
+        } else {
+            for (int h = 0; h < kHeads; ++h)
+                for (int b : t) out.push_back(b * kHeads + h);
+        }
+    }
+    return out;
+}
 
 template <int S>
-void run(unsigned char* buf, unsigned* d_out, int wgs_per_cu, int depth, std::mt19937_64& rng) {
-    const long region_tiles = kRegionBytes / S;
+void run(const Step& st, bool block_major, int wgs_per_cu, unsigned* d_out) {
+    const long copy_bytes = static_cast<long>(st.num_blocks) * kHeads * S;
+    unsigned char* buf;
+    CK(hipMalloc(&buf, copy_bytes * kCopies));
+    CK(hipMemset(buf, 1, copy_bytes * kCopies));
+    std::vector<int> list = tile_list(st, block_major);
     const int grid = 256 * wgs_per_cu;
-    const int per = static_cast<int>(kTiles / grid);
-    const long n = static_cast<long>(per) * grid;
-    std::vector<int*> d_idx(kRegions);
-    std::vector<int> perm(region_tiles), h(n);
-    for (int r = 0; r < kRegions; ++r) {
-        for (long i = 0; i < region_tiles; ++i) perm[i] = static_cast<int>(i);
-        std::shuffle(perm.begin(), perm.end(), rng);
-        for (long i = 0; i < n; ++i) {
-            h[i] = static_cast<int>(r * region_tiles + perm[i]);
-            if (h[i] < 0 || h[i] >= region_tiles * kRegions) { printf("bad index\n"); exit(1); }
-        }
-        CK(hipMalloc(&d_idx[r], sizeof(int) * n));
-        CK(hipMemcpy(d_idx[r], h.data(), sizeof(int) * n, hipMemcpyHostToDevice));
-    }
-    // LDS per work-group that lets exactly wgs_per_cu of them share a CU's 160 KB
-    const size_t lds = wgs_per_cu == 2 ? 64 * 1024 : (wgs_per_cu == 3 ? 48 * 1024 : 36 * 1024);
-    auto launch = [&](int r) {
-        if (depth == 2) hipLaunchKernelGGL((read_tiles<S, 2>), dim3(grid), dim3(256), lds, 0, buf, d_idx[r], per, d_out);
-        else hipLaunchKernelGGL((read_tiles<S, 1>), dim3(grid), dim3(256), lds, 0, buf, d_idx[r], per, d_out);
+    const int per = static_cast<int>((list.size() + grid - 1) / grid);
+    const int total = static_cast<int>(list.size());
+    const long tiles = total;
+    for (int x : list)
+        if (x < 0 || static_cast<long>(x) >= static_cast<long>(st.num_blocks) * kHeads) { printf("bad tile\n"); exit(1); }
+    if (static_cast<long>(per) * grid < total) { printf("bad runs\n"); exit(1); }
+    int* d_list;
+    CK(hipMalloc(&d_list, sizeof(int) * list.size()));
+    CK(hipMemcpy(d_list, list.data(), sizeof(int) * list.size(), hipMemcpyHostToDevice));
+    auto launch = [&](int c) {
+        if (wgs_per_cu >= 8)
+            hipLaunchKernelGGL((read_tiles<S, 0>), dim3(grid), dim3(256), 0, 0, buf + c * copy_bytes, d_list, per,
+                               total, d_out);
+        else if (wgs_per_cu >= 4)
+            hipLaunchKernelGGL((read_tiles<S, 1>), dim3(grid), dim3(256), 0, 0, buf + c * copy_bytes, d_list, per,
+                               total, d_out);
+        else
+            hipLaunchKernelGGL((read_tiles<S, 2>), dim3(grid), dim3(256), 0, 0, buf + c * copy_bytes, d_list, per,
+                               total, d_out);
         CK(hipGetLastError());
     };
-    for (int w = 0; w < 6; ++w) launch(w % kRegions);
+    for (int w = 0; w < 6; ++w) launch(w % kCopies);
     CK(hipDeviceSynchronize());
     hipEvent_t e0, e1;
     CK(hipEventCreate(&e0));
@@ -114,7 +189,7 @@ void run(unsigned char* buf, unsigned* d_out, int wgs_per_cu, int depth, std::mt
     std::vector<float> ts;
     for (int rep = 0; rep < 30; ++rep) {
         CK(hipEventRecord(e0));
-        launch(rep % kRegions);
+        launch(rep % kCopies);
         CK(hipEventRecord(e1));
         CK(hipEventSynchronize(e1));
         float ms = 0;
@@ -122,29 +197,31 @@ void run(unsigned char* buf, unsigned* d_out, int wgs_per_cu, int depth, std::mt
         ts.push_back(ms);
     }
     std::sort(ts.begin(), ts.end());
-    const double gb = static_cast<double>(n) * S / 1e9;
-    printf("tile %5d B  %6.1f MB  %d work-groups/CU  %d in flight/wave: %6.1f us (%5.0f GB/s), p10 %.1f p90 %.1f us\n",
-           S, gb * 1e3, wgs_per_cu, depth, ts[15] * 1e3, gb / (ts[15] * 1e-3), ts[3] * 1e3, ts[27] * 1e3);
+    const double gb = static_cast<double>(tiles) * S / 1e9;
+    printf("tile %5d B  order %-5s  %d WG/CU: %6.1f MB  median %6.1f us (%5.0f GB/s)  p10 %6.1f  p90 %6.1f us\n",
+           S, block_major ? "block" : "head", wgs_per_cu, gb * 1e3, ts[15] * 1e3, gb / (ts[15] * 1e-3),
+           ts[3] * 1e3, ts[27] * 1e3);
     fflush(stdout);
     CK(hipEventDestroy(e0));
     CK(hipEventDestroy(e1));
-    for (int r = 0; r < kRegions; ++r) CK(hipFree(d_idx[r]));
+    CK(hipFree(d_list));
+    CK(hipFree(buf));
 }
 
 int main() {
-    unsigned char* buf;
+    std::mt19937_64 rng(293002);
+    const Step st = make_step(rng);
+    long tokens = 0;
+    for (int n : st.lens) tokens += n;
+    printf("decode step: %d sequences, %ld tokens, pool of %d blocks\n", kSeqs, tokens, st.num_blocks);
     unsigned* d_out;
-    CK(hipMalloc(&buf, kRegionBytes * kRegions));
-    CK(hipMemset(buf, 1, kRegionBytes * kRegions));
-    CK(hipMalloc(&d_out, sizeof(unsigned) * 1024));
-    std::mt19937_64 rng(293);
-    for (int wpc = 2; wpc <= 4; ++wpc)
-        for (int depth = 1; depth <= 2; ++depth) {
-            run<8192>(buf, d_out, wpc, depth, rng);
-            run<4096>(buf, d_out, wpc, depth, rng);
-            run<2048>(buf, d_out, wpc, depth, rng);
+    CK(hipMalloc(&d_out, sizeof(unsigned) * 256 * 8));
+    for (int wpc : {2, 4, 8})
+        for (int bm = 0; bm <= 1; ++bm) {
+            run<8192>(st, bm == 1, wpc, d_out);
+            run<4096>(st, bm == 1, wpc, d_out);
+            run<2048>(st, bm == 1, wpc, d_out);
         }
-    CK(hipFree(buf));
     CK(hipFree(d_out));
     return 0;
 }

@@ -1,85 +1,149 @@
-// HBM read ceilings of this device, for the attention kernels' rooflines: a
-// standalone program (not part of the library).  Each wave reads whole tiles
-// of S bytes (K and V tile of one block and KV head: 2 KiB int4, 4 KiB int8 /
-// fp8, 8 KiB bf16 at head dim 128) at tile indices from a host-made list,
-// four tiles in flight per wave, 8 waves per SIMD, from a 2 GiB buffer:
-// "random" draws the indices uniformly (paged placement), "stream" takes them
-// in order (a contiguous read).  Every index is checked against the tile
-// count on the host.  Prints GB/s per mode and tile size.
+// HBM read ceiling of this device: a standalone program (not part of the
+// library).  Each launch reads one whole 768 MiB region once, in 8 KiB
+// pieces (16 bytes per lane per load, 1 KiB per wave load), in one of three
+// orders:
+//   stream  : pieces in address order (the region read front to back);
+//   random8 : a random permutation of the pieces (each read once);
+//   random64: a random permutation of 64 KiB blocks, each block's 8 pieces
+//             in order (the pool's (block, 8 KV heads) runs at bf16 d 128).
+// Piece p of the list is read by wave p mod W of the grid (W waves in all),
+// so at any moment adjacent list entries are read by waves running side by
+// side.  Three regions are read in turn, so no launch finds the previous
+// one's bytes in the 256 MB Infinity Cache.  Grids of 2 work-groups per CU
+// (three pieces per wave, two in flight while one is consumed) and 8 per CU
+// (one piece per wave at a time); a work-group is one wave on each SIMD.
+// Every piece index is checked against the region on the host.  Prints the
+// median launch time over 30 launches and the rate.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
-#include <vector>
 #include <random>
+#include <vector>
+
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 #define CK(x) do { hipError_t e = (x); if (e != hipSuccess) { printf("HIP error %s at %d\n", hipGetErrorString(e), __LINE__); exit(1); } } while (0)
 
-template <int S>
-__global__ __launch_bounds__(256) void probe(const u32x4* __restrict__ buf, const int* __restrict__ idx,
-                                             int tiles_per_wave, unsigned* out) {
-    const int lane = threadIdx.x & 63;
-    const int wave = (blockIdx.x * 4) + (threadIdx.x >> 6);
-    const int* my = idx + static_cast<long>(wave) * tiles_per_wave;
-    constexpr int PER = S / 1024;          // 1 KiB per wave instruction
-    unsigned acc = 0;
-    for (int t = 0; t < tiles_per_wave; t += 4) {
-        u32x4 v[4][PER];
+constexpr int kPiece = 8192;
+constexpr long kRegionBytes = 768L << 20;
+constexpr int kRegions = 3;
+constexpr int kPieces = static_cast<int>(kRegionBytes / kPiece);
+
+struct Piece { u32x4 w[kPiece / 1024]; };
+
+__device__ __forceinline__ void load_piece(Piece& t, const unsigned char* region, int piece, bool valid, int lane) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(region + static_cast<long>(piece) * kPiece), 0, valid ? kPiece : 0, 0x00020000);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const u32x4* base = buf + static_cast<long>(my[t + u]) * (S / 16);
-#pragma unroll
-            for (int p = 0; p < PER; ++p) v[u][p] = base[p * 64 + lane];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int p = 0; p < PER; ++p) acc ^= v[u][p][0] ^ v[u][p][1] ^ v[u][p][2] ^ v[u][p][3];
-    }
-    if (acc == 0x12345678u) out[wave] = acc;     // keeps the loads alive
+    for (int s = 0; s < kPiece / 1024; ++s)
+        t.w[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 1024 * s, 0));
 }
 
-template <int S>
-void run(const u32x4* buf, size_t bytes, int* d_idx, std::vector<int>& h_idx, unsigned* d_out, bool random) {
-    const long n_tiles = static_cast<long>(bytes / S);
-    const int waves = 256 * 4 * 8;              // 8 waves per SIMD
-    const int tpw = static_cast<int>((1L << 30) / S / waves) / 4 * 4;   // ~1 GiB read per launch
-    std::mt19937_64 rng(293);
-    for (long i = 0; i < static_cast<long>(waves) * tpw; ++i)
-        h_idx[i] = static_cast<int>(random ? rng() % n_tiles : i % n_tiles);
-    for (long i = 0; i < static_cast<long>(waves) * tpw; ++i)
-        if (h_idx[i] < 0 || h_idx[i] >= n_tiles) { printf("bad index\n"); exit(1); }
-    CK(hipMemcpy(d_idx, h_idx.data(), sizeof(int) * waves * tpw, hipMemcpyHostToDevice));
-    hipEvent_t e0, e1;
-    CK(hipEventCreate(&e0)); CK(hipEventCreate(&e1));
-    for (int w = 0; w < 3; ++w) hipLaunchKernelGGL(probe<S>, dim3(waves / 4), dim3(256), 0, 0, buf, d_idx, tpw, d_out);
-    CK(hipDeviceSynchronize());
-    const int reps = 10;
-    CK(hipEventRecord(e0));
-    for (int r = 0; r < reps; ++r) hipLaunchKernelGGL(probe<S>, dim3(waves / 4), dim3(256), 0, 0, buf, d_idx, tpw, d_out);
-    CK(hipEventRecord(e1));
-    CK(hipEventSynchronize(e1));
-    float ms = 0; CK(hipEventElapsedTime(&ms, e0, e1));
-    const double gb = static_cast<double>(waves) * tpw * S * reps / 1e9;
-    printf("%-6s tile %6d B: %8.1f GB/s (%.3f ms per launch)\n", random ? "random" : "stream", S,
-           gb / (ms * 1e-3), ms / reps);
-    fflush(stdout);
+__device__ __forceinline__ unsigned fold(const Piece& t) {
+    unsigned a = 0;
+#pragma unroll
+    for (int s = 0; s < kPiece / 1024; ++s) a ^= t.w[s][0] ^ t.w[s][1] ^ t.w[s][2] ^ t.w[s][3];
+    return a;
+}
+
+// Wave g reads list[g], list[g + W], ...  (cnt of them).
+template <int DEPTH>
+__global__ __launch_bounds__(256) void read_region(const unsigned char* region, const int* list, int n, unsigned* out) {
+    const int lane = threadIdx.x & 63;
+    const int W = static_cast<int>(gridDim.x) * 4;
+    const int g = static_cast<int>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int cnt = g < n ? (n - g + W - 1) / W : 0;
+    auto id = [&](int i) { return i < cnt ? list[g + i * W] : 0; };
+    unsigned acc = 0;
+    if constexpr (DEPTH == 2) {
+        Piece ta, tb, tc;
+        load_piece(ta, region, id(0), cnt > 0, lane);
+        load_piece(tb, region, id(1), cnt > 1, lane);
+        int i = 0;
+        for (; i + 2 < cnt; i += 3) {
+            load_piece(tc, region, id(i + 2), true, lane);
+            acc += fold(ta);
+            load_piece(ta, region, id(i + 3), i + 3 < cnt, lane);
+            acc += fold(tb);
+            load_piece(tb, region, id(i + 4), i + 4 < cnt, lane);
+            acc += fold(tc);
+        }
+        if (i < cnt) acc += fold(ta);
+        if (i + 1 < cnt) acc += fold(tb);
+    } else {
+        for (int i = 0; i < cnt; ++i) {
+            Piece t;
+            load_piece(t, region, id(i), true, lane);
+            acc += fold(t);
+        }
+    }
+    if (acc == 0x12345678u) out[blockIdx.x] = acc;   // keeps the loads
 }
 
 int main() {
-    const size_t bytes = 2ull << 30;
-    u32x4* buf; int* d_idx; unsigned* d_out;
-    CK(hipMalloc(&buf, bytes));
-    CK(hipMemset(buf, 1, bytes));
-    const size_t max_idx = (1ull << 30) / 2048;    // tile >= 2 KiB
-    CK(hipMalloc(&d_idx, sizeof(int) * max_idx));
-    CK(hipMalloc(&d_out, sizeof(unsigned) * 256 * 4 * 8));
-    std::vector<int> h_idx(max_idx);
-    for (int random = 1; random >= 0; --random) {
-        run<2048>(buf, bytes, d_idx, h_idx, d_out, random);
-        run<4096>(buf, bytes, d_idx, h_idx, d_out, random);
-        run<8192>(buf, bytes, d_idx, h_idx, d_out, random);
-        run<16384>(buf, bytes, d_idx, h_idx, d_out, random);
+    unsigned char* buf;
+    unsigned* d_out;
+    int* d_list;
+    CK(hipMalloc(&buf, kRegionBytes * kRegions));
+    CK(hipMemset(buf, 1, kRegionBytes * kRegions));
+    CK(hipMalloc(&d_out, sizeof(unsigned) * 256 * 8));
+    CK(hipMalloc(&d_list, sizeof(int) * kPieces));
+    std::mt19937_64 rng(293);
+    const char* names[3] = {"stream", "random8", "random64"};
+    for (int mode = 0; mode < 3; ++mode) {
+        std::vector<int> list(kPieces);
+        if (mode == 0) {
+            for (int i = 0; i < kPieces; ++i) list[i] = i;
+        } else if (mode == 1) {
+            for (int i = 0; i < kPieces; ++i) list[i] = i;
+            std::shuffle(list.begin(), list.end(), rng);
+        } else {
+            std::vector<int> blocks(kPieces / 8);
+            for (int i = 0; i < kPieces / 8; ++i) blocks[i] = i;
+            std::shuffle(blocks.begin(), blocks.end(), rng);
+            for (int i = 0; i < kPieces; ++i) list[i] = blocks[i / 8] * 8 + i % 8;
+        }
+        std::vector<char> seen(kPieces, 0);
+        for (int x : list) {
+            if (x < 0 || x >= kPieces || seen[x]) { printf("bad piece list\n"); exit(1); }
+            seen[x] = 1;
+        }
+        CK(hipMemcpy(d_list, list.data(), sizeof(int) * kPieces, hipMemcpyHostToDevice));
+        for (int wpc : {2, 8}) {
+            const int grid = 256 * wpc;
+            auto launch = [&](int r) {
+                const unsigned char* region = buf + r * kRegionBytes;
+                if (wpc == 2) hipLaunchKernelGGL(read_region<2>, dim3(grid), dim3(256), 0, 0, region, d_list, kPieces, d_out);
+                else hipLaunchKernelGGL(read_region<0>, dim3(grid), dim3(256), 0, 0, region, d_list, kPieces, d_out);
+                CK(hipGetLastError());
+            };
+            for (int w = 0; w < 6; ++w) launch(w % kRegions);
+            CK(hipDeviceSynchronize());
+            hipEvent_t e0, e1;
+            CK(hipEventCreate(&e0));
+            CK(hipEventCreate(&e1));
+            std::vector<float> ts;
+            for (int rep = 0; rep < 30; ++rep) {
+                CK(hipEventRecord(e0));
+                launch(rep % kRegions);
+                CK(hipEventRecord(e1));
+                CK(hipEventSynchronize(e1));
+                float ms = 0;
+                CK(hipEventElapsedTime(&ms, e0, e1));
+                ts.push_back(ms);
+            }
+            std::sort(ts.begin(), ts.end());
+            const double gb = static_cast<double>(kRegionBytes) / 1e9;
+            printf("%-8s %d WG/CU: %.1f MB per launch, median %7.1f us (%5.0f GB/s), p10 %7.1f  p90 %7.1f us\n",
+                   names[mode], wpc, gb * 1e3, ts[15] * 1e3, gb / (ts[15] * 1e-3), ts[3] * 1e3, ts[27] * 1e3);
+            fflush(stdout);
+            CK(hipEventDestroy(e0));
+            CK(hipEventDestroy(e1));
+        }
     }
-    CK(hipFree(buf)); CK(hipFree(d_idx)); CK(hipFree(d_out));
+    CK(hipFree(buf));
+    CK(hipFree(d_out));
+    CK(hipFree(d_list));
     return 0;
 }
