@@ -59,6 +59,9 @@ typedef int32_t pkv_status;
 #define PKV_ERR_WORKSPACE   (-5) /* device buffer or workspace too small       */
 #define PKV_ERR_HIP         (-6) /* the HIP runtime reported an error          */
 #define PKV_ERR_OUT_OF_BLOCKS (-7) /* block manager: not enough free blocks     */
+#define PKV_ERR_TABLE_STALE (-8) /* an earlier attention launch on this table
+                                    failed; its merge counters may not be zero:
+                                    upload the table again                      */
 
 /* Element types. */
 #define PKV_F32      0  /* IEEE binary32                                        */
@@ -84,8 +87,8 @@ typedef int32_t pkv_status;
  * The pool is one caller-owned device buffer of kv_pool_bytes(desc) bytes,
  * i.e. num_blocks * 16 token slots times the per-token size
  * 2 * num_layers * num_kv_heads * head_dim * b (b = 4, 2, 1, 1/2 bytes), which is
- * the page-1 formula of section "KV cache memory math" applied to the pool's
- * capacity.
+ * the per-token formula of page "KV cache & continuous batching", section "KV
+ * cache memory math", applied to the pool's capacity.
  *
  * Byte layout.  The buffer is an array of tiles, one per
  * (layer l, physical block p, KV head h, kv in {K = 0, V = 1}); tile
@@ -138,7 +141,13 @@ int64_t kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t hea
 int64_t kv_pool_bytes(const pkv_pool_desc* desc);
 
 /*
- * Wrap a caller-allocated pool buffer in a handle.
+ * Wrap a caller-allocated pool buffer in a handle: the physical blocks the
+ * block tables name (page "KV cache & continuous batching", section
+ * "2. PagedAttention (vLLM)": the cache is split into fixed-size physical
+ * blocks that need not be contiguous, handed to requests on demand; section
+ * "KV cache memory math" for the bytes per token; page "LLM Serving - KV
+ * Cache, Batching, Speculative Decoding", section "KV memory, paging and
+ * prefix identity": physical blocks may be shared by several sequences).
  *   dev_base   device buffer of at least kv_pool_bytes(desc) bytes, 256-byte aligned.
  *   dev_k_scale, dev_v_scale  float32 [num_layers][num_kv_heads] device arrays;
  *              required (non-NULL) for PKV_FP8_E4M3, PKV_INT8 and PKV_INT4, ignored otherwise.
@@ -186,8 +195,11 @@ size_t block_table_device_bytes(const pkv_pool* pool, const int32_t* host_seq_le
  * The host arrays are copied into the handle before returning; the copy to
  * dev_buffer is enqueued on `stream`.  Destroying the handle waits for that
  * copy.  The buffer also holds the arrival counters of the in-kernel merge,
- * which every attention call leaves at zero: attention calls that use one
- * table must not overlap (issue them on one stream).  Errors: PKV_ERR_INVALID, PKV_ERR_BLOCK_RANGE, PKV_ERR_SEQ_LEN,
+ * which every attention launch that completes leaves at zero: attention calls
+ * that use one table must not overlap (issue them on one stream).  A table
+ * whose attention launch returned PKV_ERR_HIP is marked stale and refused by
+ * later attention calls (PKV_ERR_TABLE_STALE) until it is uploaded again.
+ * Errors: PKV_ERR_INVALID, PKV_ERR_BLOCK_RANGE, PKV_ERR_SEQ_LEN,
  * PKV_ERR_WORKSPACE (dev_buffer too small), PKV_ERR_HIP.
  */
 pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_table,
@@ -250,7 +262,14 @@ size_t paged_attention_workspace_bytes(const pkv_pool* pool, const pkv_table* ta
                                        int32_t num_q_heads, int32_t query_rows);
 
 /*
- * Decode attention, one query token per sequence:
+ * Decode attention, one query token per sequence (page "KV cache & continuous
+ * batching", section "The core insight": the new token's query attends over
+ * the cached K and V of every earlier token and its own; section
+ * "2. PagedAttention (vLLM)": K and V are gathered through the sequence's list
+ * of blocks; section "KV cache memory math": query heads of a group share a KV
+ * head; page "LLM Serving - KV Cache, Batching, Speculative Decoding", section
+ * "Hands-on: cache equivalence and scheduling oracles": the cached result is
+ * softmax attention over the visible rows):
  *   out[s][g] = softmax( scale * q[s][g] . K_s[t][h]^T, t < seq_len[s] ) V_s[t][h],
  *   h = g / (num_q_heads / num_kv_heads)          (grouped-query sharing)
  * with K_s, V_s read from `layer` of the pool through the table's block list.
@@ -266,7 +285,9 @@ size_t paged_attention_workspace_bytes(const pkv_pool* pool, const pkv_table* ta
  * codes convert to bf16 exactly) go through the matrix cores with float32
  * accumulation, probabilities rounded to bfloat16.
  * Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_BLOCK_RANGE (the table's
- * entries do not fit this pool), PKV_ERR_WORKSPACE, PKV_ERR_HIP.
+ * entries do not fit this pool), PKV_ERR_WORKSPACE, PKV_ERR_HIP (the table is
+ * then marked stale), PKV_ERR_TABLE_STALE (an earlier launch on this table
+ * failed: upload it again).
  */
 pkv_status paged_attention_decode(const pkv_pool* pool, int32_t layer, const pkv_table* table,
                                   const void* dev_q, int32_t q_dtype, int32_t num_q_heads,

@@ -28,7 +28,9 @@ BLOCK = 16
 
 
 def blocks_for(tokens):
-    """ceil(tokens / 16) (page 1: 50 tokens -> 4 blocks, 5000 -> 313)."""
+    """ceil(tokens / 16): whole 16-token blocks (page "KV cache & continuous
+    batching", section "Visual: the lifecycle of a request in continuous
+    batching", counts 4 blocks for 50 tokens and 313 for 5000)."""
     return -(-tokens // BLOCK)
 
 

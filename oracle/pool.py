@@ -34,7 +34,7 @@ so the oracle reads the pool from the definition, not from library code):
   V (token o = 4 g + t, dim i = 16 m + c):  N = (g * 16 + c) * W + t * (d // 16) + m.
 
 Pins: the layout formula is checked against hand-computed offsets stored in
-``tests/golden/pool_layout.txt``; the slot rule against the page-1 block-table
+``tests/golden/pool_layout.txt``; the slot rule against the block-table
 example (``tests/golden/page1_block_tables.txt``); the cache write and the
 gather against each other and against brute-force loops in the tests.
 """

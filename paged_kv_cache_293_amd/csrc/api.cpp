@@ -44,6 +44,10 @@ struct pkv_table {
     int32_t* d_unit_ids;
     std::vector<int32_t> staging;   // source of the asynchronous upload
     hipEvent_t uploaded;
+    // Set when an attention launch on this table returned an error: the
+    // launch may have left merge tickets or queue counters non-zero, so the
+    // table is refused until uploaded again.
+    bool stale = false;
 };
 
 namespace {
@@ -298,6 +302,7 @@ const char* pkv_status_string(pkv_status s) {
         case PKV_ERR_WORKSPACE: return "device buffer or workspace too small";
         case PKV_ERR_HIP: return "HIP runtime error";
         case PKV_ERR_OUT_OF_BLOCKS: return "not enough free blocks";
+        case PKV_ERR_TABLE_STALE: return "an earlier attention launch on this table failed; upload it again";
         default: return "unknown status";
     }
 }
@@ -543,6 +548,7 @@ pkv_status attention_call(const pkv_pool* pool, int32_t layer, const pkv_table* 
                           int32_t query_rows, int32_t num_q_heads, float scale, void* dev_workspace,
                           size_t workspace_bytes, void* dev_out, int32_t out_dtype, void* stream) {
     if (!pool || !table || !dev_q || !dev_out) return PKV_ERR_INVALID;
+    if (table->stale) return PKV_ERR_TABLE_STALE;
     if (layer < 0 || layer >= pool->desc.num_layers) return PKV_ERR_INVALID;
     if (query_rows < 1 || num_q_heads < 1) return PKV_ERR_INVALID;
     if (!std::isfinite(scale)) return PKV_ERR_INVALID;
@@ -605,8 +611,10 @@ pkv_status attention_call(const pkv_pool* pool, int32_t layer, const pkv_table* 
     a.fuse_max_parts = pkv::kFuseMaxParts;
     a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
     a.score_scale = scale * 1.4426950408889634f;
-    return hip_status(pkv::launch_attention(a, kv, pool->desc.head_dim, table->num_units,
-                                            static_cast<hipStream_t>(stream)));
+    const hipError_t err = pkv::launch_attention(a, kv, pool->desc.head_dim, table->num_units,
+                                                 static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) const_cast<pkv_table*>(table)->stale = true;
+    return hip_status(err);
 }
 
 }  // namespace

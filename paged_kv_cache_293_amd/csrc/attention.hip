@@ -6,9 +6,9 @@
 // oracles"): each query row of a sequence attends with softmax weights over the
 // K/V of the positions it may see, K and V being gathered through the
 // sequence's block table.  Query heads of one GQA group share the KV head
-// (page 1, section "KV cache memory math"); a verify call carries k query rows
-// per sequence with causal visibility among them (page 1, section
-// "5. Speculative decoding").
+// (page "KV cache & continuous batching", section "KV cache memory math"); a
+// verify call carries k query rows per sequence with causal visibility among
+// them (same page, section "5. Speculative decoding").
 //
 // Work decomposition.  An item is one (sequence, partition) unit for one KV
 // head.  One work-group of W = 4 wavefronts attends over an item: its waves

@@ -19,8 +19,10 @@
 //  3. S = sum of the segment totals (fixed order), T = u * S; the wave whose
 //     segment crosses T finds the crossing tile from its totals, re-reads that
 //     tile and scans it in index order: the emitted token is the first index
-//     whose running sum exceeds T (if rounding leaves T past the tile's own
-//     scan, its last weighted index).  A residual with no mass falls back to p_a.
+//     whose running sum exceeds T.  Where float32 rounding leaves T at or past
+//     the end of a scan (u close to 1), the last segment, tile or index with
+//     weight is taken, so a row with mass always yields a token; only a
+//     residual with no mass (S = 0) falls back to p_a.
 // The row is read once (plus one tile); the kernel is bound by HBM.
 #include "pkv_internal.h"
 
@@ -137,20 +139,30 @@ __global__ __launch_bounds__(kSpThreads) void speculative_accept_kernel(SpecArgs
         for (int w = 0; w < kSpWaves; ++w) S += seg_total[w];
         if (S > 0.f) {
             const float T = __fmul_rn(u, S);
-            // 3. the crossing segment, tile and index
-            float base = 0.f;
-            int cw = kSpWaves - 1;
+            // 3. the crossing segment, tile and index.  Partial sums are
+            // formed in the order S and the segment totals were (segment
+            // totals from 0 in segment order; tile totals from 0 in tile
+            // order), so a segment found crossing holds a crossing tile.
+            // Where rounding leaves T at or past the end (u close to 1),
+            // the fallback is the last segment, then tile, with weight.
+            float base = 0.f, base_last = 0.f;
+            int cw = -1, last_w = -1;
             for (int w = 0; w < kSpWaves; ++w) {
-                if (base + seg_total[w] > T) { cw = w; break; }
-                base += seg_total[w];
+                if (seg_total[w] > 0.f) { last_w = w; base_last = base; }
+                if (cw < 0 && base + seg_total[w] > T) cw = w;
+                if (cw < 0) base += seg_total[w];
             }
+            if (cw < 0) { cw = last_w; base = base_last; }
             if (wave == cw) {
-                int ct = tiles - 1;
-                float tb = base;
+                int ct = -1, last_t = -1;
+                float r = 0.f, r_ct = 0.f, r_last = 0.f;   // tile totals before t
                 for (int t = 0; t < tiles; ++t) {
-                    if (tb + my_tot[t] > T) { ct = t; break; }
-                    tb += my_tot[t];
+                    if (my_tot[t] > 0.f) { last_t = t; r_last = r; }
+                    if (ct < 0 && base + (r + my_tot[t]) > T) { ct = t; r_ct = r; }
+                    r += my_tot[t];
                 }
+                if (ct < 0) { ct = last_t; r_ct = r_last; }
+                const float tb = base + r_ct;
                 // scan the crossing tile in index order: its four 256-weight parts in turn
                 int pick = -1;
                 int last_pick = -1;

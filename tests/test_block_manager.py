@@ -61,8 +61,9 @@ def _check_content(m, content, live, width=512):
 
 
 def test_pages_block_counts(pk):
-    # page 1: a 50-token response uses 4 blocks, a 5000-token one 313; blocks
-    # come back in 16-token increments when the request finishes
+    # Page "KV cache & continuous batching", section "Visual: the lifecycle of
+    # a request in continuous batching": 4 blocks hold 50 tokens and 313 hold
+    # 5000, and finishing a request returns all of its blocks
     for n, want in [(int(a), int(b)) for a, b in golden_lines("block_counts.txt")]:
         m = pk.BlockManager(400)
         m.add(1, np.arange(n))

@@ -19,7 +19,7 @@ def _pk():
 
 
 def test_slot_mapping_page1_fixture():
-    log("slot mapping: page-1 block tables")
+    log("slot mapping: the worked block tables A and B")
     pk = _pk()
     tables, slots = {}, []
     for row in golden_lines("page1_block_tables.txt"):

@@ -115,3 +115,24 @@ def test_full_size_vocabulary():
     a, toks = _run(w)
     amb = _check(w, a, toks)
     log(f"  mean accepted {a.mean():.2f}; boundary-ambiguous draws {amb}")
+
+
+def test_draw_near_the_end_of_the_row():
+    """u just below 1 at Llama-3's vocabulary, with the rows' last 2,256
+    weights zero (the last wave's trailing tiles carry no weight): every draw
+    must still be a weighted token, the last one or within rounding of the
+    row's end, for a residual (rejection at position 0) and a bonus draw."""
+    log("speculative u near 1")
+    w = workloads.make_spec("sps", seed=31, batch=4, k=4, vocab=128256)
+    w.p[:, :, 126000:] = 0.0
+    w.q[:, :, 126000:] = 0.0
+    w.q[0] = w.p[0, :4]                       # identical: all accepted, the bonus row is drawn
+    w.draft[0] = np.argmax(w.p[0, :4], axis=1)
+    w.u_accept[0] = 0.5
+    w.u_accept[1, 0] = 0.999999               # position 0 rejects: a residual draw
+    w.draft[1, 0] = int(np.argmax(w.q[1, 0] - w.p[1, 0]))
+    w.u_sample[:] = np.float32(1.0) - np.float32(2.0 ** -24)
+    a, toks = _run(w)
+    _check(w, a, toks)
+    assert a[0] == 4 and a[1] == 0
+    assert (toks[np.arange(4), a] >= 0).all() and (toks[np.arange(4), a] < 126000).all()

@@ -104,8 +104,10 @@ def test_verify_rows_against_brute_force_and_sequential_decode():
 
 
 def test_cached_equals_uncached_causal_attention():
-    # A 7-token, width-4 toy in float64 as on page 2's hands-on: decoding with
-    # the cache at every prefix equals the last row of full causal attention.
+    # A 7-token, width-4 toy in float64 as on page "LLM Serving - KV Cache,
+    # Batching, Speculative Decoding" (section "Hands-on: cache equivalence
+    # and scheduling oracles"): decoding with the cache at every prefix equals
+    # the last row of full causal attention.
     rng = np.random.default_rng(124)
     x = rng.standard_normal((7, 4))
     Wq, Wk, Wv = (rng.standard_normal((4, 4)) for _ in range(3))
