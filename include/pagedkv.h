@@ -313,6 +313,27 @@ pkv_status paged_attention_verify(const pkv_pool* pool, int32_t layer, const pkv
                                   void* stream);
 
 /*
+ * paged_attention_verify without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The split-KV partial results go to a
+ * static device array of PKV_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on each GPU it runs on until the process ends (its address is looked
+ * up on the first call on that device; the call allocates nothing).  A table
+ * whose partials need more (paged_attention_workspace_bytes(...) >
+ * PKV_NOALLOC_SCRATCH_BYTES) is refused with PKV_ERR_WORKSPACE before
+ * anything is enqueued.  Every call on one GPU shares its array: calls that
+ * may overlap on one GPU (other streams, other host threads) race and must
+ * be serialised by the caller.  Nothing in the array needs clearing between
+ * calls: each call writes every partial it reads.  Arguments, results and
+ * other errors as paged_attention_verify (decode when query_rows = 1).
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pkv_status paged_attention_verify_noalloc(const pkv_pool* pool, int32_t layer, const pkv_table* table,
+                                          const void* dev_q, int32_t q_dtype, int32_t query_rows,
+                                          int32_t num_q_heads, float scale, void* dev_out,
+                                          int32_t out_dtype, void* stream);
+
+/*
  * One decode (or verify) step in one launch: append the K and V of every
  * sequence's k newest tokens to the pool, then attend.  Equivalent to
  * slot_mapping_compute for positions n-k .. n-1 of each sequence, then

@@ -7,6 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "lib", "libpagedkv.so")
 
 BLOCK_SIZE = 16
+NOALLOC_SCRATCH_BYTES = 64 << 20   # PKV_NOALLOC_SCRATCH_BYTES
 F32, BF16, FP8_E4M3, INT8, INT4 = 0, 1, 2, 3, 4
 
 _c_int32 = ctypes.c_int32
@@ -51,6 +52,8 @@ PROTOTYPES = {
                                           _vp, _c_size, _vp, _c_int32, _vp]),
     "paged_attention_verify": (_c_int32, [_vp, _c_int32, _vp, _vp, _c_int32, _c_int32, _c_int32,
                                           ctypes.c_float, _vp, _c_size, _vp, _c_int32, _vp]),
+    "paged_attention_verify_noalloc": (_c_int32, [_vp, _c_int32, _vp, _vp, _c_int32, _c_int32, _c_int32,
+                                                  ctypes.c_float, _vp, _c_int32, _vp]),
     "paged_attention_append": (_c_int32, [_vp, _c_int32, _vp, _vp, _vp, _c_int32, _vp, _c_int32, _c_int32,
                                           _c_int32, ctypes.c_float, _vp, _c_size, _vp, _c_int32, _vp]),
     "paged_attention_prefill": (_c_int32, [_vp, _c_int32, _vp, _vp, _c_int32, _c_int32, _c_int32, ctypes.c_float,

@@ -214,6 +214,25 @@ def paged_attention_verify(pool, layer, table, q, scale=None, workspace=None, ou
     return out
 
 
+def paged_attention_verify_noalloc(pool, layer, table, q, scale=None, out=None, out_dtype=None):
+    """paged_attention_verify with the partial results in the library's static
+    per-device scratch (no workspace): q [B][k][H_q][d] -> out [B][k][H_q][d]."""
+    assert q.dim() == 4 and q.shape[0] == table.num_seqs
+    k = q.shape[1]
+    assert q.is_cuda and q.is_contiguous() and q.dtype in _TORCH_CODE
+    Hq = q.shape[-2]
+    if out_dtype is None:
+        out_dtype = torch.float32 if pool.kv_dtype == F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    assert out.shape == q.shape and out.is_contiguous() and out.dtype in _TORCH_CODE
+    scale = 1.0 / math.sqrt(pool.head_dim) if scale is None else float(scale)
+    _check("paged_attention_verify_noalloc", lib.paged_attention_verify_noalloc(
+        pool.handle, int(layer), table.handle, _ptr(q), _TORCH_CODE[q.dtype], int(k), Hq, scale,
+        _ptr(out), _TORCH_CODE[out.dtype], _stream(q.device)))
+    return out
+
+
 def paged_attention_append(pool, layer, table, k_new, v_new, q, scale=None, workspace=None, out=None,
                            out_dtype=None):
     """Append then attend in one launch.

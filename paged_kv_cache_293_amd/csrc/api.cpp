@@ -629,6 +629,22 @@ pkv_status paged_attention_verify(const pkv_pool* pool, int32_t layer, const pkv
                           dev_workspace, workspace_bytes, dev_out, out_dtype, stream);
 }
 
+static_assert(PKV_NOALLOC_SCRATCH_BYTES == pkv::kNoAllocScratchBytes, "scratch size");
+
+pkv_status paged_attention_verify_noalloc(const pkv_pool* pool, int32_t layer, const pkv_table* table,
+                                          const void* dev_q, int32_t q_dtype, int32_t query_rows,
+                                          int32_t num_q_heads, float scale, void* dev_out, int32_t out_dtype,
+                                          void* stream) {
+    if (!pool || !table) return PKV_ERR_INVALID;
+    const size_t need = paged_attention_workspace_bytes(pool, table, num_q_heads, query_rows);
+    if (need > PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_WORKSPACE;
+    void* scratch = nullptr;
+    size_t scratch_bytes = 0;
+    if (pkv::attention_scratch(&scratch, &scratch_bytes) != hipSuccess) return PKV_ERR_HIP;
+    return attention_call(pool, layer, table, nullptr, nullptr, 0, dev_q, q_dtype, query_rows, num_q_heads, scale,
+                          scratch, scratch_bytes, dev_out, out_dtype, stream);
+}
+
 pkv_status paged_attention_append(const pkv_pool* pool, int32_t layer, const pkv_table* table,
                                   const void* dev_k_new, const void* dev_v_new, int32_t in_dtype,
                                   const void* dev_q, int32_t q_dtype, int32_t query_rows, int32_t num_q_heads,

@@ -42,10 +42,19 @@
 //         takes out of the scores (bias x the query row's sum) and of the
 //         output (bias x the probability sum); scales as fp8;
 //   f32 : v_mfma_f32_16x16x4_f32 for both products, probabilities in f32.
+#include <mutex>
+
 #include "pkv_mfma.h"
 
 namespace pkv {
 namespace {
+
+// Partial results (O, m, l) of split sequences for paged_attention_verify_noalloc,
+// which takes no workspace argument: one array per device, alive until the
+// process ends.  Host code must not pass this name to a kernel (on the host
+// it is only a stand-in for the symbol); it uses the device address that
+// attention_scratch() looks up per device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 constexpr int kWaves = 4;
 constexpr float kLazyMax = 8.f;   // exp2 units the running max may lag behind a row's scores
@@ -910,6 +919,27 @@ hipError_t launch_rows(const AttnArgs& a, int num_units, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t attention_scratch(void** ptr, size_t* bytes) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* address[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (address[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        address[dev] = p;
+    }
+    *ptr = address[dev];
+    *bytes = kNoAllocScratchBytes;
+    return hipSuccess;
+}
 
 hipError_t launch_attention(const AttnArgs& a, int kv_dtype, int head_dim, int num_units,
                             hipStream_t stream) {

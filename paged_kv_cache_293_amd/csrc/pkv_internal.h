@@ -109,6 +109,14 @@ struct AttnArgs {
     float score_scale;           // softmax scale * log2(e)
 };
 
+// Size of the per-device static scratch array that holds the split-KV
+// partial results of paged_attention_verify_noalloc.
+constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(64) << 20;
+
+// Device address of this device's scratch array (looked up once per device,
+// on the first call with that device current) and its size.
+hipError_t attention_scratch(void** ptr, size_t* bytes);
+
 // Launch the attention kernels (partition pass, then the split-KV merge when
 // some sequence is split).  kv_dtype / head_dim / rows select the instance.
 hipError_t launch_attention(const AttnArgs& a, int kv_dtype, int head_dim, int num_units,
