@@ -384,9 +384,17 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     // The next block's loads are issued unconditionally so the wait counts
     // stay static; past the last block they go through a zero-sized
     // resource (no memory traffic, zeros returned).
-    auto rsrc = [&](int i, bool valid) {
-        const int pid = __builtin_amdgcn_readlane(id, min(i, 63));
-        return tile_rsrc(head_base + static_cast<int64_t>(pid) * block_stride, valid ? a.tile_bytes : 0);
+    // Block i of the chunk: the tiles of a block several sequences share
+    // (flagged in its id) are read with the cached policy, the others
+    // streamed.  The flag is uniform over the wave, so the branch is too,
+    // and both arms issue the same loads.
+    auto issue = [&](TileRegs<KVT, D>& t, int i, bool valid) {
+        const int raw = __builtin_amdgcn_readlane(id, min(i, 63));
+        const int pid = raw & ~kSharedBlockFlag;
+        const __amdgpu_buffer_rsrc_t r =
+            tile_rsrc(head_base + static_cast<int64_t>(pid) * block_stride, valid ? a.tile_bytes : 0);
+        if (raw & kSharedBlockFlag) t.template load<kCachedLoad>(r, koff, voff);
+        else t.template load<kStreamLoad>(r, koff, voff);
     };
     TileRegs<KVT, D> ta, tb, tc;
     // First loads of a chunk: one block in flight, two with three buffers.
@@ -399,9 +407,9 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             id = 0;
             if (base + kWaves * lane < a.unit_stride) id = uids[base + kWaves * lane];
         }
-        id = min(max(id, 0), a.num_blocks - 1);
-        ta.load(rsrc(0, cnt > 0), koff, voff);
-        if constexpr (deep) tb.load(rsrc(1, cnt > 1), koff, voff);
+        id = (id & kSharedBlockFlag) | min(max(id & ~kSharedBlockFlag, 0), a.num_blocks - 1);
+        issue(ta, 0, cnt > 0);
+        if constexpr (deep) issue(tb, 1, cnt > 1);
     };
     // Fused append (paged_attention_append): the k newest positions n-k ..
     // n-1 of the sequence are written into the pool, for this KV head, by the
@@ -477,7 +485,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     {
         int j = appends ? blk_lo + min(tid, (hi - 1) / kBlock - blk_lo) - b0 - rot : 0;
         if (j < 0) j += nb;
-        pid_r = uids[j];
+        pid_r = uids[j] & ~kSharedBlockFlag;
     }
     if constexpr (kv_scaled<KVT>()) {
         k_sc = a.k_scale[a.layer * a.num_kv_heads + h];
@@ -503,11 +511,11 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             // are in flight.
             int i = 0;
             for (; i + 2 < cnt; i += 3) {
-                tc.load(rsrc(i + 2, true), koff, voff);
+                issue(tc, i + 2, true);
                 process(ta, logical(base + kWaves * i));
-                ta.load(rsrc(i + 3, i + 3 < cnt), koff, voff);
+                issue(ta, i + 3, i + 3 < cnt);
                 process(tb, logical(base + kWaves * (i + 1)));
-                tb.load(rsrc(i + 4, i + 4 < cnt), koff, voff);
+                issue(tb, i + 4, i + 4 < cnt);
                 process(tc, logical(base + kWaves * (i + 2)));
             }
             if (i < cnt) process(ta, logical(base + kWaves * i));
@@ -516,9 +524,9 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             // Two buffers: one block in flight while the other is processed.
             int i = 0;
             for (; i + 1 < cnt; i += 2) {
-                tb.load(rsrc(i + 1, true), koff, voff);
+                issue(tb, i + 1, true);
                 process(ta, logical(base + kWaves * i));
-                ta.load(rsrc(i + 2, i + 2 < cnt), koff, voff);
+                issue(ta, i + 2, i + 2 < cnt);
                 process(tb, logical(base + kWaves * (i + 1)));
             }
             if (i < cnt) process(ta, logical(base + kWaves * i));

@@ -21,6 +21,11 @@ constexpr int kUnitSlot = 6;     // partial-result slot (split sequences) or -1
 constexpr int kUnitRot = 7;      // walking-order rotation, seq mod nb
 constexpr int kUnitInts = 8;
 
+// Flag in a unit's block ids: the physical block is named by more than one
+// sequence of the batch (a shared prefix).  Its tiles are read with the
+// cached load policy; the others are streamed.  Block ids stay below 2^30.
+constexpr int32_t kSharedBlockFlag = 1 << 30;
+
 // Sequences with at most this many partitions are merged inside the
 // partition kernel; longer ones by the separate merge kernel.
 constexpr int kFuseMaxParts = 32;

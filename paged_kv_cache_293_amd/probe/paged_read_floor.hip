@@ -23,7 +23,9 @@
 // keeps one tile per wave in flight while one is consumed, and the 8 per CU
 // grid one tile per wave (load, consume).  Every tile index is checked
 // against the pool on the host.
-// Prints the median launch time over 30 launches, p10 and p90, and the rate.
+// Every configuration runs with the default cache policy of the loads and
+// with the non-temporal one the decode kernel uses.  Prints the median launch
+// time over 30 launches, p10 and p90, and the rate.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -41,14 +43,15 @@ constexpr int kCopies = 3;
 
 template <int S> struct Tile { u32x4 w[S / 1024]; };   // 1 KiB per wave load
 
-template <int S>
+// POL: the loads' cache-policy bits (0 default, 2 non-temporal).
+template <int S, int POL>
 __device__ __forceinline__ void load_tile(Tile<S>& t, const unsigned char* pool, long tile, bool valid, int lane) {
     // a zero-sized resource returns zeros without touching memory
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned char*>(pool + tile * S), 0, valid ? S : 0, 0x00020000);
 #pragma unroll
     for (int s = 0; s < S / 1024; ++s)
-        t.w[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 1024 * s, 0));
+        t.w[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 1024 * s, POL));
 }
 
 template <int S>
@@ -63,7 +66,7 @@ __device__ __forceinline__ unsigned fold(const Tile<S>& t) {
 // last runs may be shorter); wave w takes w, w + 4, ...  DEPTH 2: three tile
 // buffers (two tiles in flight while one is consumed); DEPTH 1: two buffers;
 // DEPTH 0: one buffer (load, consume, load).
-template <int S, int DEPTH>
+template <int S, int DEPTH, int POL>
 __global__ __launch_bounds__(256) void read_tiles(const unsigned char* pool, const int* list, int per, int total,
                                                   unsigned* out) {
     const int lane = threadIdx.x & 63;
@@ -75,34 +78,34 @@ __global__ __launch_bounds__(256) void read_tiles(const unsigned char* pool, con
     unsigned acc = 0;
     if constexpr (DEPTH == 2) {
         Tile<S> ta, tb, tc;
-        load_tile<S>(ta, pool, id(0), cnt > 0, lane);
-        load_tile<S>(tb, pool, id(1), cnt > 1, lane);
+        load_tile<S, POL>(ta, pool, id(0), cnt > 0, lane);
+        load_tile<S, POL>(tb, pool, id(1), cnt > 1, lane);
         int i = 0;
         for (; i + 2 < cnt; i += 3) {
-            load_tile<S>(tc, pool, id(i + 2), true, lane);
+            load_tile<S, POL>(tc, pool, id(i + 2), true, lane);
             acc += fold<S>(ta);
-            load_tile<S>(ta, pool, id(i + 3), i + 3 < cnt, lane);
+            load_tile<S, POL>(ta, pool, id(i + 3), i + 3 < cnt, lane);
             acc += fold<S>(tb);
-            load_tile<S>(tb, pool, id(i + 4), i + 4 < cnt, lane);
+            load_tile<S, POL>(tb, pool, id(i + 4), i + 4 < cnt, lane);
             acc += fold<S>(tc);
         }
         if (i < cnt) acc += fold<S>(ta);
         if (i + 1 < cnt) acc += fold<S>(tb);
     } else if constexpr (DEPTH == 1) {
         Tile<S> ta, tb;
-        load_tile<S>(ta, pool, id(0), cnt > 0, lane);
+        load_tile<S, POL>(ta, pool, id(0), cnt > 0, lane);
         int i = 0;
         for (; i + 1 < cnt; i += 2) {
-            load_tile<S>(tb, pool, id(i + 1), true, lane);
+            load_tile<S, POL>(tb, pool, id(i + 1), true, lane);
             acc += fold<S>(ta);
-            load_tile<S>(ta, pool, id(i + 2), i + 2 < cnt, lane);
+            load_tile<S, POL>(ta, pool, id(i + 2), i + 2 < cnt, lane);
             acc += fold<S>(tb);
         }
         if (i < cnt) acc += fold<S>(ta);
     } else {
         for (int i = 0; i < cnt; ++i) {
             Tile<S> t;
-            load_tile<S>(t, pool, id(i), true, lane);
+            load_tile<S, POL>(t, pool, id(i), true, lane);
             acc += fold<S>(t);
         }
     }
@@ -152,7 +155,7 @@ std::vector<int> tile_list(const Step& st, bool block_major) {
     return out;
 }
 
-template <int S>
+template <int S, int POL>
 void run(const Step& st, bool block_major, int wgs_per_cu, unsigned* d_out) {
     const long copy_bytes = static_cast<long>(st.num_blocks) * kHeads * S;
     unsigned char* buf;
@@ -171,13 +174,13 @@ void run(const Step& st, bool block_major, int wgs_per_cu, unsigned* d_out) {
     CK(hipMemcpy(d_list, list.data(), sizeof(int) * list.size(), hipMemcpyHostToDevice));
     auto launch = [&](int c) {
         if (wgs_per_cu >= 8)
-            hipLaunchKernelGGL((read_tiles<S, 0>), dim3(grid), dim3(256), 0, 0, buf + c * copy_bytes, d_list, per,
+            hipLaunchKernelGGL((read_tiles<S, 0, POL>), dim3(grid), dim3(256), 0, 0, buf + c * copy_bytes, d_list, per,
                                total, d_out);
         else if (wgs_per_cu >= 4)
-            hipLaunchKernelGGL((read_tiles<S, 1>), dim3(grid), dim3(256), 0, 0, buf + c * copy_bytes, d_list, per,
+            hipLaunchKernelGGL((read_tiles<S, 1, POL>), dim3(grid), dim3(256), 0, 0, buf + c * copy_bytes, d_list, per,
                                total, d_out);
         else
-            hipLaunchKernelGGL((read_tiles<S, 2>), dim3(grid), dim3(256), 0, 0, buf + c * copy_bytes, d_list, per,
+            hipLaunchKernelGGL((read_tiles<S, 2, POL>), dim3(grid), dim3(256), 0, 0, buf + c * copy_bytes, d_list, per,
                                total, d_out);
         CK(hipGetLastError());
     };
@@ -198,8 +201,8 @@ void run(const Step& st, bool block_major, int wgs_per_cu, unsigned* d_out) {
     }
     std::sort(ts.begin(), ts.end());
     const double gb = static_cast<double>(tiles) * S / 1e9;
-    printf("tile %5d B  order %-5s  %d WG/CU: %6.1f MB  median %6.1f us (%5.0f GB/s)  p10 %6.1f  p90 %6.1f us\n",
-           S, block_major ? "block" : "head", wgs_per_cu, gb * 1e3, ts[15] * 1e3, gb / (ts[15] * 1e-3),
+    printf("tile %5d B  order %-5s  %d WG/CU  policy %d: %6.1f MB  median %6.1f us (%5.0f GB/s)  p10 %6.1f  p90 %6.1f us\n",
+           S, block_major ? "block" : "head", wgs_per_cu, POL, gb * 1e3, ts[15] * 1e3, gb / (ts[15] * 1e-3),
            ts[3] * 1e3, ts[27] * 1e3);
     fflush(stdout);
     CK(hipEventDestroy(e0));
@@ -218,9 +221,15 @@ int main() {
     CK(hipMalloc(&d_out, sizeof(unsigned) * 256 * 8));
     for (int wpc : {2, 4, 8})
         for (int bm = 0; bm <= 1; ++bm) {
-            run<8192>(st, bm == 1, wpc, d_out);
-            run<4096>(st, bm == 1, wpc, d_out);
-            run<2048>(st, bm == 1, wpc, d_out);
+            run<8192, 0>(st, bm == 1, wpc, d_out);
+            run<4096, 0>(st, bm == 1, wpc, d_out);
+            run<2048, 0>(st, bm == 1, wpc, d_out);
+        }
+    for (int wpc : {2, 4, 8})
+        for (int bm = 0; bm <= 1; ++bm) {
+            run<8192, 2>(st, bm == 1, wpc, d_out);
+            run<4096, 2>(st, bm == 1, wpc, d_out);
+            run<2048, 2>(st, bm == 1, wpc, d_out);
         }
     CK(hipFree(d_out));
     return 0;

@@ -12,6 +12,8 @@
 // one's bytes in the 256 MB Infinity Cache.  Grids of 2 work-groups per CU
 // (three pieces per wave, two in flight while one is consumed) and 8 per CU
 // (one piece per wave at a time); a work-group is one wave on each SIMD.
+// The 2 per CU grid also runs with the loads' cache-policy bits set:
+// non-temporal (2), sc0 (1), sc0 + non-temporal (3), sc0 + sc1 (17).
 // Every piece index is checked against the region on the host.  Prints the
 // median launch time over 30 launches and the rate.
 #include <hip/hip_runtime.h>
@@ -32,12 +34,15 @@ constexpr int kPieces = static_cast<int>(kRegionBytes / kPiece);
 
 struct Piece { u32x4 w[kPiece / 1024]; };
 
+// POL: the load's cache-policy bits (0 default; 2 non-temporal; 1, 3, 17, 19
+// with the coherence bits sc0 (1) and sc1 (16)).
+template <int POL>
 __device__ __forceinline__ void load_piece(Piece& t, const unsigned char* region, int piece, bool valid, int lane) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned char*>(region + static_cast<long>(piece) * kPiece), 0, valid ? kPiece : 0, 0x00020000);
 #pragma unroll
     for (int s = 0; s < kPiece / 1024; ++s)
-        t.w[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 1024 * s, 0));
+        t.w[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, 1024 * s, POL));
 }
 
 __device__ __forceinline__ unsigned fold(const Piece& t) {
@@ -48,7 +53,7 @@ __device__ __forceinline__ unsigned fold(const Piece& t) {
 }
 
 // Wave g reads list[g], list[g + W], ...  (cnt of them).
-template <int DEPTH>
+template <int DEPTH, int POL>
 __global__ __launch_bounds__(256) void read_region(const unsigned char* region, const int* list, int n, unsigned* out) {
     const int lane = threadIdx.x & 63;
     const int W = static_cast<int>(gridDim.x) * 4;
@@ -58,15 +63,15 @@ __global__ __launch_bounds__(256) void read_region(const unsigned char* region, 
     unsigned acc = 0;
     if constexpr (DEPTH == 2) {
         Piece ta, tb, tc;
-        load_piece(ta, region, id(0), cnt > 0, lane);
-        load_piece(tb, region, id(1), cnt > 1, lane);
+        load_piece<POL>(ta, region, id(0), cnt > 0, lane);
+        load_piece<POL>(tb, region, id(1), cnt > 1, lane);
         int i = 0;
         for (; i + 2 < cnt; i += 3) {
-            load_piece(tc, region, id(i + 2), true, lane);
+            load_piece<POL>(tc, region, id(i + 2), true, lane);
             acc += fold(ta);
-            load_piece(ta, region, id(i + 3), i + 3 < cnt, lane);
+            load_piece<POL>(ta, region, id(i + 3), i + 3 < cnt, lane);
             acc += fold(tb);
-            load_piece(tb, region, id(i + 4), i + 4 < cnt, lane);
+            load_piece<POL>(tb, region, id(i + 4), i + 4 < cnt, lane);
             acc += fold(tc);
         }
         if (i < cnt) acc += fold(ta);
@@ -74,7 +79,7 @@ __global__ __launch_bounds__(256) void read_region(const unsigned char* region, 
     } else {
         for (int i = 0; i < cnt; ++i) {
             Piece t;
-            load_piece(t, region, id(i), true, lane);
+            load_piece<POL>(t, region, id(i), true, lane);
             acc += fold(t);
         }
     }
@@ -91,6 +96,7 @@ int main() {
     CK(hipMalloc(&d_list, sizeof(int) * kPieces));
     std::mt19937_64 rng(293);
     const char* names[3] = {"stream", "random8", "random64"};
+    for (int pol : {0, 2, 1, 3, 17}) {
     for (int mode = 0; mode < 3; ++mode) {
         std::vector<int> list(kPieces);
         if (mode == 0) {
@@ -111,11 +117,16 @@ int main() {
         }
         CK(hipMemcpy(d_list, list.data(), sizeof(int) * kPieces, hipMemcpyHostToDevice));
         for (int wpc : {2, 8}) {
+            if (pol != 0 && wpc != 2) continue;
             const int grid = 256 * wpc;
             auto launch = [&](int r) {
                 const unsigned char* region = buf + r * kRegionBytes;
-                if (wpc == 2) hipLaunchKernelGGL(read_region<2>, dim3(grid), dim3(256), 0, 0, region, d_list, kPieces, d_out);
-                else hipLaunchKernelGGL(read_region<0>, dim3(grid), dim3(256), 0, 0, region, d_list, kPieces, d_out);
+                if (wpc == 8) hipLaunchKernelGGL((read_region<0, 0>), dim3(grid), dim3(256), 0, 0, region, d_list, kPieces, d_out);
+                else if (pol == 0) hipLaunchKernelGGL((read_region<2, 0>), dim3(grid), dim3(256), 0, 0, region, d_list, kPieces, d_out);
+                else if (pol == 2) hipLaunchKernelGGL((read_region<2, 2>), dim3(grid), dim3(256), 0, 0, region, d_list, kPieces, d_out);
+                else if (pol == 1) hipLaunchKernelGGL((read_region<2, 1>), dim3(grid), dim3(256), 0, 0, region, d_list, kPieces, d_out);
+                else if (pol == 3) hipLaunchKernelGGL((read_region<2, 3>), dim3(grid), dim3(256), 0, 0, region, d_list, kPieces, d_out);
+                else hipLaunchKernelGGL((read_region<2, 17>), dim3(grid), dim3(256), 0, 0, region, d_list, kPieces, d_out);
                 CK(hipGetLastError());
             };
             for (int w = 0; w < 6; ++w) launch(w % kRegions);
@@ -135,12 +146,13 @@ int main() {
             }
             std::sort(ts.begin(), ts.end());
             const double gb = static_cast<double>(kRegionBytes) / 1e9;
-            printf("%-8s %d WG/CU: %.1f MB per launch, median %7.1f us (%5.0f GB/s), p10 %7.1f  p90 %7.1f us\n",
-                   names[mode], wpc, gb * 1e3, ts[15] * 1e3, gb / (ts[15] * 1e-3), ts[3] * 1e3, ts[27] * 1e3);
+            printf("%-8s %d WG/CU policy %2d: %.1f MB per launch, median %7.1f us (%5.0f GB/s), p10 %7.1f  p90 %7.1f us\n",
+                   names[mode], wpc, pol, gb * 1e3, ts[15] * 1e3, gb / (ts[15] * 1e-3), ts[3] * 1e3, ts[27] * 1e3);
             fflush(stdout);
             CK(hipEventDestroy(e0));
             CK(hipEventDestroy(e1));
         }
+    }
     }
     CK(hipFree(buf));
     CK(hipFree(d_out));
