@@ -389,6 +389,31 @@ pkv_status paged_attention_prefill(const pkv_pool* pool, int32_t layer, const pk
                                    void* stream);
 
 /*
+ * Chunked-prefill attention with a chunk length per sequence (page "KV cache
+ * & continuous batching", section "3. Chunked prefill": prompts of any length
+ * are cut into chunks, so one batch carries a full chunk of one prompt and the
+ * shorter last chunk of another).  Sequence s carries C_s =
+ * host_query_start[s + 1] - host_query_start[s] query tokens (0 allowed) at
+ * positions n-C_s .. n-1 of its sequence, their K/V appended beforehand; row
+ * j attends causally to positions t <= n - C_s + j, as
+ * paged_attention_prefill computes for a uniform C.
+ *   dev_q, dev_out  [host_query_start[num_seqs]][num_q_heads][head_dim]: the
+ *            chunks' rows packed in sequence order (sequence s from row
+ *            host_query_start[s]).
+ *   host_query_start  int32 [num_seqs + 1] host array, read during the call:
+ *            0 = qs[0] <= qs[1] <= ... and qs[s + 1] - qs[s] <= seq_len[s].
+ *   dev_query_start   the same values in a device array, read by the kernel
+ *            (the caller keeps the two equal).
+ * Other arguments, pools and errors as paged_attention_prefill; PKV_ERR_INVALID
+ * for a decreasing or non-zero-based host_query_start, PKV_ERR_SEQ_LEN for a
+ * chunk longer than its sequence.  A batch with no chunk token enqueues nothing.
+ */
+pkv_status paged_attention_prefill_varlen(const pkv_pool* pool, int32_t layer, const pkv_table* table,
+                                          const void* dev_q, int32_t q_dtype, const int32_t* host_query_start,
+                                          const int32_t* dev_query_start, int32_t num_q_heads, float scale,
+                                          void* dev_out, int32_t out_dtype, void* stream);
+
+/*
  * Exact speculative acceptance (page "LLM Serving - KV Cache, Batching,
  * Speculative Decoding", section "Speculative decoding: distribution and
  * break-even"; page "KV cache & continuous batching", section "5. Speculative

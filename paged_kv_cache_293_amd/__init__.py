@@ -12,7 +12,7 @@ from ._lib import (  # noqa: F401
 )
 from .api import (  # noqa: F401
     BlockManager, BlockTable, KVPool, block_table_upload, kv_bytes_per_token, kv_copy_blocks, kv_pool_bytes,
-    kv_pool_create, paged_attention_append, paged_attention_decode, paged_attention_prefill,
+    kv_pool_create, paged_attention_append, paged_attention_decode, paged_attention_prefill, paged_attention_prefill_varlen,
     paged_attention_verify, paged_attention_verify_noalloc,
     paged_attention_workspace_bytes, reshape_and_cache, slot_mapping_compute, speculative_accept,
 )

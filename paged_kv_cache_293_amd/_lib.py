@@ -58,6 +58,8 @@ PROTOTYPES = {
                                           _c_int32, ctypes.c_float, _vp, _c_size, _vp, _c_int32, _vp]),
     "paged_attention_prefill": (_c_int32, [_vp, _c_int32, _vp, _vp, _c_int32, _c_int32, _c_int32, ctypes.c_float,
                                            _vp, _c_int32, _vp]),
+    "paged_attention_prefill_varlen": (_c_int32, [_vp, _c_int32, _vp, _vp, _c_int32, _vp, _vp, _c_int32,
+                                                  ctypes.c_float, _vp, _c_int32, _vp]),
     "speculative_accept": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _vp, _vp, _vp]),
     "kv_copy_blocks": (_c_int32, [_vp, _vp, _c_int32, _vp]),
     "block_manager_create": (_c_int32, [_c_int32, ctypes.POINTER(_vp)]),

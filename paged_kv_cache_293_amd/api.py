@@ -277,6 +277,28 @@ def paged_attention_prefill(pool, layer, table, q, scale=None, out=None, out_dty
     return out
 
 
+def paged_attention_prefill_varlen(pool, layer, table, q, query_start, scale=None, out=None, out_dtype=None):
+    """Chunked prefill with a chunk per sequence: q [T][H_q][d] bfloat16, the
+    chunks' rows packed in sequence order, query_start the B + 1 row offsets
+    (host ints; copied to the device here) -> out [T][H_q][d]."""
+    qs = np.ascontiguousarray(np.asarray(query_start, dtype=np.int32))
+    assert qs.ndim == 1 and qs.shape[0] == table.num_seqs + 1
+    assert q.dim() == 3 and q.is_cuda and q.is_contiguous() and q.dtype == torch.bfloat16
+    assert q.shape[0] == int(qs[-1])
+    Hq = q.shape[1]
+    if out_dtype is None:
+        out_dtype = torch.bfloat16
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    assert out.shape == q.shape and out.is_contiguous() and out.dtype in _TORCH_CODE
+    dev_qs = torch.from_numpy(qs).to(q.device)
+    scale = 1.0 / math.sqrt(pool.head_dim) if scale is None else float(scale)
+    _check("paged_attention_prefill_varlen", lib.paged_attention_prefill_varlen(
+        pool.handle, int(layer), table.handle, _ptr(q), BF16, qs.ctypes.data_as(ctypes.c_void_p), _ptr(dev_qs),
+        Hq, scale, _ptr(out), _TORCH_CODE[out.dtype], _stream(q.device)))
+    return out
+
+
 def speculative_accept(p, q, draft, u_accept, u_sample, num_accepted=None, tokens=None):
     """Exact speculative acceptance: p [B][K+1][V], q [B][K][V] float32,
     draft [B][K] int32, u_accept [B][K], u_sample [B] float32 uniforms in

@@ -42,7 +42,8 @@ struct pkv_table {
     int32_t* d_queue;
     int32_t* d_units;
     int32_t* d_unit_ids;
-    std::vector<int32_t> staging;   // source of the asynchronous upload
+    std::vector<int32_t> staging;   // source of the asynchronous upload (host image of the buffer)
+    size_t seq_lens_offset = 0;     // byte offset of the lengths in that image
     hipEvent_t uploaded;
     // Set when an attention launch on this table returned an error: the
     // launch may have left merge tickets or queue counters non-zero, so the
@@ -421,6 +422,7 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
         t->d_queue = reinterpret_cast<int32_t*>(base + L.queue);
         t->d_units = reinterpret_cast<int32_t*>(base + L.units);
         t->d_unit_ids = reinterpret_cast<int32_t*>(base + L.unit_ids);
+        t->seq_lens_offset = L.seq_lens;
 
         // One host image of the whole buffer (counters start at zero), copied once.
         t->staging.assign(L.total / sizeof(int32_t), 0);
@@ -627,6 +629,72 @@ pkv_status attention_call(const pkv_pool* pool, int32_t layer, const pkv_table* 
     return hip_status(err);
 }
 
+// Chunked-prefill attention: every sequence's chunk is chunk_tokens long
+// (host_query_start NULL) or host_query_start[s + 1] - host_query_start[s]
+// long, its rows packed from host_query_start[s] (the device copy is what the
+// kernel reads).
+pkv_status prefill_call(const pkv_pool* pool, int32_t layer, const pkv_table* table, const void* dev_q,
+                        int32_t q_dtype, int32_t chunk_tokens, const int32_t* host_query_start,
+                        const int32_t* dev_query_start, int32_t num_q_heads, float scale, void* dev_out,
+                        int32_t out_dtype, void* stream) {
+    if (!pool || !table) return PKV_ERR_INVALID;
+    if (layer < 0 || layer >= pool->desc.num_layers) return PKV_ERR_INVALID;
+    if (num_q_heads < 1 || !std::isfinite(scale)) return PKV_ERR_INVALID;
+    const int32_t hkv = pool->desc.num_kv_heads;
+    if (num_q_heads % hkv || table->num_kv_heads != hkv) return PKV_ERR_INVALID;
+    const int32_t kv = pool->desc.kv_dtype;
+    if (kv == PKV_F32) return PKV_ERR_UNSUPPORTED;
+    if (q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (table->max_block_id >= pool->desc.num_blocks) return PKV_ERR_BLOCK_RANGE;
+    const int32_t group = num_q_heads / hkv;
+    int64_t longest = chunk_tokens;
+    if (host_query_start) {
+        // chunks: non-negative lengths, each within its sequence, rows packed in order
+        if (host_query_start[0] != 0) return PKV_ERR_INVALID;
+        const int32_t* lens = table->staging.data() + table->seq_lens_offset / 4;
+        longest = 0;
+        for (int32_t s = 0; s < table->num_seqs; ++s) {
+            const int64_t c = static_cast<int64_t>(host_query_start[s + 1]) - host_query_start[s];
+            if (c < 0) return PKV_ERR_INVALID;
+            if (c > lens[s]) return PKV_ERR_SEQ_LEN;
+            longest = std::max(longest, c);
+        }
+        if (static_cast<int64_t>(host_query_start[table->num_seqs]) * num_q_heads > INT32_MAX)
+            return PKV_ERR_UNSUPPORTED;
+    } else {
+        if (table->min_seq_len < chunk_tokens) return PKV_ERR_SEQ_LEN;
+        if (static_cast<int64_t>(chunk_tokens) * table->num_seqs * num_q_heads > INT32_MAX) return PKV_ERR_UNSUPPORTED;
+    }
+    const int64_t tiles = (longest * group + pkv::kPrefillRows - 1) / pkv::kPrefillRows;
+    if (tiles == 0) return PKV_OK;   // no chunk token in the batch (q and out may be NULL)
+    if (!dev_q || !dev_out) return PKV_ERR_INVALID;
+    if (tiles * table->num_seqs * hkv > INT32_MAX) return PKV_ERR_UNSUPPORTED;
+    pkv::PrefillArgs a;
+    a.pool = pool->base;
+    a.k_scale = pool->k_scale;
+    a.v_scale = pool->v_scale;
+    a.table = table->d_table;
+    a.seq_lens = table->d_seq_lens;
+    a.q = dev_q;
+    a.out = dev_out;
+    a.query_start = dev_query_start;
+    a.tile_bytes = pool->tile_bytes;
+    a.layer = layer;
+    a.num_blocks = pool->desc.num_blocks;
+    a.num_seqs = table->num_seqs;
+    a.num_kv_heads = hkv;
+    a.num_q_heads = num_q_heads;
+    a.group = group;
+    a.chunk = chunk_tokens;
+    a.max_blocks = table->max_blocks;
+    a.row_tiles = static_cast<int32_t>(tiles);
+    a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
+    a.score_scale = scale * 1.4426950408889634f;
+    const int32_t kvt = kv;   // PKV_* element codes equal the kernels' KV_* codes
+    return hip_status(pkv::launch_prefill(a, kvt, pool->desc.head_dim, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -668,42 +736,19 @@ pkv_status paged_attention_append(const pkv_pool* pool, int32_t layer, const pkv
 pkv_status paged_attention_prefill(const pkv_pool* pool, int32_t layer, const pkv_table* table, const void* dev_q,
                                    int32_t q_dtype, int32_t chunk_tokens, int32_t num_q_heads, float scale,
                                    void* dev_out, int32_t out_dtype, void* stream) {
-    if (!pool || !table || !dev_q || !dev_out) return PKV_ERR_INVALID;
-    if (layer < 0 || layer >= pool->desc.num_layers) return PKV_ERR_INVALID;
-    if (chunk_tokens < 1 || num_q_heads < 1 || !std::isfinite(scale)) return PKV_ERR_INVALID;
-    const int32_t hkv = pool->desc.num_kv_heads;
-    if (num_q_heads % hkv || table->num_kv_heads != hkv) return PKV_ERR_INVALID;
-    const int32_t kv = pool->desc.kv_dtype;
-    if (kv != PKV_BF16 && kv != PKV_FP8_E4M3 && kv != PKV_INT8) return PKV_ERR_UNSUPPORTED;
-    if (q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
-    if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
-    if (table->min_seq_len < chunk_tokens) return PKV_ERR_SEQ_LEN;
-    if (table->max_block_id >= pool->desc.num_blocks) return PKV_ERR_BLOCK_RANGE;
-    const int64_t rows = static_cast<int64_t>(chunk_tokens) * (num_q_heads / hkv);
-    const int64_t tiles = (rows + pkv::kPrefillRows - 1) / pkv::kPrefillRows;
-    if (tiles * table->num_seqs * hkv > INT32_MAX) return PKV_ERR_UNSUPPORTED;
-    pkv::PrefillArgs a;
-    a.pool = pool->base;
-    a.k_scale = pool->k_scale;
-    a.v_scale = pool->v_scale;
-    a.table = table->d_table;
-    a.seq_lens = table->d_seq_lens;
-    a.q = dev_q;
-    a.out = dev_out;
-    a.tile_bytes = pool->tile_bytes;
-    a.layer = layer;
-    a.num_blocks = pool->desc.num_blocks;
-    a.num_seqs = table->num_seqs;
-    a.num_kv_heads = hkv;
-    a.num_q_heads = num_q_heads;
-    a.group = num_q_heads / hkv;
-    a.chunk = chunk_tokens;
-    a.max_blocks = table->max_blocks;
-    a.row_tiles = static_cast<int32_t>(tiles);
-    a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
-    a.score_scale = scale * 1.4426950408889634f;
-    const int32_t kvt = kv;   // PKV_* element codes equal the kernels' KV_* codes
-    return hip_status(pkv::launch_prefill(a, kvt, pool->desc.head_dim, static_cast<hipStream_t>(stream)));
+    if (!table) return PKV_ERR_INVALID;
+    if (chunk_tokens < 1) return PKV_ERR_INVALID;
+    return prefill_call(pool, layer, table, dev_q, q_dtype, chunk_tokens, nullptr, nullptr, num_q_heads, scale,
+                        dev_out, out_dtype, stream);
+}
+
+pkv_status paged_attention_prefill_varlen(const pkv_pool* pool, int32_t layer, const pkv_table* table,
+                                          const void* dev_q, int32_t q_dtype, const int32_t* host_query_start,
+                                          const int32_t* dev_query_start, int32_t num_q_heads, float scale,
+                                          void* dev_out, int32_t out_dtype, void* stream) {
+    if (!table || !host_query_start || !dev_query_start) return PKV_ERR_INVALID;
+    return prefill_call(pool, layer, table, dev_q, q_dtype, 0, host_query_start, dev_query_start, num_q_heads, scale,
+                        dev_out, out_dtype, stream);
 }
 
 pkv_status kv_copy_blocks(const pkv_pool* pool, const int32_t* dev_pairs, int32_t num_pairs, void* stream) {

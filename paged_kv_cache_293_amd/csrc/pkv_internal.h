@@ -139,8 +139,9 @@ struct PrefillArgs {
     const float* v_scale;
     const int32_t* table;        // [B][max_blocks] block table (validated at upload)
     const int32_t* seq_lens;     // [B]
-    const void* q;               // [B][chunk][H_q][D] bfloat16
-    void* out;                   // [B][chunk][H_q][D]
+    const void* q;               // [total chunk tokens][H_q][D] bfloat16, sequences in order
+    void* out;                   // [total chunk tokens][H_q][D]
+    const int32_t* query_start;  // [B + 1] first packed row of each sequence's chunk, or null: s * chunk
     int64_t tile_bytes;
     int32_t layer;
     int32_t num_blocks;
@@ -148,9 +149,9 @@ struct PrefillArgs {
     int32_t num_kv_heads;
     int32_t num_q_heads;
     int32_t group;               // G = H_q / H_kv
-    int32_t chunk;               // query tokens per sequence
+    int32_t chunk;               // query tokens per sequence (without query_start)
     int32_t max_blocks;          // table row stride
-    int32_t row_tiles;           // ceil(chunk * G / kPrefillRows)
+    int32_t row_tiles;           // ceil(longest chunk * G / kPrefillRows)
     int32_t out_bf16;
     float score_scale;           // softmax scale * log2(e)
 };

@@ -21,7 +21,8 @@
 // the visible blocks stream through a three-stage LDS ring, two blocks (a
 // "pair") per stage, copied straight from the pool into LDS by
 // global_load_lds_dwordx4 (no register staging); each wave issues its share
-// of the pair two steps ahead, and one barrier per pair publishes it.
+// of the pair two steps ahead, and one barrier per pair publishes it.  The
+// block ids are read with scalar loads, a pair ahead of their use.
 //
 // Matrix cores.  Scores: S^T[token][row] = K[token][:] . Q^T[:][row] with
 // v_mfma_f32_16x16x32_bf16 per block (K is the A operand, one 16-byte LDS
@@ -31,13 +32,19 @@
 // each block of the pair (its 4 + 4 probabilities straight from the two score
 // tiles, and the matching 8-byte V^T reads), so the contraction runs at the
 // full-rate 32-deep instruction.  fp8 codes are converted to bf16 exactly
-// after the LDS read, and so are int8 codes; the K scale folds into the score
-// scale, the V scale into the final divide.
+// after the LDS read, and so are int8 codes; int4 codes are widened to bf16
+// biased by kI4Bias (as in the decode kernel: each lane reads its own run of
+// a tile), the bias taken out of the scores (kI4Bias times the query row's
+// sum) and of the output (kI4Bias times the row's probability sum).  The K
+// scale folds into the score scale, the V scale into the final divide.
 //
 // Work-group order: groups of 8 (sequence, KV head) pairs x all row tiles,
 // the pair fastest; work-groups go to the 8 XCDs round-robin, so each XCD
 // serves one pair's row tiles and its L2 holds that pair's K/V for all of
-// them.  Row tiles go longest (most visible tokens) first.
+// them.  Row tiles go longest (most visible tokens) first.  Sequences may
+// carry chunks of different lengths (query_start): the grid holds the
+// longest chunk's row tiles for every sequence, and a work-group whose tile
+// lies past its own sequence's chunk returns at once.
 #include "pkv_mfma.h"
 
 namespace pkv {
@@ -51,38 +58,59 @@ constexpr int kPfNT = kPrefillRows / (16 * kPfWaves);   // column tiles per wave
 constexpr int kPfStages = PKV_PREFILL_STAGES;           // LDS ring of block pairs
 constexpr int kPfAhead = kPfStages - 1;                 // pairs in flight ahead of the one computed
 static_assert(kPfAhead >= 1 && kPfAhead <= 3, "the wait counts cover up to 3 pairs in flight");
-constexpr int kPfIdWindow = 2048;                       // block ids held in LDS at a time
 constexpr int kPfXcds = 8;
 constexpr float kLazyMax = 8.f;                         // exp2 units the running max may lag
 
 template <int KVT, int D> struct PfGeom {
-    static constexpr int EB = KVT == KV_BF16 ? 2 : 1;
-    static constexpr int TILE = 16 * D * EB;               // one K or V tile
+    static constexpr int EB = KVT == KV_BF16 ? 2 : 1;      // bytes per element (int4: 2 codes per byte)
+    static constexpr int TILE = KVT == KV_INT4 ? 8 * D : 16 * D * EB;   // one K or V tile
     static constexpr int PAIR = 4 * TILE;                  // K_A, V_A, K_B, V_B
-    static constexpr int LOADS = PAIR / 1024 / kPfWaves;   // 1 KiB wave loads per wave per pair
-    static_assert(LOADS >= 1, "a pair must give every wave at least one load");
-    static constexpr int LDS = kPfStages * PAIR + 4 * kPfIdWindow;
+    static constexpr int PIECES = PAIR / 1024;             // 1 KiB wave loads per pair
+    // wave loads per wave per pair (int4 at head dim 64: waves 2 and 3 load nothing)
+    static constexpr int LOADS = (PIECES + kPfWaves - 1) / kPfWaves;
+    static_assert(PIECES >= 1 && (TILE % 1024 == 0 || TILE == 512), "whole 1 KiB pieces per tile pair");
+    static constexpr int LDS = kPfStages * PAIR;
 };
 
 // s_waitcnt immediate: vector-memory count <= N, no wait on the other counters.
 template <int N> constexpr int vmcnt_imm() { return (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14); }
 
+// LDS placement of the bf16 V^T tiles.  A V^T row (one dim, 16 tokens) is
+// 32 bytes, two 16-byte halves of 8 tokens; the PV operand read of a lane is
+// 8 bytes of row 16m + col, and the 32 lanes of one LDS cycle take rows
+// col = 0 .. 15, which 64 four-byte banks would map with rows col and col + 8
+// on the same banks.  Rows whose dim has bit 3 set therefore hold their two
+// halves swapped: row r's half h sits at half h ^ ((r >> 3) & 1).  As chunk
+// index (2r + h) in the tile, the 16-byte chunk stored at LDS chunk c is the
+// pool's chunk c ^ ((c >> 4) & 1).  One-byte codes (16-byte rows, 4-byte
+// reads) are read without conflicts as stored.
+template <int KVT>
+__device__ __forceinline__ int pf_v_chunk(int c) {
+    if constexpr (KVT == KV_BF16) return c ^ ((c >> 4) & 1);
+    else return c;
+}
+
 // Copy one pair (blocks id_a, id_b) of this KV head into an LDS stage: this
-// wave's share of the 1 KiB pieces, 16 bytes per lane, straight into LDS.
+// wave's share of the 1 KiB pieces, 16 bytes per lane, straight into LDS (the
+// lane's 16 bytes land at LDS offset lane * 16 of the piece; V tiles take
+// their chunks in the order pf_v_chunk gives).
 template <int KVT, int D>
 __device__ __forceinline__ void pf_issue(const uint8_t* head_base, int64_t block_stride, int id_a, int id_b,
                                          uint8_t* stage, int wave, int lane) {
     using Gm = PfGeom<KVT, D>;
-    constexpr int PER_TILE = Gm::TILE / 1024;
 #pragma unroll
     for (int k = 0; k < Gm::LOADS; ++k) {
-        const int gk = wave + kPfWaves * k;
-        const int tile = gk / PER_TILE;                 // 0 K_A, 1 V_A, 2 K_B, 3 V_B
-        const int off = (gk % PER_TILE) * 1024;
+        const int gk = wave + kPfWaves * k;             // 1 KiB piece of the pair's 4 tiles
+        if (Gm::PIECES % kPfWaves != 0 && gk >= Gm::PIECES) break;
+        const int at = gk * 1024;                       // byte of the pair in LDS
+        // this lane's 16 bytes: chunk c of tile 0 K_A, 1 V_A, 2 K_B, 3 V_B (a
+        // piece spans two tiles only when tiles are 512 bytes: int4, head dim 64)
+        const int tile = (at + lane * 16) / Gm::TILE;
+        const int c = (at + lane * 16 - tile * Gm::TILE) / 16;
+        const int chunk = (tile & 1) ? pf_v_chunk<KVT>(c) : c;
         const int id = tile < 2 ? id_a : id_b;
-        const uint8_t* src = head_base + static_cast<int64_t>(id) * block_stride + (tile & 1) * Gm::TILE + off +
-                             lane * 16;
-        __builtin_amdgcn_global_load_lds(src, stage + tile * Gm::TILE + off, 16, 0, 0);
+        const uint8_t* src = head_base + static_cast<int64_t>(id) * block_stride + (tile & 1) * Gm::TILE + chunk * 16;
+        __builtin_amdgcn_global_load_lds(src, stage + at, 16, 0, 0);
     }
 }
 
@@ -90,7 +118,18 @@ __device__ __forceinline__ void pf_issue(const uint8_t* head_base, int64_t block
 // the decode kernel's buffer loads: token lane % 16, 16-byte chunk).
 template <int KVT, int D>
 __device__ __forceinline__ void pf_k_regs(TileRegs<KVT, D>& t, const uint8_t* tile, int lane) {
-    if constexpr (KVT == KV_BF16) {
+    if constexpr (KVT == KV_INT4) {
+        // the lane's run of D / 4 nibbles (layout in the library header)
+        if constexpr (D == 128) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(tile + lane * 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t.k[j] = w[j];
+        } else {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(tile + lane * 8);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) t.k[j] = w[j];
+        }
+    } else if constexpr (KVT == KV_BF16) {
 #pragma unroll
         for (int s = 0; s < D / 32; ++s) t.k[s] = *reinterpret_cast<const u32x4*>(tile + lane * 16 + 1024 * s);
     } else {
@@ -104,7 +143,8 @@ __device__ __forceinline__ void pf_k_regs(TileRegs<KVT, D>& t, const uint8_t* ti
 template <int KVT, int D>
 __device__ __forceinline__ u32x4 pf_v_op(const uint8_t* va, const uint8_t* vb, int m, int col, int lg) {
     if constexpr (KVT == KV_BF16) {
-        const int off = (16 * m + col) * 32 + lg * 8;
+        // tokens 4lg .. +3: half lg >> 1 (swapped in rows with dim bit 3), 8 bytes in
+        const int off = (16 * m + col) * 32 + (((lg >> 1) ^ ((col >> 3) & 1)) << 4) + (lg & 1) * 8;
         const u32x2 x = *reinterpret_cast<const u32x2*>(va + off);
         const u32x2 y = *reinterpret_cast<const u32x2*>(vb + off);
         return u32x4{x[0], x[1], y[0], y[1]};
@@ -116,6 +156,36 @@ __device__ __forceinline__ u32x4 pf_v_op(const uint8_t* va, const uint8_t* vb, i
                      byte2_to_bf16x2<KVT, true>(y)};
     }
 }
+
+// int4 V^T operand over a pair.  Lane (col, lg)'s run of a V tile holds
+// tokens 4lg .. 4lg+3 of dims 16m + col, m = 0 .. D/16 - 1 (layout in the
+// library header); its codes, biased by 8 (so code + kI4Bias as bf16), split
+// by the parity of m: ev[t] / od[t] hold token t's even / odd m in bytes.
+template <int D>
+struct PfV4 {
+    unsigned ev[8], od[8];   // tokens 0..3 of block A, then of block B
+    __device__ __forceinline__ void load(const uint8_t* va, const uint8_t* vb, int lane) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const uint8_t* run = (b == 0 ? va : vb) + lane * (D / 8);
+            if constexpr (D == 128) {
+                const u32x4 w = *reinterpret_cast<const u32x4*>(run);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) i4_split(w[t], ev[4 * b + t], od[4 * b + t]);
+            } else {
+                const u32x2 w = *reinterpret_cast<const u32x2*>(run);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) i4_split(w[t / 2] >> (16 * (t % 2)), ev[4 * b + t], od[4 * b + t]);
+            }
+        }
+    }
+    // 8 biased bf16: dim 16m + col, tokens 0..3 of A then of B
+    __device__ __forceinline__ u32x4 op(int m) const {
+        const unsigned* src = (m % 2) ? od : ev;
+        return u32x4{i4_pair(src[0], src[1], m / 2), i4_pair(src[2], src[3], m / 2), i4_pair(src[4], src[5], m / 2),
+                     i4_pair(src[6], src[7], m / 2)};
+    }
+};
 
 // Zero, in an LDS stage, the V entries of tokens >= n of both blocks of the
 // pair starting at token t0 (bytes past the sequence end, or the second block
@@ -130,8 +200,11 @@ __device__ __forceinline__ void pf_zero_v_tail(uint8_t* stage, int t0, int n, in
         const int dim = r - blk * D;
         const int cut = n - (t0 + 16 * blk);          // tokens of this block below n
         uint8_t* row = stage + (2 * blk + 1) * Gm::TILE + dim * 16 * Gm::EB;
-        for (int o = max(cut, 0); o < 16; ++o)
-            for (int b = 0; b < Gm::EB; ++b) row[o * Gm::EB + b] = 0;
+        for (int o = max(cut, 0); o < 16; ++o) {
+            // byte of token o in the row as placed in LDS (see pf_v_chunk)
+            const int at = Gm::EB == 2 ? ((((o >> 3) ^ ((dim >> 3) & 1)) << 4) + (o & 7) * 2) : o;
+            for (int b = 0; b < Gm::EB; ++b) row[at + b] = 0;
+        }
     }
 }
 
@@ -140,7 +213,6 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
 void attn_prefill_kernel(PrefillArgs a) {
     using Gm = PfGeom<KVT, D>;
     extern __shared__ __attribute__((aligned(16))) uint8_t pf_smem[];
-    int32_t* ids = reinterpret_cast<int32_t*>(pf_smem + kPfStages * Gm::PAIR);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -160,11 +232,15 @@ void attn_prefill_kernel(PrefillArgs a) {
     const int h = sh - s * H;
 
     const int n = a.seq_lens[s];
-    const int C = a.chunk;
+    // The sequence's chunk: C tokens whose queries (and outputs) are rows
+    // q0 .. q0 + C - 1 of the packed arrays.
+    const int q0 = a.query_start ? a.query_start[s] : s * a.chunk;
+    const int C = a.query_start ? a.query_start[s + 1] - q0 : a.chunk;
     const int G = a.group;
     const int Rt = C * G;                       // query rows of this (sequence, KV head)
     const int first = n - C;                    // position of chunk token 0
     const int row_wg = rt * kPrefillRows;
+    if (row_wg >= Rt) return;                   // a row tile past a shorter chunk (the whole work-group)
     const int last_row = min(Rt, row_wg + kPrefillRows) - 1;
     const int nblk = (first + last_row / G + kBlock) / kBlock;   // blocks the tile's last row sees
     const int npair = (nblk + 1) >> 1;
@@ -187,10 +263,14 @@ void attn_prefill_kernel(PrefillArgs a) {
         const int j = valid ? row / G : 0;
         const int g = valid ? row - (row / G) * G : 0;
         const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) +
-            ((static_cast<int64_t>(s) * C + j) * a.num_q_heads + h * G + g) * D;
+            ((static_cast<int64_t>(q0) + j) * a.num_q_heads + h * G + g) * D;
         qr[c].load(qrow, valid, lane);
         lim[c] = valid ? first + j + 1 : 0;
     }
+    // int4: kI4Bias times each query row's sum (the bias of its scores)
+    float qbias[kPfNT];
+#pragma unroll
+    for (int c = 0; c < kPfNT; ++c) qbias[c] = KVT == KV_INT4 ? kI4Bias * query_row_sum<D>(qr[c])[0] : 0.f;
 
     // o: unnormalised output per (column tile, 16 dims); ol: the row sums of
     // the bf16 probabilities, accumulated by the matrix cores against a tile
@@ -212,24 +292,31 @@ void attn_prefill_kernel(PrefillArgs a) {
                                static_cast<int64_t>(h) * 2 * a.tile_bytes;
     const int32_t* trow = a.table + static_cast<int64_t>(s) * a.max_blocks;
 
-    // The tile's block ids, a window of them at a time, in LDS.
-    int win_lo = 0;
-    auto load_window = [&](int lo) {
-        const int cnt = min(kPfIdWindow, nblk - lo);
-        for (int e = tid; e < cnt; e += 64 * kPfWaves) ids[e] = trow[lo + e];
-        win_lo = lo;
+    // Block ids come straight from the table through scalar loads (the row is
+    // uniform over the work-group and read-only during the kernel), the ids
+    // of the pair after next fetched one iteration before they are needed.
+    // Scalar loads leave the vector-memory counter to the LDS copies alone:
+    // block ids loaded with vector loads (or staged through LDS) made the
+    // compiler wait for every copy in flight before each pair's LDS reads.
+    typedef const int32_t __attribute__((address_space(4)))* ConstIds;
+    const ConstIds crow = (ConstIds)(trow);
+    auto ids_of = [&](int q, int& ia, int& ib) {
+        ia = crow[2 * q];
+        ib = 2 * q + 1 < nblk ? crow[2 * q + 1] : ia;
     };
-    auto issue = [&](int q) {
-        const int b = 2 * q - win_lo;
-        const int ia = __builtin_amdgcn_readfirstlane(ids[b]);
-        const int ib = 2 * q + 1 < nblk ? __builtin_amdgcn_readfirstlane(ids[b + 1]) : ia;
+    auto issue = [&](int q, int ia, int ib) {
         pf_issue<KVT, D>(head_base, block_stride, ia, ib, pf_smem + (q % kPfStages) * Gm::PAIR, wave, lane);
     };
-    load_window(0);
-    __syncthreads();
 #pragma unroll
-    for (int q = 0; q < kPfAhead; ++q)
-        if (q < npair) issue(q);
+    for (int q = 0; q < kPfAhead; ++q) {
+        if (q < npair) {
+            int ia, ib;
+            ids_of(q, ia, ib);
+            issue(q, ia, ib);
+        }
+    }
+    int next_a = 0, next_b = 0;   // ids of pair p + kPfAhead
+    if (kPfAhead < npair) ids_of(kPfAhead, next_a, next_b);
 
     for (int p = 0; p < npair; ++p) {
         // This wave's pieces of pair p have landed (the next pairs may still
@@ -241,21 +328,15 @@ void attn_prefill_kernel(PrefillArgs a) {
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
         __builtin_amdgcn_s_barrier();
         if (p + kPfAhead < npair) {
-            const int q = p + kPfAhead;
-            if (min(2 * q + 1, nblk - 1) >= win_lo + kPfIdWindow) {
-                // next window of ids: drain, swap, publish (once per 2048 blocks)
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
-                __builtin_amdgcn_s_barrier();
-                load_window(2 * q);
-                __syncthreads();
-            }
-            issue(q);
+            issue(p + kPfAhead, next_a, next_b);
+            if (p + kPfAhead + 1 < npair) ids_of(p + kPfAhead + 1, next_a, next_b);
         }
 
         uint8_t* st = pf_smem + (p % kPfStages) * Gm::PAIR;
         const int t0 = 32 * p;
-        if (t0 + 32 > n) {
-            // only the last pair reaches past the sequence end; nothing is in flight
+        if (KVT != KV_INT4 && t0 + 32 > n) {
+            // only the last pair reaches past the sequence end; nothing is in
+            // flight (every int4 nibble is a finite value: no zeroing needed)
             pf_zero_v_tail<KVT, D>(st, t0, n, tid);
             __syncthreads();
         }
@@ -270,6 +351,11 @@ void attn_prefill_kernel(PrefillArgs a) {
         for (int c = 0; c < kPfNT; ++c) {
             f32x4 sa = scores<D>(ka, qr[c]);
             f32x4 sb = scores<D>(kb, qr[c]);
+            if constexpr (KVT == KV_INT4) {
+                // int4 scores come out biased by kI4Bias times the query row's sum
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { sa[i] -= qbias[c]; sb[i] -= qbias[c]; }
+            }
             if (need_mask) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -313,9 +399,14 @@ void attn_prefill_kernel(PrefillArgs a) {
             ol[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, pop[c]), ol[c], 0, 0, 0);
         const uint8_t* va = st + Gm::TILE;
         const uint8_t* vb = st + 3 * Gm::TILE;
+        PfV4<D> v4;
+        if constexpr (KVT == KV_INT4) v4.load(va, vb, lane);
 #pragma unroll
         for (int m = 0; m < D / 16; ++m) {
-            const bf16x8 av = __builtin_bit_cast(bf16x8, pf_v_op<KVT, D>(va, vb, m, col, lg));
+            u32x4 vop;
+            if constexpr (KVT == KV_INT4) vop = v4.op(m);
+            else vop = pf_v_op<KVT, D>(va, vb, m, col, lg);
+            const bf16x8 av = __builtin_bit_cast(bf16x8, vop);
 #pragma unroll
             for (int c = 0; c < kPfNT; ++c)
                 o[c][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, pop[c]), o[c][m],
@@ -327,12 +418,17 @@ void attn_prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int c = 0; c < kPfNT; ++c) {
         const float l = ol[c][0];
+        if constexpr (KVT == KV_INT4) {
+            // int4: the output came out biased by kI4Bias times the row's probability sum
+#pragma unroll
+            for (int m = 0; m < D / 16; ++m) o[c][m] -= kI4Bias * l;
+        }
         const int row = row_w + 16 * c + col;
         if (row >= Rt) continue;
         const int j = row / G;
         const int g = row - j * G;
         const float inv = vscale / l;
-        const int64_t base = ((static_cast<int64_t>(s) * C + j) * a.num_q_heads + h * G + g) * D + 4 * lg;
+        const int64_t base = ((static_cast<int64_t>(q0) + j) * a.num_q_heads + h * G + g) * D + 4 * lg;
 #pragma unroll
         for (int m = 0; m < D / 16; ++m) {
             const f32x4 v = o[c][m] * inv;
@@ -359,6 +455,7 @@ hipError_t launch_pf(const PrefillArgs& a, hipStream_t stream) {
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, hipStream_t stream) {
     if (kv_dtype == KV_BF16) return head_dim == 128 ? launch_pf<KV_BF16, 128>(a, stream) : launch_pf<KV_BF16, 64>(a, stream);
     if (kv_dtype == KV_INT8) return head_dim == 128 ? launch_pf<KV_INT8, 128>(a, stream) : launch_pf<KV_INT8, 64>(a, stream);
+    if (kv_dtype == KV_INT4) return head_dim == 128 ? launch_pf<KV_INT4, 128>(a, stream) : launch_pf<KV_INT4, 64>(a, stream);
     return head_dim == 128 ? launch_pf<KV_FP8, 128>(a, stream) : launch_pf<KV_FP8, 64>(a, stream);
 }
 

@@ -207,16 +207,39 @@ class Setup:
         w = self.w
         scale = w.scale if scale is None else scale
         od = None if out_dtype is None else {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
-        out = self.pk.paged_attention_prefill(self.pool, w.layer, self.table, self.q, scale, out_dtype=od)
+        if w.chunk_lens is not None:
+            out = self.pk.paged_attention_prefill_varlen(self.pool, w.layer, self.table, self.q, w.query_start,
+                                                         scale, out_dtype=od)
+        else:
+            out = self.pk.paged_attention_prefill(self.pool, w.layer, self.table, self.q, scale, out_dtype=od)
         torch.cuda.synchronize()
         return out
 
     def oracle_prefill(self, seqs=None, rows=None, scale=None):
+        """Uniform chunks: the oracle's prefill over the batch.  Ragged
+        chunks: the oracle's prefill per sequence with that sequence's chunk,
+        placed at its packed rows (``rows`` then indexes the packed rows)."""
         w = self.w
         scale = w.scale if scale is None else scale
         q = q_values(w.q, w.q_dtype)
-        return oatt.prefill(self.desc, self.oracle_image(), w.layer, w.block_tables, w.seq_lens, q,
-                            w.k_rows, scale, self.k_scale, self.v_scale, seqs=seqs, rows=rows)
+        if w.chunk_lens is None:
+            return oatt.prefill(self.desc, self.oracle_image(), w.layer, w.block_tables, w.seq_lens, q,
+                                w.k_rows, scale, self.k_scale, self.v_scale, seqs=seqs, rows=rows)
+        qs = w.query_start
+        out = np.zeros_like(q)
+        want = None if rows is None else set(int(r) for r in rows)
+        for s in (range(w.batch) if seqs is None else seqs):
+            c = int(w.chunk_lens[s])
+            if c == 0:
+                continue
+            local = [j for j in range(c) if want is None or qs[s] + j in want]
+            if not local:
+                continue
+            ref = oatt.prefill(self.desc, self.oracle_image(), w.layer, w.block_tables[s:s + 1],
+                               w.seq_lens[s:s + 1], q[None, qs[s]:qs[s] + c], c, scale, self.k_scale,
+                               self.v_scale, rows=local)
+            out[qs[s] + np.asarray(local)] = ref[0, local]
+        return out
 
     def oracle(self, seqs=None, scale=None):
         w = self.w

@@ -3,8 +3,9 @@ per layer and KV head, two codes per byte in the nibble layout of the library
 header) through every call that reads or writes the cache: bit-exact pool
 bytes after reshape_and_cache (bf16 and float32 inputs, ties, saturation,
 NaN), decode / verify / fused append against the float64 oracle, every code
-decoded exactly through attention, the full-size Llama-3-8B-shaped decode on
-sampled sequences, and the prefill call refusing int4 pools."""
+decoded exactly through attention, and chunked prefill over int4 pools (the
+full-size Llama-3-8B-shaped decode is checked on every sequence in
+test_gpu_fullsize.py)."""
 
 import numpy as np
 import pytest
@@ -136,14 +137,17 @@ def test_int4_verify_rows(k, Hq, Hkv, d):
     assert_close(out_values(s.run()), s.oracle(), "int4", f"int4 verify k={k}")
 
 
-def test_int4_prefill_is_refused():
-    log("int4 prefill refused")
-    pk = _pk()
-    w = workloads.custom(4500, [40, 64], num_q_heads=8, num_kv_heads=2, head_dim=128, kv_dtype="int4",
-                         k_rows=16, partition_tokens=0)
+@pytest.mark.parametrize("Hq,Hkv,d,C,lens", [(32, 8, 128, 40, [40, 64, 301]), (8, 8, 64, 33, [33, 100, 190]),
+                                             (64, 8, 128, 20, [20, 47])])
+def test_int4_prefill(Hq, Hkv, d, C, lens):
+    """Chunked prefill over int4 pools (codes widened to biased bf16 from
+    each lane's run in LDS) against the oracle."""
+    log(f"int4 prefill {Hq}/{Hkv} d{d} C={C}")
+    w = workloads.custom(4500 + C + d, lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, kv_dtype="int4",
+                         k_rows=C, partition_tokens=0)
     s = Setup(w)
-    with pytest.raises(pk.PagedKVError):
-        s.run_prefill()
+    err = assert_close(out_values(s.run_prefill()), s.oracle_prefill(), "int4", f"int4 prefill d{d}")
+    log(f"  max abs err {err:.3e}")
 
 
 # The full-size c2i4 workload is checked on every sequence in test_gpu_fullsize.py.

@@ -2,12 +2,13 @@
 
 Every sequence carries C query tokens at positions n-C .. n-1 (their K/V
 appended through the library first); row j sees positions t <= n-C+j.
-Tolerance as for decode: 1e-2 max-abs for bf16 / fp8 KV on unit-scale
-outputs.  Covered: the reduced and full-size chunked-prefill workloads,
-GQA / MQA / MHA heads, head_dim 64 and 128, bf16 and fp8 pools, chunks that
-do not fill the last 256-row tile or the last block, a chunk that is the whole
-sequence, a causal needle, and agreement with the verify kernel where both
-apply.
+Tolerance as for decode: 1e-2 max-abs for bf16 / fp8 / int8 / int4 KV on
+unit-scale outputs.  Covered: the reduced and full-size chunked-prefill
+workloads, GQA / MQA / MHA heads, head_dim 64 and 128, bf16 and fp8 pools,
+chunks that do not fill the last 192-row tile or the last block, a chunk that
+is the whole sequence, a causal needle, agreement with the verify kernel
+where both apply, and batches whose sequences carry chunks of different
+lengths (0, 1, 17, ragged; every pool type) through the varlen call.
 """
 
 import numpy as np
@@ -109,3 +110,76 @@ def test_prefill_full_size_sampled(seqs, rows):
     ref = s.oracle_prefill(seqs=seqs, rows=rows)
     err = assert_close(got[np.ix_(seqs, rows)], ref[np.ix_(seqs, rows)], "bf16", "pf sampled")
     log(f"  max abs err {err:.3e}")
+
+
+# ------------------------------------------------- a chunk length per sequence
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8", "int4"])
+def test_prefill_ragged_chunks(kv):
+    """Sequences with chunks of 0, 1, 17 and ~40-250 tokens in one call
+    (packed rows), every row against the oracle run per sequence."""
+    log(f"prefill ragged pfvs {kv}")
+    w = workloads.make_ragged_prefill("pfvs", kv_dtype=kv)
+    s = Setup(w)
+    got = out_values(s.run_prefill())
+    err = assert_close(got, s.oracle_prefill(), kv, f"pfvs {kv}")
+    log(f"  pfvs {kv}: chunks {list(w.chunk_lens)}, max abs err {err:.3e}")
+
+
+def test_prefill_varlen_equals_uniform_call():
+    """Uniform chunks given as packed rows with query_start = s * C: the
+    varlen call returns the uniform call's output bit for bit."""
+    import paged_kv_cache_293_amd as pk
+    log("prefill varlen == uniform")
+    C = 70
+    w = workloads.custom(701, [70, 150, 333], num_q_heads=32, num_kv_heads=8, head_dim=128, kv_dtype="bf16",
+                         k_rows=C, partition_tokens=0)
+    s = Setup(w)
+    uni = s.run_prefill()
+    q = s.q.reshape(-1, w.num_q_heads, w.head_dim)
+    var = pk.paged_attention_prefill_varlen(s.pool, 0, s.table, q, np.arange(w.batch + 1) * C, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(var.reshape(uni.shape), uni)
+
+
+def test_prefill_varlen_contract():
+    import paged_kv_cache_293_amd as pk
+    log("prefill varlen contract")
+    w = workloads.make_ragged_prefill("pfvs")
+    s = Setup(w)
+    qs = w.query_start
+    B = w.batch
+    too_long = np.concatenate([[0], np.cumsum([int(w.seq_lens[0]) + 1] + [0] * (B - 1))]).astype(np.int32)
+    cases = [(qs + 1, -1), (too_long, -4), (np.concatenate([[0, 5, 3], qs[3:] + 10]).astype(np.int32), -1)]
+    for bad, status in cases:
+        q = torch.zeros((int(bad[-1]), w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(pk.PagedKVError) as e:
+            pk.paged_attention_prefill_varlen(s.pool, 0, s.table, q, bad)
+        assert e.value.status == status
+    # a batch without chunk tokens enqueues nothing
+    empty = torch.zeros((0, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    out = pk.paged_attention_prefill_varlen(s.pool, 0, s.table, empty, np.zeros(B + 1, np.int32))
+    torch.cuda.synchronize()
+    assert out.shape[0] == 0
+
+
+def test_prefill_ragged_full_size_sampled():
+    """pfv: 8 sequences, cached prefixes to 14336 tokens, chunks uniform in
+    [1, 2048]; the first, last and sampled rows of every chunk against the
+    oracle reading the device pool back (unused blocks hold NaN)."""
+    log("prefill ragged full size pfv")
+    w = workloads.make_ragged_prefill("pfv")
+    s = Setup(w, poison=True)
+    got = out_values(s.run_prefill())
+    assert np.isfinite(got).all()
+    qs = w.query_start
+    rng = np.random.default_rng(5)
+    rows = []
+    for sq in range(w.batch):
+        c = int(w.chunk_lens[sq])
+        rows += [int(qs[sq]), int(qs[sq]) + c - 1] + [int(qs[sq]) + int(j) for j in rng.choice(c, size=min(c, 3),
+                                                                                                replace=False)]
+    rows = sorted(set(rows))
+    ref = s.oracle_prefill(rows=rows)
+    err = assert_close(got[rows], ref[rows], "bf16", "pfv sampled")
+    log(f"  pfv: chunks {list(w.chunk_lens)}, {len(rows)} rows, max abs err {err:.3e}")

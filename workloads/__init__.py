@@ -26,6 +26,8 @@ c5     Speculative verify over a shared prefix: 32 / 8 heads, d 128, fp8 E4M3 KV
 pf     Chunked prefill, Llama-3-8B-shaped layer (32 / 8 heads, d 128, bf16):
        8 sequences, each a cached prefix of uniform [0, 14336] tokens followed
        by a chunk of 2048 query tokens.
+pfv    Chunked prefill with a chunk length per sequence: as pf, chunks uniform
+       in [1, 2048] (make_ragged_prefill; pfvs is its reduced variant).
 =====  ==========================================================================
 
 Reduced variants (``c2s`` ... ``c5s``) keep the head shapes and the length mix
@@ -52,7 +54,8 @@ Conventions (readings recorded in the design notes):
   for head h with codes drawn as e4m3(x*448/4) (int8: round(x*127/4)
   saturated to +-127; int4: round(x*7/4) saturated to +-7, two per byte).
 
-Seeds: 293000 + config number (c1 -> 293001, ...; pf, pfs -> 293006).
+Seeds: 293000 + config number (c1 -> 293001, ...; pf, pfs -> 293006; pfv,
+pfvs -> 293008).
 """
 
 import math
@@ -96,6 +99,7 @@ class Workload:
     k_scale: Optional[np.ndarray] = None   # float32 [L][H_kv] (fp8, int8 and int4 only)
     v_scale: Optional[np.ndarray] = None
     shared_prefix_tokens: int = 0
+    chunk_lens: Optional[np.ndarray] = None   # int32 [B]: ragged chunked prefill (q packed [T][H_q][d])
     info: dict = field(default_factory=dict)
 
     @property
@@ -109,6 +113,11 @@ class Workload:
     @property
     def max_blocks(self):
         return int(self.block_tables.shape[1])
+
+    @property
+    def query_start(self):
+        """Ragged prefill: first packed query row of each sequence's chunk (B + 1 entries)."""
+        return np.concatenate([[0], np.cumsum(self.chunk_lens)]).astype(np.int32)
 
 
 # ------------------------------------------------------------------ casts
@@ -308,6 +317,89 @@ def _make_prefill(name, materialize, seed):
     lens = _uniform(rng, 0, P, B) + C
     return build(name, seed, rng, lens, num_q_heads=32, num_kv_heads=8, head_dim=128, kv_dtype="bf16",
                  k_rows=C, materialize=materialize, partition_tokens=0)
+
+
+def build_ragged(name, seed, rng, prefix_lens, chunk_lens, *, num_q_heads, num_kv_heads, head_dim, kv_dtype,
+                 materialize=True):
+    """A chunked-prefill batch whose sequences carry chunks of different
+    lengths: sequence s has prefix_lens[s] cached tokens followed by
+    chunk_lens[s] chunk tokens (their K/V appended this step).  Queries and
+    outputs are packed [sum of chunks][H_q][d] in sequence order.  Draw order
+    as ``build``: placement, Q, prefill K/V (materialised only), chunk K/V."""
+    prefix_lens = np.asarray(prefix_lens, dtype=np.int64)
+    chunk_lens = np.asarray(chunk_lens, dtype=np.int64)
+    seq_lens = prefix_lens + chunk_lens
+    B = seq_lens.shape[0]
+    blocks_per_seq = [-(-int(n) // BLOCK) for n in seq_lens]
+    used = sum(blocks_per_seq)
+    num_blocks = max(1, math.ceil(1.25 * used))
+    max_blocks = max(1, max(blocks_per_seq))
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    tables = np.full((B, max_blocks), -1, dtype=np.int32)
+    cursor = 0
+    for s in range(B):
+        tables[s, :blocks_per_seq[s]] = perm[cursor:cursor + blocks_per_seq[s]]
+        cursor += blocks_per_seq[s]
+    q_dtype = in_dtype = "bf16"
+    Hq, Hkv, d = num_q_heads, num_kv_heads, head_dim
+    T = int(chunk_lens.sum())
+    q = _cast(rng.standard_normal((T, Hq, d), dtype=np.float32), q_dtype)
+    pre_seq_ids = pre_positions = k_pre = v_pre = None
+    if materialize:
+        pre_seq_ids = np.concatenate([np.full(int(p), s, np.int32) for s, p in enumerate(prefix_lens)] +
+                                     [np.zeros(0, np.int32)])
+        pre_positions = np.concatenate([np.arange(int(p), dtype=np.int32) for p in prefix_lens] +
+                                       [np.zeros(0, np.int32)])
+        k_pre = _cast(rng.standard_normal((pre_seq_ids.shape[0], Hkv, d), dtype=np.float32), in_dtype)
+        v_pre = _cast(rng.standard_normal((pre_seq_ids.shape[0], Hkv, d), dtype=np.float32), in_dtype)
+    new_ids = np.concatenate([np.full(int(c), s, np.int32) for s, c in enumerate(chunk_lens)] + [np.zeros(0, np.int32)])
+    new_pos = np.concatenate([np.arange(int(p), int(p + c), dtype=np.int32) for p, c in zip(prefix_lens, chunk_lens)]
+                             + [np.zeros(0, np.int32)])
+    k_new = _cast(rng.standard_normal((T, Hkv, d), dtype=np.float32), in_dtype)
+    v_new = _cast(rng.standard_normal((T, Hkv, d), dtype=np.float32), in_dtype)
+    k_scale = v_scale = None
+    if kv_dtype in ("fp8", "int8", "int4"):
+        qmax = np.float32({"fp8": 448.0, "int8": 127.0, "int4": 7.0}[kv_dtype])
+        base = np.float32(4.0) / qmax
+        if materialize and k_pre.shape[0]:
+            k_scale = (np.abs(values_f32(k_pre, in_dtype)).max(axis=(0, 2)) / qmax).astype(np.float32)[None, :]
+            v_scale = (np.abs(values_f32(v_pre, in_dtype)).max(axis=(0, 2)) / qmax).astype(np.float32)[None, :]
+        else:
+            per_head = (base * (1.0 + np.arange(Hkv, dtype=np.float32) / 8.0)).astype(np.float32)
+            k_scale = per_head[None, :].copy()
+            v_scale = per_head[None, :].copy()
+    return Workload(
+        name=name, seed=seed, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, kv_dtype=kv_dtype, q_dtype=q_dtype,
+        out_dtype="bf16", k_rows=0, num_blocks=int(num_blocks), seq_lens=seq_lens.astype(np.int32),
+        block_tables=tables, q=q, new_seq_ids=new_ids, new_positions=new_pos, k_new=k_new, v_new=v_new,
+        in_dtype=in_dtype, partition_tokens=0, materialized=materialize, pre_seq_ids=pre_seq_ids,
+        pre_positions=pre_positions, k_pre=k_pre, v_pre=v_pre, k_scale=k_scale, v_scale=v_scale,
+        chunk_lens=chunk_lens.astype(np.int32), info={"blocks_used": int(used)})
+
+
+def make_ragged_prefill(name, materialize=None, seed=None, kv_dtype="bf16"):
+    """Chunked prefill with a chunk length per sequence, Llama-3-8B-shaped
+    layer (32 / 8 heads, d 128):
+    pfv:  8 sequences, cached prefixes uniform [0, 14336], chunks uniform
+          [1, 2048] (the last chunks of prompts of any length);
+    pfvs: 5 sequences, prefixes uniform [0, 300], chunks {0, 1, 17, uniform
+          [40, 250] twice} in seeded order (an empty chunk, a one-token chunk,
+          ragged tiles)."""
+    seed = SEED_BASE + 8 if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    small = name == "pfvs"
+    if materialize is None:
+        materialize = small
+    if small:
+        prefix = _uniform(rng, 0, 300, 5)
+        chunks = np.concatenate([[0, 1, 17], _uniform(rng, 40, 250, 2)])
+        chunks = chunks[rng.permutation(5)]
+        prefix = np.maximum(prefix, 1)   # every sequence holds at least one token
+    else:
+        prefix = _uniform(rng, 0, 14336, 8)
+        chunks = _uniform(rng, 1, 2048, 8)
+    return build_ragged(name, seed, rng, prefix, chunks, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                        kv_dtype=kv_dtype, materialize=materialize)
 
 
 def custom(seed, seq_lens, **kw):
