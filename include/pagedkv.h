@@ -112,7 +112,7 @@ typedef int32_t pkv_status;
  */
 typedef struct pkv_pool_desc {
     int32_t num_layers;    /* >= 1                                    */
-    int32_t num_blocks;    /* 1 .. 2^30 - 1 physical blocks per layer  */
+    int32_t num_blocks;    /* >= 1 physical blocks per layer          */
     int32_t num_kv_heads;  /* >= 1                                    */
     int32_t head_dim;      /* 64 or 128                               */
     int32_t block_size;    /* must be PKV_BLOCK_SIZE (16)             */
@@ -152,8 +152,7 @@ int64_t kv_pool_bytes(const pkv_pool_desc* desc);
  *   dev_k_scale, dev_v_scale  float32 [num_layers][num_kv_heads] device arrays;
  *              required (non-NULL) for PKV_FP8_E4M3, PKV_INT8 and PKV_INT4, ignored otherwise.
  * Errors: PKV_ERR_INVALID (null, short or misaligned buffer, bad counts),
- *         PKV_ERR_UNSUPPORTED (block_size != 16, head_dim not 64/128, dtype,
- *         num_blocks >= 2^30).
+ *         PKV_ERR_UNSUPPORTED (block_size != 16, head_dim not 64/128, dtype).
  * The buffer contents are not touched.
  */
 pkv_status kv_pool_create(const pkv_pool_desc* desc, void* dev_base, size_t dev_bytes,

@@ -49,6 +49,7 @@ struct pkv_table {
     // launch may have left merge tickets or queue counters non-zero, so the
     // table is refused until uploaded again.
     bool stale = false;
+    bool shared_blocks = false;     // some physical block is named by two sequences
 };
 
 namespace {
@@ -75,7 +76,6 @@ bool scaled_dtype(int32_t dtype) { return dtype == PKV_FP8_E4M3 || dtype == PKV_
 pkv_status check_desc(const pkv_pool_desc* d) {
     if (!d) return PKV_ERR_INVALID;
     if (d->num_layers < 1 || d->num_blocks < 1 || d->num_kv_heads < 1) return PKV_ERR_INVALID;
-    if (d->num_blocks >= pkv::kSharedBlockFlag) return PKV_ERR_UNSUPPORTED;   // ids carry a flag bit
     if (d->block_size != PKV_BLOCK_SIZE) return PKV_ERR_UNSUPPORTED;
     if (d->head_dim != 64 && d->head_dim != 128) return PKV_ERR_UNSUPPORTED;
     if (elem_bits(d->kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
@@ -432,13 +432,20 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
         std::memcpy(hs + L.seq_lens / 4, host_seq_lens, sizeof(int32_t) * num_seqs);
         std::memcpy(hs + L.seq_parts / 4, P.seq_parts.data(), sizeof(int32_t) * 2 * num_seqs);
         std::memcpy(hs + L.units / 4, P.units.data(), sizeof(int32_t) * P.units.size());
-        // Blocks named by more than one sequence (a shared prefix) are read
-        // by every one of them: flagged, they keep the cached load policy.
-        std::vector<uint8_t> refs(static_cast<size_t>(nb_pool), 0);
-        for (int32_t s = 0; s < num_seqs; ++s) {
-            const int32_t used = (host_seq_lens[s] + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
-            const int32_t* row = host_block_table + static_cast<int64_t>(s) * max_blocks_per_seq;
-            for (int32_t j = 0; j < used; ++j) refs[row[j]] = static_cast<uint8_t>(std::min(2, refs[row[j]] + 1));
+        // Is any physical block named twice among the used entries (a prefix
+        // shared by several sequences)?  Such a batch reads those blocks once
+        // per reference, and its attention launches keep the cached
+        // tile-load policy instead of streaming.
+        {
+            std::vector<uint8_t> seen(static_cast<size_t>(nb_pool), 0);
+            for (int32_t s = 0; s < num_seqs && !t->shared_blocks; ++s) {
+                const int32_t used = (host_seq_lens[s] + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
+                const int32_t* row = host_block_table + static_cast<int64_t>(s) * max_blocks_per_seq;
+                for (int32_t j = 0; j < used; ++j) {
+                    if (seen[row[j]]) { t->shared_blocks = true; break; }
+                    seen[row[j]] = 1;
+                }
+            }
         }
         for (int32_t u = 0; u < P.num_units; ++u) {
             const int32_t* d = &P.units[static_cast<size_t>(u) * pkv::kUnitInts];
@@ -449,8 +456,7 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
             const int32_t b0 = d[pkv::kUnitB0], nb = d[pkv::kUnitNb], rot = d[pkv::kUnitRot];
             for (int32_t j = 0; j < P.stride; ++j) {
                 const int32_t jj = j < nb ? (j + rot) % nb : rot;
-                const int32_t id = row[b0 + jj];
-                ids[j] = id | (refs[id] > 1 ? pkv::kSharedBlockFlag : 0);
+                ids[j] = row[b0 + jj];
             }
         }
         hipStream_t st = static_cast<hipStream_t>(stream);
@@ -624,7 +630,7 @@ pkv_status attention_call(const pkv_pool* pool, int32_t layer, const pkv_table* 
     a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
     a.score_scale = scale * 1.4426950408889634f;
     const hipError_t err = pkv::launch_attention(a, kv, pool->desc.head_dim, table->num_units,
-                                                 static_cast<hipStream_t>(stream));
+                                                 table->shared_blocks, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) const_cast<pkv_table*>(table)->stale = true;
     return hip_status(err);
 }

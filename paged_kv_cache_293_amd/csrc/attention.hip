@@ -188,7 +188,7 @@ __host__ __device__ inline int acc_area_floats(int rows, int d, int k_rows, int 
 // four waves, merge the waves, then write the output (unsplit sequence) or the
 // partial result, merging the sequence's partials when this is the last of
 // them to arrive.
-template <int KVT, int D, int NT>
+template <int KVT, int D, int NT, int POL>
 __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, const int h, float* smem,
                                             int* ticket_s, int& claimed, const int tid) {
     const int R = a.rows;
@@ -384,17 +384,11 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     // The next block's loads are issued unconditionally so the wait counts
     // stay static; past the last block they go through a zero-sized
     // resource (no memory traffic, zeros returned).
-    // Block i of the chunk: the tiles of a block several sequences share
-    // (flagged in its id) are read with the cached policy, the others
-    // streamed.  The flag is uniform over the wave, so the branch is too,
-    // and both arms issue the same loads.
+    // Block i of the chunk, loaded with the launch's cache policy POL.
     auto issue = [&](TileRegs<KVT, D>& t, int i, bool valid) {
-        const int raw = __builtin_amdgcn_readlane(id, min(i, 63));
-        const int pid = raw & ~kSharedBlockFlag;
-        const __amdgpu_buffer_rsrc_t r =
-            tile_rsrc(head_base + static_cast<int64_t>(pid) * block_stride, valid ? a.tile_bytes : 0);
-        if (raw & kSharedBlockFlag) t.template load<kCachedLoad>(r, koff, voff);
-        else t.template load<kStreamLoad>(r, koff, voff);
+        const int pid = __builtin_amdgcn_readlane(id, min(i, 63));
+        t.template load<POL>(tile_rsrc(head_base + static_cast<int64_t>(pid) * block_stride, valid ? a.tile_bytes : 0),
+                             koff, voff);
     };
     TileRegs<KVT, D> ta, tb, tc;
     // First loads of a chunk: one block in flight, two with three buffers.
@@ -407,7 +401,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             id = 0;
             if (base + kWaves * lane < a.unit_stride) id = uids[base + kWaves * lane];
         }
-        id = (id & kSharedBlockFlag) | min(max(id & ~kSharedBlockFlag, 0), a.num_blocks - 1);
+        id = min(max(id, 0), a.num_blocks - 1);
         issue(ta, 0, cnt > 0);
         if constexpr (deep) issue(tb, 1, cnt > 1);
     };
@@ -485,7 +479,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     {
         int j = appends ? blk_lo + min(tid, (hi - 1) / kBlock - blk_lo) - b0 - rot : 0;
         if (j < 0) j += nb;
-        pid_r = uids[j] & ~kSharedBlockFlag;
+        pid_r = uids[j];
     }
     if constexpr (kv_scaled<KVT>()) {
         k_sc = a.k_scale[a.layer * a.num_kv_heads + h];
@@ -760,7 +754,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
 // counters back to zero for the next call.  When the grid has a work-group
 // per item nothing is claimed and the queue is not touched.  No work-group
 // ever waits for another.
-template <int KVT, int D, int NT>
+template <int KVT, int D, int NT, int POL>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(NT == 1 ? decode_wgs_per_cu(KVT, D) : (NT == 2 && KVT != KV_F32 ? 2 : 1))))
 void attn_partition_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -788,7 +782,7 @@ void attn_partition_kernel(AttnArgs a) {
         // across the whole loop.
         int tid = wave_s * 64 + static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)));
         asm volatile("" : "+v"(tid));
-        attend_item<KVT, D, NT>(ia, unit, h, smem, &ticket, claimed, tid);
+        attend_item<KVT, D, NT, POL>(ia, unit, h, smem, &ticket, claimed, tid);
         if (tid == 0) next_item = static_cast<int>(gridDim.x) + claimed;
         lds_barrier();   // next_item visible; this item's LDS reads are done
         item = next_item;
@@ -889,7 +883,7 @@ int resident_work_groups() {
                                                                     NT == 1 ? kWaves : 1)) +
                                 2 * kWaves * rows) * sizeof(float);
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_partition_kernel<KVT, D, NT>, 64 * kWaves,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_partition_kernel<KVT, D, NT, kStreamLoad>, 64 * kWaves,
                                                          lds_max) != hipSuccess || n < 1)
             n = 1;
         per_cu = n;
@@ -902,13 +896,18 @@ int resident_work_groups() {
 }
 
 template <int KVT, int D, int NT>
-hipError_t launch_instance(const AttnArgs& a, int num_units, hipStream_t stream) {
+hipError_t launch_instance(const AttnArgs& a, int num_units, bool shared_blocks, hipStream_t stream) {
     (void)num_units;
     const size_t lds = (static_cast<size_t>(acc_area_floats(a.rows, D, a.k_rows, stage_token_bytes<KVT, D>(),
                                                             NT == 1 ? kWaves : 1)) +
                         2 * kWaves * a.rows) * sizeof(float);
     const int grid = std::min(a.num_items, resident_work_groups<KVT, D, NT>());
-    hipLaunchKernelGGL((attn_partition_kernel<KVT, D, NT>), dim3(grid), dim3(64 * kWaves), lds, stream, a);
+    // Tiles are streamed (each is read once per step) unless the batch shares
+    // blocks between sequences, whose repeated reads should hit the caches.
+    if (shared_blocks)
+        hipLaunchKernelGGL((attn_partition_kernel<KVT, D, NT, kCachedLoad>), dim3(grid), dim3(64 * kWaves), lds, stream, a);
+    else
+        hipLaunchKernelGGL((attn_partition_kernel<KVT, D, NT, kStreamLoad>), dim3(grid), dim3(64 * kWaves), lds, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (a.max_parts > a.fuse_max_parts) {
@@ -920,10 +919,10 @@ hipError_t launch_instance(const AttnArgs& a, int num_units, hipStream_t stream)
 }
 
 template <int KVT, int D>
-hipError_t launch_rows(const AttnArgs& a, int num_units, hipStream_t stream) {
-    if (a.rows <= 16) return launch_instance<KVT, D, 1>(a, num_units, stream);
-    if (a.rows <= 32) return launch_instance<KVT, D, 2>(a, num_units, stream);
-    return launch_instance<KVT, D, 4>(a, num_units, stream);
+hipError_t launch_rows(const AttnArgs& a, int num_units, bool shared, hipStream_t stream) {
+    if (a.rows <= 16) return launch_instance<KVT, D, 1>(a, num_units, shared, stream);
+    if (a.rows <= 32) return launch_instance<KVT, D, 2>(a, num_units, shared, stream);
+    return launch_instance<KVT, D, 4>(a, num_units, shared, stream);
 }
 
 }  // namespace
@@ -949,23 +948,24 @@ hipError_t attention_scratch(void** ptr, size_t* bytes) {
     return hipSuccess;
 }
 
-hipError_t launch_attention(const AttnArgs& a, int kv_dtype, int head_dim, int num_units,
+hipError_t launch_attention(const AttnArgs& a, int kv_dtype, int head_dim, int num_units, bool shared_blocks,
                             hipStream_t stream) {
     if (num_units <= 0) return hipSuccess;
+    const bool sh = shared_blocks;
     if (kv_dtype == KV_BF16)
-        return head_dim == 128 ? launch_rows<KV_BF16, 128>(a, num_units, stream)
-                               : launch_rows<KV_BF16, 64>(a, num_units, stream);
+        return head_dim == 128 ? launch_rows<KV_BF16, 128>(a, num_units, sh, stream)
+                               : launch_rows<KV_BF16, 64>(a, num_units, sh, stream);
     if (kv_dtype == KV_FP8)
-        return head_dim == 128 ? launch_rows<KV_FP8, 128>(a, num_units, stream)
-                               : launch_rows<KV_FP8, 64>(a, num_units, stream);
+        return head_dim == 128 ? launch_rows<KV_FP8, 128>(a, num_units, sh, stream)
+                               : launch_rows<KV_FP8, 64>(a, num_units, sh, stream);
     if (kv_dtype == KV_INT8)
-        return head_dim == 128 ? launch_rows<KV_INT8, 128>(a, num_units, stream)
-                               : launch_rows<KV_INT8, 64>(a, num_units, stream);
+        return head_dim == 128 ? launch_rows<KV_INT8, 128>(a, num_units, sh, stream)
+                               : launch_rows<KV_INT8, 64>(a, num_units, sh, stream);
     if (kv_dtype == KV_INT4)
-        return head_dim == 128 ? launch_rows<KV_INT4, 128>(a, num_units, stream)
-                               : launch_rows<KV_INT4, 64>(a, num_units, stream);
-    return head_dim == 128 ? launch_rows<KV_F32, 128>(a, num_units, stream)
-                           : launch_rows<KV_F32, 64>(a, num_units, stream);
+        return head_dim == 128 ? launch_rows<KV_INT4, 128>(a, num_units, sh, stream)
+                               : launch_rows<KV_INT4, 64>(a, num_units, sh, stream);
+    return head_dim == 128 ? launch_rows<KV_F32, 128>(a, num_units, sh, stream)
+                           : launch_rows<KV_F32, 64>(a, num_units, sh, stream);
 }
 
 }  // namespace pkv

@@ -21,11 +21,6 @@ constexpr int kUnitSlot = 6;     // partial-result slot (split sequences) or -1
 constexpr int kUnitRot = 7;      // walking-order rotation, seq mod nb
 constexpr int kUnitInts = 8;
 
-// Flag in a unit's block ids: the physical block is named by more than one
-// sequence of the batch (a shared prefix).  Its tiles are read with the
-// cached load policy; the others are streamed.  Block ids stay below 2^30.
-constexpr int32_t kSharedBlockFlag = 1 << 30;
-
 // Sequences with at most this many partitions are merged inside the
 // partition kernel; longer ones by the separate merge kernel.
 constexpr int kFuseMaxParts = 32;
@@ -123,8 +118,10 @@ constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(64) << 20;
 hipError_t attention_scratch(void** ptr, size_t* bytes);
 
 // Launch the attention kernels (partition pass, then the split-KV merge when
-// some sequence is split).  kv_dtype / head_dim / rows select the instance.
-hipError_t launch_attention(const AttnArgs& a, int kv_dtype, int head_dim, int num_units,
+// some sequence is split).  kv_dtype / head_dim / rows select the instance;
+// shared_blocks (some physical block is named by more than one sequence of
+// the batch) selects cached instead of streaming tile loads.
+hipError_t launch_attention(const AttnArgs& a, int kv_dtype, int head_dim, int num_units, bool shared_blocks,
                             hipStream_t stream);
 
 // Chunked-prefill attention: every sequence carries `chunk` query tokens at

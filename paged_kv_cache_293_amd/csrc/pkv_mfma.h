@@ -64,9 +64,13 @@ __device__ __forceinline__ float xwg_load(const float* p) {
 // one sequence owns once, so its tiles are streamed past the caches
 // (non-temporal, "nt"); measured on MI355X (paged_read_floor / read_ceiling
 // probes and the decode step itself) this raises the read rate by 10-13%
-// over the default policy, random 8 KiB reads from 5.8 to 6.5 TB/s.  A block
-// several sequences share (a common prefix) is read once per sequence, and
-// those reads should hit in the caches: it keeps the default policy.
+// over the default policy, random 8 KiB reads from 5.8 to 6.5 TB/s.  A batch
+// in which several sequences share blocks (a common prefix) reads those
+// blocks once per sequence, and those reads should hit in the caches: its
+// launches keep the default policy.  The policy is chosen per launch (a
+// template argument), not per block: a per-block branch between the two
+// loads made the compiler's wait counts conservative and the pipeline
+// shallow.
 constexpr int kStreamLoad = 2;
 constexpr int kCachedLoad = 0;
 
