@@ -231,7 +231,8 @@ def main():
         pool = pools[i % len(pools)] if pool is None else pool
         if args.separate:
             pk.slot_mapping_compute(table, sid, pos, out=slots)
-            pk.reshape_and_cache(pool, w.layer, k_new, v_new, slots)
+            pk.reshape_and_cache(pool, w.layer, k_new.view(-1, w.num_kv_heads, w.head_dim),
+                                 v_new.view(-1, w.num_kv_heads, w.head_dim), slots)
         if timed:
             ev[i][0].record()
         if args.separate and kq == 1:

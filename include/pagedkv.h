@@ -190,6 +190,24 @@ size_t block_table_device_bytes(const pkv_pool* pool, const int32_t* host_seq_le
  *                     attended independently and their partial results
  *                     merged (inside the attention kernel for up to 32
  *                     partitions, by a second kernel beyond that).
+ *                     With -1 the upload also looks for a shared prefix (page
+ *                     "KV cache & continuous batching", section "4. Prefix
+ *                     caching / prompt caching": requests with a common
+ *                     prefix reuse its cached K/V; page "LLM Serving - KV
+ *                     Cache, Batching, Speculative Decoding", section "KV
+ *                     memory, paging and prefix identity"): the longest run
+ *                     of leading physical blocks that every row names alike,
+ *                     kept when it holds 8 or more blocks, the batch has 4 or
+ *                     more sequences, the pool is not PKV_F32 and every
+ *                     sequence has a position past it.  An attention call on
+ *                     such a table whose rows all see the whole prefix
+ *                     (shortest seq_len - query_rows >= 16 * prefix blocks)
+ *                     attends to the prefix once for all sequences' query
+ *                     rows (a dense pass over the shared blocks, in up to 4
+ *                     chunks, each giving a partial result per row) and
+ *                     walks only each sequence's own blocks, one partition
+ *                     per sequence merged with the prefix partials: the
+ *                     same softmax, split at the prefix end.
  *   dev_buffer        device buffer of >= block_table_device_bytes(...) bytes;
  *                     it must stay valid and unmodified while the table is in use.
  * The host arrays are copied into the handle before returning; the copy to
@@ -217,6 +235,13 @@ pkv_status block_table_destroy(pkv_table* table);
  */
 pkv_status block_table_info(const pkv_table* table, int32_t* num_units, int32_t* num_split_slots,
                             int32_t* max_seq_len, int32_t* min_seq_len, int32_t* max_parts);
+
+/*
+ * The table's shared prefix (see block_table_upload, partition_tokens = -1):
+ * its length in blocks and the chunks the prefix pass cuts it into; both 0
+ * when the table has none.  Either output pointer may be NULL.
+ */
+pkv_status block_table_shared_prefix(const pkv_table* table, int32_t* prefix_blocks, int32_t* prefix_chunks);
 
 /*
  * Slot of each (sequence, position) pair through the uploaded tables:
@@ -255,7 +280,8 @@ pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, const void* de
 /*
  * Workspace bytes paged_attention_decode (query_rows = 1) or
  * paged_attention_verify needs with this pool and table: the split-KV partial
- * results (float32 output, max and sum per partition, query row and KV head).
+ * results (float32 output, max and sum per partition, query row and KV head),
+ * with a shared prefix also those of the prefix chunks.
  * 0 when no sequence is split.  Returns 0 for invalid arguments as well.
  */
 size_t paged_attention_workspace_bytes(const pkv_pool* pool, const pkv_table* table,

@@ -45,6 +45,7 @@ PROTOTYPES = {
     "block_table_info": (_c_int32, [_vp, ctypes.POINTER(_c_int32), ctypes.POINTER(_c_int32),
                                     ctypes.POINTER(_c_int32), ctypes.POINTER(_c_int32),
                                     ctypes.POINTER(_c_int32)]),
+    "block_table_shared_prefix": (_c_int32, [_vp, ctypes.POINTER(_c_int32), ctypes.POINTER(_c_int32)]),
     "slot_mapping_compute": (_c_int32, [_vp, _vp, _vp, _c_int32, _vp, _vp]),
     "reshape_and_cache": (_c_int32, [_vp, _c_int32, _vp, _vp, _c_int32, _vp, _c_int32, _vp]),
     "paged_attention_workspace_bytes": (_c_size, [_vp, _vp, _c_int32, _c_int32]),

@@ -117,6 +117,13 @@ class BlockTable:
         keys = ("num_units", "num_split_slots", "max_seq_len", "min_seq_len", "max_parts")
         return dict(zip(keys, (v.value for v in vals)))
 
+    def shared_prefix(self):
+        """(prefix blocks, prefix chunks) of the table's shared prefix, (0, 0) without one."""
+        pb, pc = ctypes.c_int32(), ctypes.c_int32()
+        _check("block_table_shared_prefix",
+               lib.block_table_shared_prefix(self._handle, ctypes.byref(pb), ctypes.byref(pc)))
+        return pb.value, pc.value
+
     def __del__(self):
         h = getattr(self, "_handle", None)
         if h:

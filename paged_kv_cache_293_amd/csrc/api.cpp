@@ -50,6 +50,20 @@ struct pkv_table {
     // table is refused until uploaded again.
     bool stale = false;
     bool shared_blocks = false;     // some physical block is named by two sequences
+    // Shared-prefix plan (prefix_blocks > 0): every sequence starts with the
+    // same prefix_blocks physical blocks; its units cover each sequence's
+    // own blocks whole, and each sequence has prefix_chunks leading partials.
+    int32_t prefix_blocks = 0;
+    int32_t prefix_chunks = 0;
+    int32_t prefix_chunk_blocks = 0;   // blocks per prefix chunk (the last one may hold fewer)
+    int32_t c_num_units = 0;
+    int32_t c_unit_stride = 0;
+    int32_t c_num_split_slots = 0;
+    int32_t c_max_parts = 0;
+    bool c_shared_blocks = false;   // blocks shared among the sequences' own blocks
+    int32_t* d_cseq_parts = nullptr;
+    int32_t* d_cunits = nullptr;
+    int32_t* d_cunit_ids = nullptr;
 };
 
 namespace {
@@ -95,7 +109,9 @@ struct Plan {
 
 // Device sub-buffers of an uploaded table, in this order, each 256-byte aligned.
 struct TableLayout {
-    size_t table, seq_lens, seq_parts, counters, queue, units, unit_ids, total;
+    size_t table, seq_lens, seq_parts, counters, queue, units, unit_ids;
+    size_t cseq_parts, cunits, cunit_ids;   // shared-prefix plan (empty without one)
+    size_t total;
 };
 
 int device_cu_count() {
@@ -188,15 +204,20 @@ std::vector<int32_t> place_on_cus(size_t num_units, int32_t num_kv_heads, int32_
 // auto_unit_blocks() blocks (no part under 2 * kAutoMinItemBlocks when the
 // batch alone fills the device).  Units are ordered longest first, or placed
 // by place_on_cus() when the grid has a work-group per item.
+// Shared-prefix plans: the units cover blocks skip .. of every sequence (the
+// first `skip` blocks are attended by the prefix pass), and every sequence
+// carries `lead` more partial results (the prefix chunks', in its first
+// slots), merged with its own.
 bool build_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, int32_t partition_tokens,
-                int32_t num_kv_heads, int32_t wgs_per_cu, Plan* P) {
+                int32_t num_kv_heads, int32_t wgs_per_cu, Plan* P, int32_t skip = 0, int32_t lead = 0) {
     if (num_seqs < 1 || max_blocks < 1) return false;
     if (partition_tokens < -1 || (partition_tokens > 0 && partition_tokens % PKV_BLOCK_SIZE)) return false;
     std::vector<int32_t> nblk(num_seqs);
     for (int32_t s = 0; s < num_seqs; ++s) {
         const int32_t n = seq_lens[s];
         if (n < 1 || static_cast<int64_t>(n) > static_cast<int64_t>(max_blocks) * PKV_BLOCK_SIZE) return false;
-        nblk[s] = (n + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
+        nblk[s] = (n + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE - skip;
+        if (nblk[s] < 1) return false;
     }
     int32_t unit_blocks;
     int32_t min_part = 1;   // balanced plan: smallest part a sequence is cut into
@@ -212,31 +233,32 @@ bool build_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, i
         if (static_cast<int64_t>(num_seqs) * num_kv_heads >= slots) min_part = 2 * pkv::kAutoMinItemBlocks;
     }
 
-    struct U { int32_t seq, b0, nb, part, parts; };
+    struct U { int32_t seq, b0, nb, part, parts, own; };
     std::vector<U> us;
     P->seq_parts.assign(2 * static_cast<size_t>(num_seqs), -1);
     P->num_split_slots = 0;
     P->max_parts = 0;
     P->stride = 0;
     for (int32_t s = 0; s < num_seqs; ++s) {
-        const int32_t parts = std::max(1, std::min((nblk[s] + unit_blocks - 1) / unit_blocks, nblk[s] / min_part));
+        const int32_t own = std::max(1, std::min((nblk[s] + unit_blocks - 1) / unit_blocks, nblk[s] / min_part));
+        const int32_t parts = lead + own;   // partial results merged for the sequence
         P->seq_parts[2 * s] = parts;
         if (parts > 1) {
             P->seq_parts[2 * s + 1] = P->num_split_slots;
             P->num_split_slots += parts;
         }
         P->max_parts = std::max(P->max_parts, parts);
-        for (int32_t p = 0; p < parts; ++p) {
+        for (int32_t p = 0; p < own; ++p) {
             int32_t b0, nb;
             if (partition_tokens == -1) {      // near-equal parts
-                const int32_t q = nblk[s] / parts, r = nblk[s] % parts;
+                const int32_t q = nblk[s] / own, r = nblk[s] % own;
                 b0 = p * q + std::min(p, r);
                 nb = q + (p < r ? 1 : 0);
             } else {
                 b0 = p * unit_blocks;
                 nb = std::min(unit_blocks, nblk[s] - b0);
             }
-            us.push_back({s, b0, nb, p, parts});
+            us.push_back({s, skip + b0, nb, lead + p, parts, own});
             P->stride = std::max(P->stride, nb);
         }
     }
@@ -261,11 +283,13 @@ bool build_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, i
         d[pkv::kUnitParts] = u.parts;
         d[pkv::kUnitSlot] = u.parts > 1 ? P->seq_parts[2 * u.seq + 1] + u.part : -1;
         d[pkv::kUnitRot] = u.seq % u.nb;   // sequences sharing blocks start their walk apart
+        d[pkv::kUnitTickets] = u.own;
     }
     return true;
 }
 
-TableLayout table_layout(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads, const Plan& P) {
+TableLayout table_layout(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads, const Plan& P,
+                         const Plan* C = nullptr) {
     TableLayout L;
     size_t off = 0;
     L.table = off;
@@ -282,11 +306,48 @@ TableLayout table_layout(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_he
     off = align_up(off + sizeof(int32_t) * pkv::kUnitInts * static_cast<size_t>(P.num_units));
     L.unit_ids = off;
     off = align_up(off + sizeof(int32_t) * static_cast<size_t>(P.num_units) * P.stride);
+    L.cseq_parts = L.cunits = L.cunit_ids = off;
+    if (C) {
+        L.cseq_parts = off;
+        off = align_up(off + sizeof(int32_t) * 2 * num_seqs);
+        L.cunits = off;
+        off = align_up(off + sizeof(int32_t) * pkv::kUnitInts * static_cast<size_t>(C->num_units));
+        L.cunit_ids = off;
+        off = align_up(off + sizeof(int32_t) * static_cast<size_t>(C->num_units) * C->stride);
+    }
     L.total = off;
     return L;
 }
 
 pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+// The largest shared prefix (in blocks) the lengths allow: every sequence
+// keeps at least one position past it.  0 when no shared-prefix plan can
+// arise (too few sequences, too short, or a float32 pool, which the prefix
+// pass does not take).
+int32_t max_prefix_blocks(const pkv_pool* pool, const int32_t* seq_lens, int32_t num_seqs) {
+    if (pool->desc.kv_dtype == PKV_F32 || num_seqs < pkv::kCascadeMinSeqs) return 0;
+    int32_t m = INT32_MAX;
+    for (int32_t s = 0; s < num_seqs; ++s) m = std::min(m, (seq_lens[s] - 1) / PKV_BLOCK_SIZE);
+    return m >= pkv::kCascadeMinBlocks ? m : 0;
+}
+
+// A shared-prefix plan: one unit per sequence over its own blocks (after
+// the prefix), prefix_chunks leading partials per sequence.
+bool build_cascade_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads,
+                        int32_t wgs_per_cu, int32_t prefix_blocks, int32_t prefix_chunks, Plan* C) {
+    return build_plan(seq_lens, num_seqs, max_blocks, 0, num_kv_heads, wgs_per_cu, C, prefix_blocks, prefix_chunks);
+}
+
+// Prefix chunks: at most kCascadeMaxChunks, each of at least
+// kCascadeChunkBlocks blocks (or one chunk of the whole prefix), an even
+// number of blocks per chunk but the last.
+void prefix_chunking(int32_t prefix_blocks, int32_t* chunk_blocks, int32_t* chunks) {
+    const int32_t want = std::max(1, std::min(pkv::kCascadeMaxChunks, prefix_blocks / pkv::kCascadeChunkBlocks));
+    const int32_t per = (prefix_blocks + 2 * want - 1) / (2 * want) * 2;
+    *chunk_blocks = per;
+    *chunks = (prefix_blocks + per - 1) / per;
+}
 
 }  // namespace
 
@@ -356,10 +417,18 @@ size_t block_table_device_bytes(const pkv_pool* pool, const int32_t* host_seq_le
     try {
         if (!pool || !host_seq_lens) return 0;
         Plan P;
-        if (!build_plan(host_seq_lens, num_seqs, max_blocks_per_seq, partition_tokens, pool->desc.num_kv_heads,
-                        pkv::decode_wgs_per_cu(pool->desc.kv_dtype, pool->desc.head_dim), &P))
+        const int32_t wpc = pkv::decode_wgs_per_cu(pool->desc.kv_dtype, pool->desc.head_dim);
+        if (!build_plan(host_seq_lens, num_seqs, max_blocks_per_seq, partition_tokens, pool->desc.num_kv_heads, wpc,
+                        &P))
             return 0;
-        return table_layout(num_seqs, max_blocks_per_seq, pool->desc.num_kv_heads, P).total;
+        // Room for a shared-prefix plan if the tables turn out to share one:
+        // the plan with the smallest prefix is the largest (one unit per
+        // sequence, ids for its longest own run).
+        Plan C;
+        const bool maybe = partition_tokens == -1 && max_prefix_blocks(pool, host_seq_lens, num_seqs) > 0 &&
+                           build_cascade_plan(host_seq_lens, num_seqs, max_blocks_per_seq, pool->desc.num_kv_heads,
+                                              wpc, pkv::kCascadeMinBlocks, 1, &C);
+        return table_layout(num_seqs, max_blocks_per_seq, pool->desc.num_kv_heads, P, maybe ? &C : nullptr).total;
     } catch (...) {
         return 0;
     }
@@ -395,10 +464,29 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
             }
         }
         Plan P;
-        if (!build_plan(host_seq_lens, num_seqs, max_blocks_per_seq, partition_tokens, hkv,
-                        pkv::decode_wgs_per_cu(pool->desc.kv_dtype, pool->desc.head_dim), &P))
+        const int32_t wpc = pkv::decode_wgs_per_cu(pool->desc.kv_dtype, pool->desc.head_dim);
+        if (!build_plan(host_seq_lens, num_seqs, max_blocks_per_seq, partition_tokens, hkv, wpc, &P))
             return PKV_ERR_INVALID;
-        const TableLayout L = table_layout(num_seqs, max_blocks_per_seq, hkv, P);
+        // Shared prefix (balanced plans only: fixed partitions are kept as
+        // asked): the longest run of leading physical blocks that every
+        // sequence's table names alike (at most what the lengths allow).
+        int32_t prefix = partition_tokens == -1 ? max_prefix_blocks(pool, host_seq_lens, num_seqs) : 0;
+        for (int32_t j = 0; j < prefix; ++j) {
+            const int32_t id = host_block_table[j];
+            for (int32_t s = 1; s < num_seqs; ++s) {
+                if (host_block_table[static_cast<int64_t>(s) * max_blocks_per_seq + j] != id) {
+                    prefix = j;
+                    break;
+                }
+            }
+        }
+        if (prefix < pkv::kCascadeMinBlocks) prefix = 0;
+        Plan C;
+        int32_t chunk_blocks = 0, chunks = 0;
+        if (prefix) prefix_chunking(prefix, &chunk_blocks, &chunks);
+        if (prefix && !build_cascade_plan(host_seq_lens, num_seqs, max_blocks_per_seq, hkv, wpc, prefix, chunks, &C))
+            return PKV_ERR_INVALID;
+        const TableLayout L = table_layout(num_seqs, max_blocks_per_seq, hkv, P, prefix ? &C : nullptr);
         if (dev_buffer_bytes < L.total) return PKV_ERR_WORKSPACE;
 
         pkv_table* t = new pkv_table;
@@ -423,6 +511,18 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
         t->d_units = reinterpret_cast<int32_t*>(base + L.units);
         t->d_unit_ids = reinterpret_cast<int32_t*>(base + L.unit_ids);
         t->seq_lens_offset = L.seq_lens;
+        if (prefix) {
+            t->prefix_blocks = prefix;
+            t->prefix_chunks = chunks;
+            t->prefix_chunk_blocks = chunk_blocks;
+            t->c_num_units = C.num_units;
+            t->c_unit_stride = C.stride;
+            t->c_num_split_slots = C.num_split_slots;
+            t->c_max_parts = C.max_parts;
+            t->d_cseq_parts = reinterpret_cast<int32_t*>(base + L.cseq_parts);
+            t->d_cunits = reinterpret_cast<int32_t*>(base + L.cunits);
+            t->d_cunit_ids = reinterpret_cast<int32_t*>(base + L.cunit_ids);
+        }
 
         // One host image of the whole buffer (counters start at zero), copied once.
         t->staging.assign(L.total / sizeof(int32_t), 0);
@@ -432,32 +532,43 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
         std::memcpy(hs + L.seq_lens / 4, host_seq_lens, sizeof(int32_t) * num_seqs);
         std::memcpy(hs + L.seq_parts / 4, P.seq_parts.data(), sizeof(int32_t) * 2 * num_seqs);
         std::memcpy(hs + L.units / 4, P.units.data(), sizeof(int32_t) * P.units.size());
-        // Is any physical block named twice among the used entries (a prefix
-        // shared by several sequences)?  Such a batch reads those blocks once
-        // per reference, and its attention launches keep the cached
-        // tile-load policy instead of streaming.
-        {
+        // Is any physical block named twice among the used entries (from
+        // block `from` on)?  Such a batch reads those blocks once per
+        // reference, and its attention launches keep the cached tile-load
+        // policy instead of streaming.
+        auto any_shared = [&](int32_t from) {
             std::vector<uint8_t> seen(static_cast<size_t>(nb_pool), 0);
-            for (int32_t s = 0; s < num_seqs && !t->shared_blocks; ++s) {
+            for (int32_t s = 0; s < num_seqs; ++s) {
                 const int32_t used = (host_seq_lens[s] + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
                 const int32_t* row = host_block_table + static_cast<int64_t>(s) * max_blocks_per_seq;
-                for (int32_t j = 0; j < used; ++j) {
-                    if (seen[row[j]]) { t->shared_blocks = true; break; }
+                for (int32_t j = from; j < used; ++j) {
+                    if (seen[row[j]]) return true;
                     seen[row[j]] = 1;
                 }
             }
-        }
-        for (int32_t u = 0; u < P.num_units; ++u) {
-            const int32_t* d = &P.units[static_cast<size_t>(u) * pkv::kUnitInts];
-            const int32_t* row = host_block_table + static_cast<int64_t>(d[pkv::kUnitSeq]) * max_blocks_per_seq;
-            int32_t* ids = hs + L.unit_ids / 4 + static_cast<size_t>(u) * P.stride;
-            // processing order j = 0 .. nb-1 walks logical blocks b0 + (j + rot) mod nb;
-            // the tail of the stride repeats the first id
-            const int32_t b0 = d[pkv::kUnitB0], nb = d[pkv::kUnitNb], rot = d[pkv::kUnitRot];
-            for (int32_t j = 0; j < P.stride; ++j) {
-                const int32_t jj = j < nb ? (j + rot) % nb : rot;
-                ids[j] = row[b0 + jj];
+            return false;
+        };
+        t->shared_blocks = any_shared(0);
+        if (prefix) t->c_shared_blocks = any_shared(prefix);
+        // Unit block ids in walking order: j = 0 .. nb-1 visits logical block
+        // b0 + (j + rot) mod nb; the tail of the stride repeats the first id.
+        auto write_ids = [&](const Plan& Q, size_t at) {
+            for (int32_t u = 0; u < Q.num_units; ++u) {
+                const int32_t* d = &Q.units[static_cast<size_t>(u) * pkv::kUnitInts];
+                const int32_t* row = host_block_table + static_cast<int64_t>(d[pkv::kUnitSeq]) * max_blocks_per_seq;
+                int32_t* ids = hs + at / 4 + static_cast<size_t>(u) * Q.stride;
+                const int32_t b0 = d[pkv::kUnitB0], nb = d[pkv::kUnitNb], rot = d[pkv::kUnitRot];
+                for (int32_t j = 0; j < Q.stride; ++j) {
+                    const int32_t jj = j < nb ? (j + rot) % nb : rot;
+                    ids[j] = row[b0 + jj];
+                }
             }
+        };
+        write_ids(P, L.unit_ids);
+        if (prefix) {
+            std::memcpy(hs + L.cseq_parts / 4, C.seq_parts.data(), sizeof(int32_t) * 2 * num_seqs);
+            std::memcpy(hs + L.cunits / 4, C.units.data(), sizeof(int32_t) * C.units.size());
+            write_ids(C, L.cunit_ids);
         }
         hipStream_t st = static_cast<hipStream_t>(stream);
         hipError_t e = hipEventCreateWithFlags(&t->uploaded, hipEventDisableTiming);
@@ -495,6 +606,13 @@ pkv_status block_table_info(const pkv_table* table, int32_t* num_units, int32_t*
     if (max_seq_len) *max_seq_len = table->max_seq_len;
     if (min_seq_len) *min_seq_len = table->min_seq_len;
     if (max_parts) *max_parts = table->max_parts;
+    return PKV_OK;
+}
+
+pkv_status block_table_shared_prefix(const pkv_table* table, int32_t* prefix_blocks, int32_t* prefix_chunks) {
+    if (!table) return PKV_ERR_INVALID;
+    if (prefix_blocks) *prefix_blocks = table->prefix_blocks;
+    if (prefix_chunks) *prefix_chunks = table->prefix_chunks;
     return PKV_OK;
 }
 
@@ -548,7 +666,10 @@ size_t paged_attention_workspace_bytes(const pkv_pool* pool, const pkv_table* ta
     const int32_t hkv = pool->desc.num_kv_heads;
     if (num_q_heads % hkv) return 0;
     const int64_t rows = static_cast<int64_t>(num_q_heads / hkv) * query_rows;
-    const int64_t entries = static_cast<int64_t>(hkv) * table->num_split_slots * rows;
+    // room for the partials of either plan (with a shared prefix, the
+    // shared-prefix plan's whenever a call can use it)
+    const int64_t slots = std::max(table->num_split_slots, table->c_num_split_slots);
+    const int64_t entries = static_cast<int64_t>(hkv) * slots * rows;
     if (entries == 0) return 0;
     const size_t o_bytes = align_up(sizeof(float) * static_cast<size_t>(entries) * pool->desc.head_dim);
     const size_t ml_bytes = align_up(sizeof(float) * static_cast<size_t>(entries));
@@ -591,13 +712,20 @@ pkv_status attention_call(const pkv_pool* pool, int32_t layer, const pkv_table* 
         if (!ok) return PKV_ERR_UNSUPPORTED;
     }
 
+    // The shared-prefix plan applies when every row of every sequence sees
+    // the whole prefix (and tokens appended by this call lie past it).
+    const bool cascade = table->prefix_blocks > 0 &&
+                         static_cast<int64_t>(table->min_seq_len) - query_rows >=
+                             static_cast<int64_t>(table->prefix_blocks) * PKV_BLOCK_SIZE;
+    const int32_t slots = std::max(table->num_split_slots, table->c_num_split_slots);
+
     pkv::AttnArgs a;
     a.pool = pool->base;
     a.k_scale = pool->k_scale;
     a.v_scale = pool->v_scale;
-    a.units = table->d_units;
-    a.unit_ids = table->d_unit_ids;
-    a.seq_parts = table->d_seq_parts;
+    a.units = cascade ? table->d_cunits : table->d_units;
+    a.unit_ids = cascade ? table->d_cunit_ids : table->d_unit_ids;
+    a.seq_parts = cascade ? table->d_cseq_parts : table->d_seq_parts;
     a.counters = table->d_counters;
     a.queue = table->d_queue;
     a.q = dev_q;
@@ -605,7 +733,7 @@ pkv_status attention_call(const pkv_pool* pool, int32_t layer, const pkv_table* 
     a.k_new = k_new;
     a.v_new = v_new;
     a.append_in_f32 = in_dtype == PKV_F32 ? 1 : 0;
-    const int64_t entries = static_cast<int64_t>(hkv) * table->num_split_slots * group * query_rows;
+    const int64_t entries = static_cast<int64_t>(hkv) * slots * group * query_rows;
     uint8_t* ws = static_cast<uint8_t*>(dev_workspace);
     const size_t o_bytes = align_up(sizeof(float) * static_cast<size_t>(entries) * pool->desc.head_dim);
     const size_t ml_bytes = align_up(sizeof(float) * static_cast<size_t>(entries));
@@ -622,15 +750,55 @@ pkv_status attention_call(const pkv_pool* pool, int32_t layer, const pkv_table* 
     a.rows = group * query_rows;
     a.k_rows = query_rows;
     a.head_dim = pool->desc.head_dim;
-    a.unit_stride = table->unit_stride;
-    a.num_items = table->num_units * hkv;
-    a.num_split_slots = table->num_split_slots;
-    a.max_parts = table->max_parts;
+    a.unit_stride = cascade ? table->c_unit_stride : table->unit_stride;
+    const int32_t units = cascade ? table->c_num_units : table->num_units;
+    a.num_items = units * hkv;
+    a.num_split_slots = slots;
+    a.max_parts = cascade ? table->c_max_parts : table->max_parts;
     a.fuse_max_parts = pkv::kFuseMaxParts;
     a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
     a.score_scale = scale * 1.4426950408889634f;
-    const hipError_t err = pkv::launch_attention(a, kv, pool->desc.head_dim, table->num_units,
-                                                 table->shared_blocks, static_cast<hipStream_t>(stream));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (cascade) {
+        // Shared-prefix pass: every sequence's query rows against the prefix
+        // chunks, one partial per (row, chunk) in the sequence's first slots.
+        pkv::PrefillArgs pa;
+        pa.pool = pool->base;
+        pa.k_scale = pool->k_scale;
+        pa.v_scale = pool->v_scale;
+        pa.table = table->d_table;
+        pa.seq_lens = table->d_seq_lens;
+        pa.q = dev_q;
+        pa.out = nullptr;
+        pa.query_start = nullptr;
+        pa.tile_bytes = pool->tile_bytes;
+        pa.layer = layer;
+        pa.num_blocks = pool->desc.num_blocks;
+        pa.num_seqs = table->num_seqs;
+        pa.num_kv_heads = hkv;
+        pa.num_q_heads = num_q_heads;
+        pa.group = group;
+        pa.chunk = query_rows;
+        pa.max_blocks = table->max_blocks;
+        const int64_t tiles = (static_cast<int64_t>(table->num_seqs) * query_rows * group + pkv::kPrefillRows - 1) /
+                              pkv::kPrefillRows;
+        if (tiles * hkv * table->prefix_chunks > INT32_MAX) return PKV_ERR_UNSUPPORTED;
+        pa.row_tiles = static_cast<int32_t>(tiles);
+        pa.out_bf16 = 0;
+        pa.score_scale = a.score_scale;
+        pa.part_o = a.part_o;
+        pa.part_m = a.part_m;
+        pa.part_l = a.part_l;
+        pa.seq_parts = table->d_cseq_parts;
+        pa.num_split_slots = slots;
+        pa.prefix_blocks = table->prefix_blocks;
+        pa.prefix_chunk_blocks = table->prefix_chunk_blocks;
+        pa.prefix_chunks = table->prefix_chunks;
+        const hipError_t e = pkv::launch_prefill(pa, kv, pool->desc.head_dim, st);
+        if (e != hipSuccess) return PKV_ERR_HIP;
+    }
+    const hipError_t err = pkv::launch_attention(a, kv, pool->desc.head_dim, units,
+                                                 cascade ? table->c_shared_blocks : table->shared_blocks, st);
     if (err != hipSuccess) const_cast<pkv_table*>(table)->stale = true;
     return hip_status(err);
 }

@@ -662,22 +662,77 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     }
 
     const bool split = parts > 1;
-    for (int e = tid; e < R * D; e += 64 * kWaves) {
+    // Own (M, L, O) of output element e, merged over the waves.
+    auto own = [&](int e, float& M, float& L, float& O) {
         const int r = e / D;
         const int d = e % D;
-        float M = neg_inf();
+        M = neg_inf();
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m_s[w * R + r]);
-        float L = 0.f;
+        L = 0.f;
         if (M != neg_inf()) {
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) L += l_s[w * R + r] * fast_exp2(m_s[w * R + r] - M);
         }
-        float O = acc_s[r * (D + 1) + d];
+        O = acc_s[r * (D + 1) + d];
         if constexpr (kCopies == kWaves) {
 #pragma unroll
             for (int w = 1; w < kWaves; ++w) O += acc_s[(w * R + r) * (D + 1) + d];
         }
+    };
+    if (split && ud[kUnitTickets] == 1 && parts - 1 <= kCascadeMaxChunks) {
+        // The sequence's only work-group in this launch, its other partials
+        // (slots before this unit's) written by the shared-prefix pass, an
+        // earlier launch: merged here at once, with no partial or ticket of
+        // its own.  Each thread's elements go in batches of kB, every load of
+        // a batch issued before any of its results is used.
+        const int lead = parts - 1;
+        const int64_t sl0 = static_cast<int64_t>(h) * a.num_split_slots + (slot - ud[kUnitPart]);
+        constexpr int kB = 4;
+        for (int e0 = tid; e0 < R * D; e0 += 64 * kWaves * kB) {
+            float pm[kB][kCascadeMaxChunks], pl[kB][kCascadeMaxChunks], po[kB][kCascadeMaxChunks];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const int e = min(e0 + 64 * kWaves * u, R * D - 1);
+                const int r = e / D;
+#pragma unroll
+                for (int c = 0; c < kCascadeMaxChunks; ++c) {
+                    const int64_t sr = (sl0 + min(c, lead - 1)) * R + r;
+                    pm[u][c] = a.part_m[sr];
+                    pl[u][c] = a.part_l[sr];
+                    po[u][c] = a.part_o[sr * D + (e - r * D)];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const int e = e0 + 64 * kWaves * u;
+                if (e >= R * D) break;
+                float Mo, Lo, Oo;
+                own(e, Mo, Lo, Oo);
+                float M = Mo;
+#pragma unroll
+                for (int c = 0; c < kCascadeMaxChunks; ++c)
+                    if (c < lead) M = fmaxf(M, pm[u][c]);
+                const float wo = Mo == neg_inf() ? 0.f : fast_exp2(Mo - M);
+                float L = Lo * wo, O = Oo * wo;
+#pragma unroll
+                for (int c = 0; c < kCascadeMaxChunks; ++c) {
+                    if (c < lead) {
+                        const float wc = fast_exp2(pm[u][c] - M);
+                        L += pl[u][c] * wc;
+                        O += po[u][c] * wc;
+                    }
+                }
+                store_out(a, seq, h, e / D, e % D, O / L * vscale);
+            }
+        }
+        return;
+    }
+    for (int e = tid; e < R * D; e += 64 * kWaves) {
+        const int r = e / D;
+        const int d = e % D;
+        float M, L, O;
+        own(e, M, L, O);
         if (!split) {
             store_out(a, seq, h, r, d, O / L * vscale);
         } else {
@@ -701,7 +756,9 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     if (tid == 0)
         *ticket_s = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (*ticket_s != parts - 1) return;
+    // (the sequence's first partials may come from an earlier shared-prefix
+    // pass: only the work-groups of this launch take tickets)
+    if (*ticket_s != ud[kUnitTickets] - 1) return;
     const int64_t sl0 = static_cast<int64_t>(h) * a.num_split_slots + (slot - ud[kUnitPart]);
     // The partials' (m, l) go to LDS in one parallel pass (every load in
     // flight at once: these loads travel to the coherent level, so a chain of

@@ -19,7 +19,19 @@ constexpr int kUnitPart = 4;     // partition index within the sequence
 constexpr int kUnitParts = 5;    // partitions of the sequence
 constexpr int kUnitSlot = 6;     // partial-result slot (split sequences) or -1
 constexpr int kUnitRot = 7;      // walking-order rotation, seq mod nb
-constexpr int kUnitInts = 8;
+constexpr int kUnitTickets = 8;  // work-groups of the sequence (per KV head) that take a merge ticket
+constexpr int kUnitInts = 9;
+
+// Shared-prefix ("cascade") plan: when every sequence of a batch starts with
+// the same kCascadeMinBlocks or more physical blocks, the prefix is attended
+// once for all sequences' query rows (a dense pass over the shared blocks,
+// cut into prefix chunks of at least kCascadeChunkBlocks blocks, each writing
+// a partial result per row) and the decode kernel walks only each
+// sequence's own blocks, merging the prefix partials with its own.
+constexpr int kCascadeMinBlocks = 8;
+constexpr int kCascadeMinSeqs = 4;
+constexpr int kCascadeChunkBlocks = 32;
+constexpr int kCascadeMaxChunks = 4;
 
 // Sequences with at most this many partitions are merged inside the
 // partition kernel; longer ones by the separate merge kernel.
@@ -151,9 +163,24 @@ struct PrefillArgs {
     int32_t row_tiles;           // ceil(longest chunk * G / kPrefillRows)
     int32_t out_bf16;
     float score_scale;           // softmax scale * log2(e)
+    // Shared-prefix pass of a verify or decode call (part_o non-null): the
+    // k = chunk query rows of every sequence ([B][k][H_q][D] in q) attend to
+    // prefix chunk c, blocks c * prefix_chunk_blocks .. (at most
+    // prefix_blocks) of the first table row, all positions visible; each row
+    // writes its partial (O, m, l) to slot seq_parts[2 s + 1] + c, laid out
+    // as the attention kernel's partials.
+    float* part_o = nullptr;     // [H_kv][slots][R][D]
+    float* part_m = nullptr;     // [H_kv][slots][R]
+    float* part_l = nullptr;
+    const int32_t* seq_parts = nullptr;
+    int32_t num_split_slots = 0;
+    int32_t prefix_blocks = 0;
+    int32_t prefix_chunk_blocks = 0;
+    int32_t prefix_chunks = 0;
 };
 
-// Launch the prefill kernel; kv_dtype is KV_BF16 or KV_FP8, head_dim 64 or 128.
+// Launch the prefill kernel (or, with part_o set, the shared-prefix pass);
+// kv_dtype is any pool code but KV_F32, head_dim 64 or 128.
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, hipStream_t stream);
 
 // Exact speculative acceptance (see speculative.hip).

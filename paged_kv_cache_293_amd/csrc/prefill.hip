@@ -208,7 +208,13 @@ __device__ __forceinline__ void pf_zero_v_tail(uint8_t* stage, int t0, int n, in
     }
 }
 
-template <int KVT, int D>
+// CASCADE: the shared-prefix pass of a verify or decode call instead of a
+// prefill.  Its "chunk" is every query row of the batch (row j of the packed
+// [B * k] tokens is row j mod k of sequence j / k), the visible positions are
+// one prefix chunk's blocks of the first table row, all of them visible to
+// every row, and each row writes its unnormalised partial result (O, m, l) to
+// the split-KV slot of that prefix chunk instead of an output.
+template <int KVT, int D, bool CASCADE>
 __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_kernel(PrefillArgs a) {
     using Gm = PfGeom<KVT, D>;
@@ -219,33 +225,46 @@ void attn_prefill_kernel(PrefillArgs a) {
     const int lg = lane >> 4;
     const int col = lane & 15;
 
-    // Work-group -> (sequence, KV head, row tile).
+    // Work-group -> (sequence, KV head, row tile); for the prefix pass
+    // (prefix chunk, KV head, row tile).
     const int H = a.num_kv_heads;
     const int RT = a.row_tiles;
-    const int pairs_sh = a.num_seqs * H;
+    const int pairs_sh = (CASCADE ? a.prefix_chunks : a.num_seqs) * H;
     const int grp = blockIdx.x / (kPfXcds * RT);
     const int r = blockIdx.x - grp * kPfXcds * RT;
     const int in_group = min(kPfXcds, pairs_sh - grp * kPfXcds);
     const int sh = grp * kPfXcds + r % in_group;
     const int rt = RT - 1 - r / in_group;
-    const int s = sh / H;
-    const int h = sh - s * H;
+    const int s = CASCADE ? 0 : sh / H;         // the prefix pass reads the first table row
+    const int pc = CASCADE ? sh / H : 0;        // prefix chunk
+    const int h = sh - (sh / H) * H;
+    const int blk0 = pc * a.prefix_chunk_blocks;   // first block of the prefix chunk
 
-    const int n = a.seq_lens[s];
-    // The sequence's chunk: C tokens whose queries (and outputs) are rows
-    // q0 .. q0 + C - 1 of the packed arrays.
-    const int q0 = a.query_start ? a.query_start[s] : s * a.chunk;
-    const int C = a.query_start ? a.query_start[s + 1] - q0 : a.chunk;
     const int G = a.group;
+    int n, q0, C, first;
+    if constexpr (CASCADE) {
+        n = kBlock * min(a.prefix_blocks - blk0, a.prefix_chunk_blocks);
+        q0 = 0;
+        C = a.num_seqs * a.chunk;
+        first = 0;
+    } else {
+        n = a.seq_lens[s];
+        // The sequence's chunk: C tokens whose queries (and outputs) are rows
+        // q0 .. q0 + C - 1 of the packed arrays.
+        q0 = a.query_start ? a.query_start[s] : s * a.chunk;
+        C = a.query_start ? a.query_start[s + 1] - q0 : a.chunk;
+        first = n - C;                          // position of chunk token 0
+    }
     const int Rt = C * G;                       // query rows of this (sequence, KV head)
-    const int first = n - C;                    // position of chunk token 0
     const int row_wg = rt * kPrefillRows;
     if (row_wg >= Rt) return;                   // a row tile past a shorter chunk (the whole work-group)
     const int last_row = min(Rt, row_wg + kPrefillRows) - 1;
-    const int nblk = (first + last_row / G + kBlock) / kBlock;   // blocks the tile's last row sees
+    // blocks the tile's last row sees
+    const int nblk = CASCADE ? n / kBlock : (first + last_row / G + kBlock) / kBlock;
     const int npair = (nblk + 1) >> 1;
     const int row_w = row_wg + wave * 16 * kPfNT;
-    const int lim_lo = row_w < Rt ? first + row_w / G + 1 : 0;  // fewest positions a row of this wave sees
+    // fewest positions a row of this wave sees
+    const int lim_lo = CASCADE ? n : (row_w < Rt ? first + row_w / G + 1 : 0);
 
     float sscale = a.score_scale;
     float vscale = 1.f;
@@ -265,7 +284,7 @@ void attn_prefill_kernel(PrefillArgs a) {
         const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) +
             ((static_cast<int64_t>(q0) + j) * a.num_q_heads + h * G + g) * D;
         qr[c].load(qrow, valid, lane);
-        lim[c] = valid ? first + j + 1 : 0;
+        lim[c] = CASCADE ? n : (valid ? first + j + 1 : 0);
     }
     // int4: kI4Bias times each query row's sum (the bias of its scores)
     float qbias[kPfNT];
@@ -290,7 +309,7 @@ void attn_prefill_kernel(PrefillArgs a) {
     const int64_t block_stride = static_cast<int64_t>(H) * 2 * a.tile_bytes;
     const uint8_t* head_base = a.pool + static_cast<int64_t>(a.layer) * a.num_blocks * block_stride +
                                static_cast<int64_t>(h) * 2 * a.tile_bytes;
-    const int32_t* trow = a.table + static_cast<int64_t>(s) * a.max_blocks;
+    const int32_t* trow = a.table + static_cast<int64_t>(s) * a.max_blocks + blk0;
 
     // Block ids come straight from the table through scalar loads (the row is
     // uniform over the work-group and read-only during the kernel), the ids
@@ -334,7 +353,7 @@ void attn_prefill_kernel(PrefillArgs a) {
 
         uint8_t* st = pf_smem + (p % kPfStages) * Gm::PAIR;
         const int t0 = 32 * p;
-        if (KVT != KV_INT4 && t0 + 32 > n) {
+        if (!CASCADE && KVT != KV_INT4 && t0 + 32 > n) {
             // only the last pair reaches past the sequence end; nothing is in
             // flight (every int4 nibble is a finite value: no zeroing needed)
             pf_zero_v_tail<KVT, D>(st, t0, n, tid);
@@ -427,6 +446,21 @@ void attn_prefill_kernel(PrefillArgs a) {
         if (row >= Rt) continue;
         const int j = row / G;
         const int g = row - j * G;
+        if constexpr (CASCADE) {
+            // partial of row jr * G + g of sequence sq, in the prefix chunk's slot
+            const int sq = j / a.chunk;
+            const int R = a.chunk * G;
+            const int rr = (j - sq * a.chunk) * G + g;
+            const int64_t sl = static_cast<int64_t>(h) * a.num_split_slots + a.seq_parts[2 * sq + 1] + pc;
+            float* po = a.part_o + (sl * R + rr) * D + 4 * lg;
+#pragma unroll
+            for (int m = 0; m < D / 16; ++m) *reinterpret_cast<f32x4*>(po + 16 * m) = o[c][m];
+            if (lg == 0) {
+                a.part_m[sl * R + rr] = m_run[c];
+                a.part_l[sl * R + rr] = l;
+            }
+            continue;
+        }
         const float inv = vscale / l;
         const int64_t base = ((static_cast<int64_t>(q0) + j) * a.num_q_heads + h * G + g) * D + 4 * lg;
 #pragma unroll
@@ -444,9 +478,14 @@ void attn_prefill_kernel(PrefillArgs a) {
 
 template <int KVT, int D>
 hipError_t launch_pf(const PrefillArgs& a, hipStream_t stream) {
-    const int grid = a.num_seqs * a.num_kv_heads * a.row_tiles;
     constexpr size_t lds = PfGeom<KVT, D>::LDS;
-    hipLaunchKernelGGL((attn_prefill_kernel<KVT, D>), dim3(grid), dim3(64 * kPfWaves), lds, stream, a);
+    if (a.part_o) {
+        const int grid = a.prefix_chunks * a.num_kv_heads * a.row_tiles;
+        hipLaunchKernelGGL((attn_prefill_kernel<KVT, D, true>), dim3(grid), dim3(64 * kPfWaves), lds, stream, a);
+    } else {
+        const int grid = a.num_seqs * a.num_kv_heads * a.row_tiles;
+        hipLaunchKernelGGL((attn_prefill_kernel<KVT, D, false>), dim3(grid), dim3(64 * kPfWaves), lds, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -1,0 +1,139 @@
+"""GPU: the shared-prefix plan.  A balanced upload (partition_tokens = -1)
+whose tables all start with the same physical blocks attends to that prefix
+once for every sequence's query rows (the prefix pass) and walks each
+sequence's own blocks in one partition merged with the prefix partials.
+
+Covered: which tables get a prefix (its length, the chunk count, the
+refusals: fixed partitions, fewer than 4 sequences, a float32 pool, a prefix
+under 8 blocks), parity with the oracle over every dtype, both head dims,
+decode and verify rows, prefix chunks of even and odd block counts and the
+shortest sequence ending right where the rows still see the whole prefix; a
+call whose rows reach into the prefix (the plan then is not used) on the same
+table as a call that uses it; agreement with an upload without the plan."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_setup import Setup, assert_close, log, out_values
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefix_workload(kv, d, Hq, Hkv, k, prefix_blocks, B, seed, exact_min=True):
+    """B sequences sharing prefix_blocks leading blocks, private suffixes of
+    k .. k + 300 tokens (the first sequence's exactly k when exact_min: its
+    rows then see the whole prefix and nothing before the appended rows)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    suffix = rng.integers(k, k + 300, size=B, endpoint=True)
+    if exact_min:
+        suffix[0] = k
+    lens = 16 * prefix_blocks + suffix
+    return workloads.build(f"prefix-{kv}", seed, rng, lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
+                           kv_dtype=kv, k_rows=k, shared_prefix_tokens=16 * prefix_blocks,
+                           materialize=True, partition_tokens=-1)
+
+
+def _chunks(prefix_blocks):
+    want = max(1, min(4, prefix_blocks // 32))
+    per = -(-prefix_blocks // (2 * want)) * 2
+    return -(-prefix_blocks // per)
+
+
+CASES = [
+    # kv, d, Hq, Hkv, k, prefix blocks, batch
+    ("bf16", 128, 32, 8, 1, 75, 6),     # decode; chunks of 38 and 37 blocks
+    ("fp8", 128, 32, 8, 5, 128, 8),     # the verify shape over a 2048-token prefix, 4 chunks
+    ("int8", 64, 16, 2, 3, 40, 5),      # one chunk
+    ("int4", 128, 32, 8, 5, 8, 4),      # the smallest prefix and batch
+    ("int4", 64, 8, 8, 2, 97, 7),       # chunks of 34, 34 and 29 blocks
+    ("bf16", 64, 64, 8, 1, 33, 9),      # 8 query heads per KV head, one odd chunk
+    ("fp8", 64, 8, 1, 8, 64, 5),        # one KV head, 64 rows per sequence
+]
+
+
+@pytest.mark.parametrize("kv,d,Hq,Hkv,k,pb,B", CASES)
+def test_shared_prefix_parity(kv, d, Hq, Hkv, k, pb, B):
+    log(f"shared prefix {kv} d{d} {Hq}/{Hkv} k={k} prefix {pb} blocks, batch {B}")
+    w = _prefix_workload(kv, d, Hq, Hkv, k, pb, B, seed=2930 + pb)
+    s = Setup(w, partition_tokens=-1)
+    assert s.table.shared_prefix() == (pb, _chunks(pb))
+    got = s.run()
+    ref = s.oracle()
+    err = assert_close(out_values(got), ref, kv, "shared-prefix plan")
+    # the same batch without the plan (fixed partitions)
+    plain = s.upload(64)
+    assert plain.shared_prefix() == (0, 0)
+    other = s.run(table=plain)
+    err2 = assert_close(out_values(other), ref, kv, "fixed partitions")
+    log(f"  max abs err {err:.2e} (fixed partitions {err2:.2e})")
+
+
+def test_rows_reaching_into_the_prefix_use_the_plain_plan():
+    """The shortest sequence has 2 positions past a 20-block prefix: a
+    5-row verify call reaches into the prefix (the plan is not used), a
+    decode call on the same table uses it; both match the oracle."""
+    log("shared prefix not used by rows that reach into it")
+    w = _prefix_workload("bf16", 128, 32, 8, 5, 20, 6, seed=29301, exact_min=False)
+    w.seq_lens[2] = 16 * 20 + 2
+    # the builder wrote sequence 2's positions for its original length; its
+    # table row covers the shorter length as well
+    s = Setup(w, partition_tokens=-1)
+    assert s.table.shared_prefix() == (20, 1)
+    got = s.run()
+    assert_close(out_values(got), s.oracle(), "bf16", "verify reaching into the prefix")
+    # decode on the same table: the last row of every sequence
+    import paged_kv_cache_293_amd as pk
+    q1 = s.q[:, -1].contiguous()
+    out1 = pk.paged_attention_decode(s.pool, w.layer, s.table, q1, w.scale)
+    torch.cuda.synchronize()
+    ref = s.oracle()[:, -1]
+    assert_close(out_values(out1), ref, "bf16", "decode with the shared-prefix plan")
+
+
+def test_which_tables_get_a_prefix():
+    import paged_kv_cache_293_amd as pk
+    log("shared prefix detection")
+    w = _prefix_workload("bf16", 64, 8, 2, 1, 20, 5, seed=29302)
+    s = Setup(w, partition_tokens=-1)
+    assert s.table.shared_prefix() == (20, 1)
+    # fixed partitions and whole sequences keep no prefix
+    assert s.upload(128).shared_prefix() == (0, 0)
+    assert s.upload(0).shared_prefix() == (0, 0)
+    # one row naming another block at block 12 shortens the prefix to 12 blocks
+    free = np.setdiff1d(np.arange(w.num_blocks), w.block_tables[w.block_tables >= 0])
+    bt = w.block_tables.copy()
+    bt[3, 12] = free[0]
+    t = pk.block_table_upload(s.pool, bt, w.seq_lens, -1)
+    assert t.shared_prefix() == (12, 1)
+    # ... at block 7: under the 8-block minimum
+    bt = w.block_tables.copy()
+    bt[4, 7] = free[1]
+    assert pk.block_table_upload(s.pool, bt, w.seq_lens, -1).shared_prefix() == (0, 0)
+    # three sequences are too few
+    assert pk.block_table_upload(s.pool, w.block_tables[:3], w.seq_lens[:3], -1).shared_prefix() == (0, 0)
+    # a float32 pool takes no prefix pass
+    f32 = pk.kv_pool_create(1, w.num_blocks, 2, 64, "f32")
+    assert pk.block_table_upload(f32, w.block_tables, w.seq_lens, -1).shared_prefix() == (0, 0)
+    # the prefix stops one position short of the shortest sequence's end
+    lens = w.seq_lens.copy()
+    lens[1] = 16 * 10 + 1
+    assert pk.block_table_upload(s.pool, w.block_tables, lens, -1).shared_prefix() == (10, 1)
+    lens[1] = 16 * 10
+    assert pk.block_table_upload(s.pool, w.block_tables, lens, -1).shared_prefix() == (9, 1)
+
+
+def test_shared_prefix_reduced_verify_config():
+    """The reduced prefix-shared verify config through the plan, every
+    output against the oracle, twice in a row (the merge counters are left
+    at zero)."""
+    log("shared prefix c5s")
+    w = workloads.make("c5s")
+    s = Setup(w, partition_tokens=-1)
+    assert s.table.shared_prefix() == (16, 1)
+    ref = s.oracle()
+    a = s.run()
+    b = s.run()
+    assert torch.equal(a, b)
+    assert_close(out_values(a), ref, w.kv_dtype, "c5s shared prefix")
