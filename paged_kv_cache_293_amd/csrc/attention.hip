@@ -183,6 +183,18 @@ __host__ __device__ inline int acc_area_floats(int rows, int d, int k_rows, int 
     return a > b ? a : b;
 }
 
+// Output copies of the wave merge: one per wave up to 32 rows (the waves
+// write at once), one shared copy beyond (the waves add in turn).
+constexpr int wave_copies(int nt) { return nt <= 2 ? kWaves : 1; }
+
+// Dynamic LDS of the partition kernel: the accumulator area, the waves' (m, l),
+// the (m, l) of up to kCascadeMaxChunks shared-prefix partials per row and
+// the output phase's row factors (8 per row).
+__host__ __device__ inline size_t partition_lds_bytes(int rows, int d, int k_rows, int stage_bytes, int copies) {
+    return (static_cast<size_t>(acc_area_floats(rows, d, k_rows, stage_bytes, copies)) + 2 * kWaves * rows +
+            2 * kCascadeMaxChunks * rows + 8 * rows) * sizeof(float);
+}
+
 // ------------------------------------------------------- partition kernel
 // One (unit, KV head) item: attend over the unit's blocks with the work-group's
 // four waves, merge the waves, then write the output (unsplit sequence) or the
@@ -196,9 +208,10 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     float* acc_s = smem;                       // [R][D + 1] merged unnormalised output
     uint8_t* stage = reinterpret_cast<uint8_t*>(smem);   // appended tokens, during the block walk
     // One-row-tile instances give every wave its own output copy to merge.
-    constexpr int kCopies = NT == 1 ? kWaves : 1;
+    constexpr int kCopies = wave_copies(NT);
     float* m_s = smem + acc_area_floats(R, D, a.k_rows, STOK, kCopies);   // [W][R]
     float* l_s = m_s + kWaves * R;             // [W][R]
+    float* pre_s = l_s + kWaves * R;           // [2][kCascadeMaxChunks * R] prefix partials' m, then l
 
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -217,6 +230,8 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     const int parts = ud[kUnitParts];
     const int slot = ud[kUnitSlot];
     const int rot = ud[kUnitRot];
+    const int part = ud[kUnitPart];
+    const int tickets = ud[kUnitTickets];
     const int G = a.group;
     const int kq = a.k_rows;
 
@@ -377,7 +392,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     // all reading the same block at the same moment.  A wave walks j = wave,
     // wave + 4, ... in chunks of up to 64 blocks (one block id per lane).
     auto logical = [&](int j) { const int x = j + rot; return b0 + (x >= nb ? x - nb : x); };
-    constexpr bool deep = NT == 1 && decode_depth(KVT, D) == 2;
+    constexpr int NBUF = decode_buffers(KVT, D, NT);   // tiles a wave holds: NBUF - 1 in flight
     int base = wave;
     int cnt = 0;
     int id = 0;
@@ -390,8 +405,8 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
         t.template load<POL>(tile_rsrc(head_base + static_cast<int64_t>(pid) * block_stride, valid ? a.tile_bytes : 0),
                              koff, voff);
     };
-    TileRegs<KVT, D> ta, tb, tc;
-    // First loads of a chunk: one block in flight, two with three buffers.
+    TileRegs<KVT, D> tr[NBUF];
+    // First loads of a chunk: NBUF - 1 blocks in flight.
     // A wave without blocks (cnt = 0) issues them through zero-sized
     // resources, so the first chunk's loads are issued on every path.
     auto begin_chunk = [&]() {
@@ -402,8 +417,8 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             if (base + kWaves * lane < a.unit_stride) id = uids[base + kWaves * lane];
         }
         id = min(max(id, 0), a.num_blocks - 1);
-        issue(ta, 0, cnt > 0);
-        if constexpr (deep) issue(tb, 1, cnt > 1);
+#pragma unroll
+        for (int b = 0; b < NBUF - 1; ++b) issue(tr[b], b, cnt > b);
     };
     // Fused append (paged_attention_append): the k newest positions n-k ..
     // n-1 of the sequence are written into the pool, for this KV head, by the
@@ -500,31 +515,19 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     }
 
     while (base < nb) {
-        if constexpr (deep) {
-            // Three buffers: while a wave processes one block the next two
-            // are in flight.
-            int i = 0;
-            for (; i + 2 < cnt; i += 3) {
-                issue(tc, i + 2, true);
-                process(ta, logical(base + kWaves * i));
-                issue(ta, i + 3, i + 3 < cnt);
-                process(tb, logical(base + kWaves * (i + 1)));
-                issue(tb, i + 4, i + 4 < cnt);
-                process(tc, logical(base + kWaves * (i + 2)));
+        // NBUF buffers in rotation: before block i + b is processed, block
+        // i + b + NBUF - 1 is issued into the buffer block i + b - 1 left.
+        int i = 0;
+        for (; i + NBUF - 1 < cnt; i += NBUF) {
+#pragma unroll
+            for (int b = 0; b < NBUF; ++b) {
+                issue(tr[(b + NBUF - 1) % NBUF], i + b + NBUF - 1, b == 0 || i + b + NBUF - 1 < cnt);
+                process(tr[b], logical(base + kWaves * (i + b)));
             }
-            if (i < cnt) process(ta, logical(base + kWaves * i));
-            if (i + 1 < cnt) process(tb, logical(base + kWaves * (i + 1)));
-        } else {
-            // Two buffers: one block in flight while the other is processed.
-            int i = 0;
-            for (; i + 1 < cnt; i += 2) {
-                issue(tb, i + 1, true);
-                process(ta, logical(base + kWaves * i));
-                issue(ta, i + 2, i + 2 < cnt);
-                process(tb, logical(base + kWaves * (i + 1)));
-            }
-            if (i < cnt) process(ta, logical(base + kWaves * i));
         }
+#pragma unroll
+        for (int b = 0; b < NBUF - 1; ++b)
+            if (i + b < cnt) process(tr[b], logical(base + kWaves * (i + b)));
         base += 64 * kWaves;
         if (base < nb) begin_chunk();
     }
@@ -601,8 +604,56 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
 
     // This work-group's blocks are read: claim its next item now, while the
     // waves merge, so work-groups that finish early take more items.
-    if (tid == 0 && a.num_items > static_cast<int>(gridDim.x))
-        claimed = __hip_atomic_fetch_add(a.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // (The offset, zero, is hidden from the optimiser: with a visibly uniform
+    // address it turns the add into a wave-wide scan whose result it waits
+    // for at once, behind every load in flight.)
+    if (tid == 0 && a.num_items > static_cast<int>(gridDim.x)) {
+        int zero = 0;
+        asm volatile("" : "+v"(zero));
+        claimed = __hip_atomic_fetch_add(a.queue + zero, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ------------------------------------------------------------ output
+    // The output phase works on groups of 4 dims: group q is row q / (D / 4),
+    // dims 4 (q % (D / 4)) .. +3.  A sequence with one partition writes its
+    // output; a split one its partial result (O, m, l), and the last of its
+    // work-groups to take a ticket merges all partials.  A sequence whose
+    // only work-group in this launch is this one, its other partials (the
+    // slots before this unit's) written by the shared-prefix pass, an
+    // earlier launch, is merged here at once, with no partial or ticket of
+    // its own; the loads of those partials go out before the waves merge
+    // (up to two row tiles), so they travel meanwhile.
+    const int lead = parts - 1;
+    const bool split = parts > 1;
+    const bool direct = split && tickets == 1 && lead <= kCascadeMaxChunks;
+    const int64_t first_slot = static_cast<int64_t>(h) * a.num_split_slots + (slot - part);
+    constexpr int Q = D / 4;                   // groups per row
+    const int groups = R * Q;
+    constexpr int kG = 4;                      // groups per thread and batch of prefix loads
+    constexpr bool kEarly = NT <= 2;
+    f32x4 po[kG][kCascadeMaxChunks];
+    // Buffer resources over the sequence's prefix partials (O, then m and l).
+    const __amdgpu_buffer_rsrc_t pre_o = __builtin_amdgcn_make_buffer_rsrc(
+        direct ? a.part_o + first_slot * R * D : a.part_o, 0, direct ? lead * R * D * 4 : 0, 0x00020000);
+    auto load_prefix = [&](int q0) {
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+            const int q = min(q0 + 64 * kWaves * u, groups - 1);
+            const int r = q / Q;
+#pragma unroll
+            for (int c = 0; c < kCascadeMaxChunks; ++c)
+                po[u][c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    pre_o, ((min(c, lead - 1) * R + r) * D + 4 * (q - r * Q)) * 4, 0, 0));
+        }
+    };
+    float pre_m = 0.f, pre_l = 0.f;
+    if (direct) {
+        if (tid < lead * R) {
+            pre_m = a.part_m[first_slot * R + tid];
+            pre_l = a.part_l[first_slot * R + tid];
+        }
+        if constexpr (kEarly) load_prefix(tid);
+    }
 
     // Merge the waves: publish (m, l), rescale O to the common max, add in LDS.
 #pragma unroll
@@ -633,12 +684,15 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     if constexpr (kCopies == kWaves) {
         // Every wave writes its rescaled output to its own copy; the output
         // loop adds the copies in wave order.
-        if (col < R) {
-            float* dst = acc_s + (wave * R + col) * (D + 1) + 4 * lg;
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            const int row = 16 * c + col;
+            if (row >= R) continue;
+            float* dst = acc_s + (wave * R + row) * (D + 1) + 4 * lg;
 #pragma unroll
             for (int m = 0; m < D / 16; ++m)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dst[16 * m + i] = o[0][m][i] * f[0];
+                for (int i = 0; i < 4; ++i) dst[16 * m + i] = o[c][m][i] * f[c];
         }
         lds_barrier();
     } else {
@@ -661,90 +715,129 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
         }
     }
 
-    const bool split = parts > 1;
-    // Own (M, L, O) of output element e, merged over the waves.
-    auto own = [&](int e, float& M, float& L, float& O) {
-        const int r = e / D;
-        const int d = e % D;
-        M = neg_inf();
+    // Row factors, one thread per row: the waves' common max M and sum L
+    // (the copies in acc_s are already relative to M); with prefix partials
+    // the max over those too, their weights and the final scale.
+    float* row_s = pre_s + 2 * kCascadeMaxChunks * R;   // [R][8]
+    if (direct) {
+        if (tid < lead * R) {
+            pre_s[tid] = pre_m;
+            pre_s[kCascadeMaxChunks * R + tid] = pre_l;
+        }
+        lds_barrier();
+    }
+    if (tid < R) {
+        const int r = tid;
+        float M = neg_inf();
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m_s[w * R + r]);
-        L = 0.f;
+        float L = 0.f;
         if (M != neg_inf()) {
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) L += l_s[w * R + r] * fast_exp2(m_s[w * R + r] - M);
         }
-        O = acc_s[r * (D + 1) + d];
+        if (direct) {
+            float Mx = M;
+#pragma unroll
+            for (int c = 0; c < kCascadeMaxChunks; ++c)
+                if (c < lead) Mx = fmaxf(Mx, pre_s[c * R + r]);
+            const float so = M == neg_inf() ? 0.f : fast_exp2(M - Mx);
+            float Lx = L * so;
+            float wc[kCascadeMaxChunks];
+#pragma unroll
+            for (int c = 0; c < kCascadeMaxChunks; ++c) {
+                wc[c] = c < lead ? fast_exp2(pre_s[c * R + r] - Mx) : 0.f;
+                if (c < lead) Lx += pre_s[kCascadeMaxChunks * R + c * R + r] * wc[c];
+            }
+            const float inv = vscale / Lx;
+            row_s[8 * r] = so * inv;
+#pragma unroll
+            for (int c = 0; c < kCascadeMaxChunks; ++c) row_s[8 * r + 1 + c] = wc[c] * inv;
+        } else if (!split) {
+            row_s[8 * r] = vscale / L;
+        } else {
+            row_s[8 * r] = M;
+            row_s[8 * r + 1] = L;
+        }
+    }
+    lds_barrier();
+
+    // Own output of group (r, dq), summed over the wave copies.
+    auto own4 = [&](int r, int dq) {
+        const float* src = acc_s + r * (D + 1) + 4 * dq;
+        f32x4 O = {src[0], src[1], src[2], src[3]};
         if constexpr (kCopies == kWaves) {
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w) O += acc_s[(w * R + r) * (D + 1) + d];
+            for (int w = 1; w < kWaves; ++w) {
+                const float* sw = acc_s + (w * R + r) * (D + 1) + 4 * dq;
+                O += f32x4{sw[0], sw[1], sw[2], sw[3]};
+            }
+        }
+        return O;
+    };
+    // Final output of group (r, dq): one 8- or 16-byte store when the output
+    // array is 16-byte aligned.
+    const bool vec_out = (reinterpret_cast<uintptr_t>(a.out) & 15) == 0;
+    auto store4 = [&](int r, int dq, const f32x4& v) {
+        if (vec_out) {
+            const int jr = r / G;
+            const int g = r - jr * G;
+            const int64_t oi =
+                ((static_cast<int64_t>(seq) * kq + jr) * a.num_q_heads + h * G + g) * D + 4 * dq;
+            if (a.out_bf16)
+                *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + oi) =
+                    u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            else
+                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + oi) = v;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) store_out(a, seq, h, r, 4 * dq + i, v[i]);
         }
     };
-    if (split && ud[kUnitTickets] == 1 && parts - 1 <= kCascadeMaxChunks) {
-        // The sequence's only work-group in this launch, its other partials
-        // (slots before this unit's) written by the shared-prefix pass, an
-        // earlier launch: merged here at once, with no partial or ticket of
-        // its own.  Each thread's elements go in batches of kB, every load of
-        // a batch issued before any of its results is used.
-        const int lead = parts - 1;
-        const int64_t sl0 = static_cast<int64_t>(h) * a.num_split_slots + (slot - ud[kUnitPart]);
-        constexpr int kB = 4;
-        for (int e0 = tid; e0 < R * D; e0 += 64 * kWaves * kB) {
-            float pm[kB][kCascadeMaxChunks], pl[kB][kCascadeMaxChunks], po[kB][kCascadeMaxChunks];
+
+    if (direct) {
+        for (int q0 = tid; q0 < groups; q0 += 64 * kWaves * kG) {
+            if (!kEarly || q0 != tid) load_prefix(q0);
 #pragma unroll
-            for (int u = 0; u < kB; ++u) {
-                const int e = min(e0 + 64 * kWaves * u, R * D - 1);
-                const int r = e / D;
-#pragma unroll
-                for (int c = 0; c < kCascadeMaxChunks; ++c) {
-                    const int64_t sr = (sl0 + min(c, lead - 1)) * R + r;
-                    pm[u][c] = a.part_m[sr];
-                    pl[u][c] = a.part_l[sr];
-                    po[u][c] = a.part_o[sr * D + (e - r * D)];
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kB; ++u) {
-                const int e = e0 + 64 * kWaves * u;
-                if (e >= R * D) break;
-                float Mo, Lo, Oo;
-                own(e, Mo, Lo, Oo);
-                float M = Mo;
+            for (int u = 0; u < kG; ++u) {
+                const int q = q0 + 64 * kWaves * u;
+                if (q >= groups) break;
+                const int r = q / Q;
+                const float* rf = row_s + 8 * r;
+                f32x4 O = own4(r, q - r * Q) * rf[0];
 #pragma unroll
                 for (int c = 0; c < kCascadeMaxChunks; ++c)
-                    if (c < lead) M = fmaxf(M, pm[u][c]);
-                const float wo = Mo == neg_inf() ? 0.f : fast_exp2(Mo - M);
-                float L = Lo * wo, O = Oo * wo;
-#pragma unroll
-                for (int c = 0; c < kCascadeMaxChunks; ++c) {
-                    if (c < lead) {
-                        const float wc = fast_exp2(pm[u][c] - M);
-                        L += pl[u][c] * wc;
-                        O += po[u][c] * wc;
-                    }
-                }
-                store_out(a, seq, h, e / D, e % D, O / L * vscale);
+                    if (c < lead) O += po[u][c] * rf[1 + c];
+                store4(r, q - r * Q, O);
             }
         }
         return;
     }
-    for (int e = tid; e < R * D; e += 64 * kWaves) {
-        const int r = e / D;
-        const int d = e % D;
-        float M, L, O;
-        own(e, M, L, O);
-        if (!split) {
-            store_out(a, seq, h, r, d, O / L * vscale);
-        } else {
-            const int64_t sl = static_cast<int64_t>(h) * a.num_split_slots + slot;
-            xwg_store(a.part_o + (sl * R + r) * D + d, O);
-            if (d == 0) {
-                xwg_store(a.part_m + sl * R + r, M);
-                xwg_store(a.part_l + sl * R + r, L);
-            }
+    if (!split) {
+        for (int q = tid; q < groups; q += 64 * kWaves) {
+            const int r = q / Q;
+            store4(r, q - r * Q, own4(r, q - r * Q) * row_s[8 * r]);
+        }
+        return;
+    }
+
+    // Partial result of this unit: O with agent-coherent (sc1) 16-byte
+    // stores, m and l by the row threads.
+    {
+        const int64_t sl = static_cast<int64_t>(h) * a.num_split_slots + slot;
+        const __amdgpu_buffer_rsrc_t po_r =
+            __builtin_amdgcn_make_buffer_rsrc(a.part_o + sl * R * D, 0, R * D * 4, 0x00020000);
+        for (int q = tid; q < groups; q += 64 * kWaves) {
+            const int r = q / Q;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, own4(r, q - r * Q)), po_r,
+                                                   (r * D + 4 * (q - r * Q)) * 4, 0, kCoherent);
+        }
+        if (tid < R) {
+            xwg_store(a.part_m + sl * R + tid, row_s[8 * tid]);
+            xwg_store(a.part_l + sl * R + tid, row_s[8 * tid + 1]);
         }
     }
-    if (!split || parts > a.fuse_max_parts) return;
+    if (parts > a.fuse_max_parts) return;
 
     // Split-KV merge in the kernel: the last of the sequence's work-groups
     // (for this KV head) to take a ticket combines all partials.  Every thread
@@ -758,8 +851,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     __syncthreads();
     // (the sequence's first partials may come from an earlier shared-prefix
     // pass: only the work-groups of this launch take tickets)
-    if (*ticket_s != ud[kUnitTickets] - 1) return;
-    const int64_t sl0 = static_cast<int64_t>(h) * a.num_split_slots + (slot - ud[kUnitPart]);
+    if (*ticket_s != tickets - 1) return;
     // The partials' (m, l) go to LDS in one parallel pass (every load in
     // flight at once: these loads travel to the coherent level, so a chain of
     // them would cost a round trip each); acc_s is free now and holds
@@ -768,8 +860,8 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     float* pw = acc_s + parts * R;    // [parts][R] sums
     float* Lr = m_s;                  // [R] common sum of each row
     for (int e = tid; e < parts * R; e += 64 * kWaves) {
-        pm[e] = xwg_load(a.part_m + sl0 * R + e);
-        pw[e] = xwg_load(a.part_l + sl0 * R + e);
+        pm[e] = xwg_load(a.part_m + first_slot * R + e);
+        pw[e] = xwg_load(a.part_l + first_slot * R + e);
     }
     __syncthreads();
     for (int r = tid; r < R; r += 64 * kWaves) {
@@ -781,23 +873,27 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             L += pw[q * R + r] * wq;
             pm[q * R + r] = wq;       // weight of partition q for row r
         }
-        Lr[r] = L;
+        Lr[r] = vscale / L;
     }
     __syncthreads();
-    for (int e = tid; e < R * D; e += 64 * kWaves) {
-        const int r = e / D;
-        const int d = e % D;
-        float O = 0.f;
-        for (int q0 = 0; q0 < parts; q0 += 8) {
-            float v[8];
+    // Partials' O: 16-byte coherent loads, 8 partitions in flight per group.
+    const __amdgpu_buffer_rsrc_t all_o =
+        __builtin_amdgcn_make_buffer_rsrc(a.part_o + first_slot * R * D, 0, parts * R * D * 4, 0x00020000);
+    for (int q = tid; q < groups; q += 64 * kWaves) {
+        const int r = q / Q;
+        const int off = (r * D + 4 * (q - r * Q)) * 4;
+        f32x4 O = {0.f, 0.f, 0.f, 0.f};
+        for (int p0 = 0; p0 < parts; p0 += 8) {
+            f32x4 v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                v[u] = q0 + u < parts ? xwg_load(a.part_o + ((sl0 + q0 + u) * R + r) * D + d) : 0.f;
+                v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    all_o, off + min(p0 + u, parts - 1) * R * D * 4, 0, kCoherent));
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (q0 + u < parts) O += v[u] * pm[(q0 + u) * R + r];
+                if (p0 + u < parts) O += v[u] * pm[(p0 + u) * R + r];
         }
-        store_out(a, seq, h, r, d, O / Lr[r] * vscale);
+        store4(r, q - r * Q, O * Lr[r]);
     }
     if (tid == 0)   // ready for the next call
         __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -936,9 +1032,7 @@ int resident_work_groups() {
     static int per_cu = 0;   // same for every device of one architecture
     if (per_cu == 0) {
         constexpr int rows = 16 * NT;   // at most rows appended tokens per sequence (G = 1)
-        const size_t lds_max = (static_cast<size_t>(acc_area_floats(rows, D, rows, stage_token_bytes<KVT, D>(),
-                                                                    NT == 1 ? kWaves : 1)) +
-                                2 * kWaves * rows) * sizeof(float);
+        const size_t lds_max = partition_lds_bytes(rows, D, rows, stage_token_bytes<KVT, D>(), wave_copies(NT));
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_partition_kernel<KVT, D, NT, kStreamLoad>, 64 * kWaves,
                                                          lds_max) != hipSuccess || n < 1)
@@ -955,9 +1049,7 @@ int resident_work_groups() {
 template <int KVT, int D, int NT>
 hipError_t launch_instance(const AttnArgs& a, int num_units, bool shared_blocks, hipStream_t stream) {
     (void)num_units;
-    const size_t lds = (static_cast<size_t>(acc_area_floats(a.rows, D, a.k_rows, stage_token_bytes<KVT, D>(),
-                                                            NT == 1 ? kWaves : 1)) +
-                        2 * kWaves * a.rows) * sizeof(float);
+    const size_t lds = partition_lds_bytes(a.rows, D, a.k_rows, stage_token_bytes<KVT, D>(), wave_copies(NT));
     const int grid = std::min(a.num_items, resident_work_groups<KVT, D, NT>());
     // Tiles are streamed (each is read once per step) unless the batch shares
     // blocks between sequences, whose repeated reads should hit the caches.

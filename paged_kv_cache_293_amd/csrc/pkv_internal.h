@@ -56,6 +56,25 @@ constexpr int kFuseMaxParts = 32;
 // d = 128 a deeper pipeline with two waves per SIMD streams faster than three
 // waves with one tile in flight each.
 constexpr int decode_depth(int kv, int d) { return kv != 0 && d == 128 ? 2 : 1; }
+// Tile buffers a wave of the decode kernel rotates through (NBUF - 1 blocks
+// in flight while one is processed): 1 + decode_depth for one row tile,
+// overridable per element size for measurements; 2 for more row tiles.
+#ifndef PKV_BUFS_1B
+#define PKV_BUFS_1B 3
+#endif
+#ifndef PKV_BUFS_I4
+#define PKV_BUFS_I4 3
+#endif
+#ifndef PKV_BUFS_NT2
+#define PKV_BUFS_NT2 2
+#endif
+constexpr int decode_buffers(int kv, int d, int nt) {
+    return nt == 2 && kv >= 2 ? PKV_BUFS_NT2
+         : nt != 1 ? 2
+         : decode_depth(kv, d) == 1 ? 2
+         : kv == 4 ? PKV_BUFS_I4
+         : (kv == 2 || kv == 3) ? PKV_BUFS_1B : 3;
+}
 constexpr int decode_wgs_per_cu(int kv, int d) { return kv == 0 ? 1 : (d == 128 ? 2 : 3); }
 constexpr int kAutoItemsPerWg = PKV_AUTO_ITEMS_PER_WG;
 constexpr int kAutoMinItemBlocks = PKV_AUTO_MIN_ITEM_BLOCKS;

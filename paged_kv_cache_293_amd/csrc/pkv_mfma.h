@@ -73,6 +73,10 @@ __device__ __forceinline__ float xwg_load(const float* p) {
 // shallow.
 constexpr int kStreamLoad = 2;
 constexpr int kCachedLoad = 0;
+// Cache-policy bits of the partial results' vector loads and stores: sc1,
+// the bit agent-scope atomic loads and stores of one dword carry (xwg_load,
+// xwg_store), so they stay coherent across the XCDs' L2 caches.
+constexpr int kCoherent = 16;
 
 // Tile load through a buffer resource with cache policy POL.
 template <typename T, int POL>
