@@ -38,9 +38,12 @@
 //         16x16x16 MFMA against a tile of ones (the values PV used);
 //   fp8 : codes converted to bf16 in registers (exact), then as bf16; the K
 //         scale folds into the score scale, the V scale into the final divide;
-//   int8, int4: codes widened to bf16 with a bias (128, 136) that the kernel
-//         takes out of the scores (bias x the query row's sum) and of the
-//         output (bias x the probability sum); scales as fp8;
+//   int8: codes widened to fp16 with a bias (1152, one byte permute per two
+//         codes), queries as fp16 times 2^-8, probabilities as fp16, with
+//         v_mfma_f32_16x16x32_f16 (QK) and v_mfma_f32_16x16x16_f16 (PV); the
+//         kernel takes the bias out of the scores (bias x the query row's
+//         sum) and of the output (bias x the probability sum); scales as fp8;
+//   int4: codes widened to bf16 with a bias (136) taken out the same way;
 //   f32 : v_mfma_f32_16x16x4_f32 for both products, probabilities in f32.
 #include <mutex>
 
@@ -78,8 +81,8 @@ __device__ __forceinline__ void accumulate_pv(const TileRegs<KV_BF16, D>& t, con
     }
 }
 
-template <int KVT, int D, int NT>
-__device__ __forceinline__ void accumulate_pv_1b(const TileRegs<KVT, D>& t, const f32x4 (&p)[NT],
+template <int D, int NT>
+__device__ __forceinline__ void accumulate_pv(const TileRegs<KV_FP8, D>& t, const f32x4 (&p)[NT],
                                               f32x4 (&o)[NT][D / 16]) {
     s16x4 pb[NT];
 #pragma unroll
@@ -88,9 +91,7 @@ __device__ __forceinline__ void accumulate_pv_1b(const TileRegs<KVT, D>& t, cons
     }
 #pragma unroll
     for (int m = 0; m < D / 16; ++m) {
-        // int8: biased by kI8Bias (the caller subtracts kI8Bias times the
-        // row's probability sum)
-        const u32x2 vb = {decode_pair<KVT, false>(t.v[m]), decode_pair<KVT, true>(t.v[m])};
+        const u32x2 vb = {decode_pair<KV_FP8, false>(t.v[m]), decode_pair<KV_FP8, true>(t.v[m])};
         const s16x4 a = __builtin_bit_cast(s16x4, vb);
 #pragma unroll
         for (int c = 0; c < NT; ++c)
@@ -98,16 +99,35 @@ __device__ __forceinline__ void accumulate_pv_1b(const TileRegs<KVT, D>& t, cons
     }
 }
 
-template <int D, int NT>
-__device__ __forceinline__ void accumulate_pv(const TileRegs<KV_FP8, D>& t, const f32x4 (&p)[NT],
-                                              f32x4 (&o)[NT][D / 16]) {
-    accumulate_pv_1b<KV_FP8, D, NT>(t, p, o);
+// The probabilities as fp16 (they lie in [0, 2^kLazyMax]), for the int8
+// products.
+template <int NT>
+__device__ __forceinline__ void probs_f16(const f32x4 (&p)[NT], f16x4 (&ph)[NT]) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+        const f16x2_t a = __builtin_convertvector(f32x2_t{p[c][0], p[c][1]}, f16x2_t);
+        const f16x2_t b = __builtin_convertvector(f32x2_t{p[c][2], p[c][3]}, f16x2_t);
+        ph[c] = __builtin_bit_cast(f16x4, u32x2{__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b)});
+    }
 }
 
+// int8: fp16 operands biased by kI8Bias (the caller subtracts kI8Bias times
+// the row's probability sum).
 template <int D, int NT>
 __device__ __forceinline__ void accumulate_pv(const TileRegs<KV_INT8, D>& t, const f32x4 (&p)[NT],
                                               f32x4 (&o)[NT][D / 16]) {
-    accumulate_pv_1b<KV_INT8, D, NT>(t, p, o);
+    f16x4 ph[NT];
+    probs_f16<NT>(p, ph);
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) {
+        const unsigned x = t.v[m] ^ 0x80808080u;
+        const f16x4 a = __builtin_bit_cast(f16x4, u32x2{i8x2_to_f16x2<false>(x), i8x2_to_f16x2<true>(x)});
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+            o[c][m] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, ph[c], o[c][m], 0, 0, 0);
+    }
 }
 
 // Biased: the caller subtracts kI4Bias times the row's probability sum.
@@ -242,9 +262,10 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
         sscale *= a.k_scale[a.layer * a.num_kv_heads + h];
         vscale = a.v_scale[a.layer * a.num_kv_heads + h];
     }
+    if constexpr (KVT == KV_INT8) sscale *= 1.f / kI8QScale;   // int8 scores come in units of kI8QScale
 
     // Query operands and per-column visibility limits.
-    using QT = QRegs<KVT, D>;
+    using QT = typename std::conditional<KVT == KV_INT8, QRegsI8<D>, QRegs<KVT, D>>::type;
     using ElemQ = typename std::conditional<KVT == KV_F32, float, uint16_t>::type;
     QT qr[NT];
     int lim[NT];
@@ -265,14 +286,14 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
         if constexpr (KVT == KV_INT4) qbias[c] = kI4Bias * query_row_sum<D>(qr[c])[0];
-        else if constexpr (KVT == KV_INT8) qbias[c] = kI8Bias * query_row_sum<D>(qr[c])[0];
+        else if constexpr (KVT == KV_INT8) qbias[c] = kI8Bias * query_row_sum<D>(qr[c])[0];   // units of kI8QScale
         else qbias[c] = 0.f;
     }
     const int mask_from = n - kq + 1;
 
     // Row sums of the probabilities: float32 pools add them on the VALU per
     // lane (l_run, four tokens per lane group); the others on the matrix
-    // cores, with the PV product's bf16 operand against a tile of ones
+    // cores, with the PV product's bf16 (int8: fp16) operand against a tile of ones
     // (lacc: every element holds the row's sum of the values used).
     f32x4 o[NT][D / 16];
     float m_run[NT], l_run[NT];
@@ -325,7 +346,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
         f32x4 s[NT];
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
-            if constexpr (KVT == KV_INT8) s[c] = scores_i8_biased<D>(tr, qr[c]);
+            if constexpr (KVT == KV_INT8) s[c] = scores_i8<D>(tr, qr[c]);
             else s[c] = scores<D>(tr, qr[c]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) s[c][i] = (s[c][i] - qbias[c]) * sscale;
@@ -344,9 +365,7 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
         float alpha[NT];
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
-            float mx = fmaxf(fmaxf(s[c][0], s[c][1]), fmaxf(s[c][2], s[c][3]));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mx = max_over_rows(smax(smax(s[c][0], s[c][1]), smax(s[c][2], s[c][3])));
             // The running max is a lagging reference: it moves only when a
             // score exceeds it by more than kLazyMax, so probabilities stay
             // <= 2^kLazyMax and the accumulators are rescaled on few blocks.
@@ -374,7 +393,14 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
                 for (int m = 0; m < D / 16; ++m) o[c][m] *= alpha[c];
             }
         }
-        if constexpr (KVT != KV_F32) {
+        if constexpr (KVT == KV_INT8) {
+            // the fp16 probabilities the int8 PV product uses
+            const f16x4 ones = __builtin_bit_cast(f16x4, u32x2{0x3c003c00u, 0x3c003c00u});
+            f16x4 ph[NT];
+            probs_f16<NT>(p, ph);
+#pragma unroll
+            for (int c = 0; c < NT; ++c) lacc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, ph[c], lacc[c], 0, 0, 0);
+        } else if constexpr (KVT != KV_F32) {
             const s16x4 ones = __builtin_bit_cast(s16x4, u32x2{0x3f803f80u, 0x3f803f80u});
 #pragma unroll
             for (int c = 0; c < NT; ++c) {

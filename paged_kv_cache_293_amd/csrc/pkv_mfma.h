@@ -15,6 +15,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -33,13 +35,19 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
+// Maximum of scores (finite, or -inf where masked): the IEEE maximum, which
+// passes NaN through and so needs no quieting of its operands (fmaxf costs
+// one canonicalising max per operand in IEEE mode); v_maximum3_f32 takes
+// three operands.
+__device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Maximum of x over the four lanes l, l^16, l^32, l^48 (the four 16-lane
 // rows of the wave), with the gfx950 row-swap permutes (no LDS traffic).
 __device__ __forceinline__ float max_over_rows(float x) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    x = smax(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return smax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Buffer resource over one block's K tile followed by its V tile.  Loads
@@ -116,26 +124,25 @@ __device__ __forceinline__ unsigned byte2_to_bf16x2(unsigned w) {
     else return fp8x2_to_bf16x2<HI>(w);
 }
 
-// Two int8 codes (bytes 0-1, or 2-3 when HI, of w) -> two bf16 values biased
-// by kI8Bias: flipping the sign bit turns code c into the byte c + 128, which
-// the byte-to-float converter takes exactly (8 significant bits fit bf16), and
-// one permute packs the pair.  The caller takes the bias out: kI8Bias times
-// the query row's sum from the scores, times the probability sum from the
-// output.
-constexpr float kI8Bias = 128.f;
+// int8 codes for the decode kernel's matrix cores, as fp16: flipping a
+// code's sign bit gives the byte u = c + 128, and the fp16 bits 0x6400 | u
+// are exactly 1024 + u = c + kI8Bias (fp16 holds every integer up to 2048).
+// One byte permute places two codes under the constant high bytes, so four
+// codes cost one XOR and two permutes.  The caller takes the bias out:
+// kI8Bias times the query row's sum from the scores, times the probability
+// sum from the output.
+constexpr float kI8Bias = 1152.f;
+// Codes b0, b1 (HI: b2, b3) of the sign-flipped dword x -> two fp16.
 template <bool HI>
-__device__ __forceinline__ unsigned i8x2_to_bf16x2_biased(unsigned w) {
-    const unsigned x = w ^ 0x80808080u;
-    const float f0 = static_cast<float>((x >> (HI ? 16 : 0)) & 0xffu);
-    const float f1 = static_cast<float>((x >> (HI ? 24 : 8)) & 0xffu);
-    return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+__device__ __forceinline__ unsigned i8x2_to_f16x2(unsigned x) {
+    return __builtin_amdgcn_perm(0x64646464u, x, HI ? 0x04030402u : 0x04010400u);
 }
 
-// Decode-kernel conversion of two one-byte codes: fp8 exact, int8 biased.
+// Two fp8 E4M3 codes of w -> bf16 pair, in the decode kernel's K order.
 template <int KVT, bool HI>
 __device__ __forceinline__ unsigned decode_pair(unsigned w) {
-    if constexpr (KVT == KV_INT8) return i8x2_to_bf16x2_biased<HI>(w);
-    else return fp8x2_to_bf16x2<HI>(w);
+    static_assert(KVT == KV_FP8, "fp8 only");
+    return fp8x2_to_bf16x2<HI>(w);
 }
 
 // Work-group barrier that orders LDS accesses only.  The plain barrier's
@@ -425,7 +432,7 @@ __device__ __forceinline__ f32x4 scores(const TileRegs<KV_BF16, D>& t, const QRe
     return acc;
 }
 
-template <int KVT, int D, bool BIASED = false>
+template <int KVT, int D>
 __device__ __forceinline__ f32x4 scores_1b(const TileRegs<KVT, D>& t, const QRegs<KVT, D>& q) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -433,8 +440,7 @@ __device__ __forceinline__ f32x4 scores_1b(const TileRegs<KVT, D>& t, const QReg
         const u32x4 w = t.k[r];
         auto cv = [](unsigned x, auto hi_half) {
             constexpr bool H = decltype(hi_half)::value;
-            if constexpr (BIASED) return decode_pair<KVT, H>(x);
-            else return byte2_to_bf16x2<KVT, H>(x);
+            return byte2_to_bf16x2<KVT, H>(x);
         };
         using L = std::false_type;
         using H = std::true_type;
@@ -456,11 +462,48 @@ __device__ __forceinline__ f32x4 scores(const TileRegs<KV_INT8, D>& t, const QRe
     return scores_1b<KV_INT8, D>(t, q);
 }
 
-// int8 scores for the decode kernel, biased: the caller subtracts kI8Bias
-// times the query row's sum.
+// Decode-kernel int8 query operand: the bf16 query times 2^-8 as fp16 (in
+// QRegs1B's dim order).  A bf16 value keeps its 8 significant bits in fp16
+// from 2^-6 to just below 2^24 in magnitude (larger ones overflow);
+// below, fp16's subnormal spacing (2^-16 in query units) bounds the error.
+// The caller multiplies the scores by 2^8.
+constexpr float kI8QScale = 1.f / 256.f;
+template <int D> struct QRegsI8 {
+    f16x8 q[D / 32];
+    __device__ __forceinline__ void load(const uint16_t* row, bool valid, int lane) {
+#pragma unroll
+        for (int st = 0; st < D / 32; ++st) {
+            const int dim0 = (4 * (st >> 1) + (lane >> 4)) * 16 + 8 * (st & 1);
+            const u32x4 w = valid ? *reinterpret_cast<const u32x4*>(row + dim0) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float lo = __uint_as_float(w[j] << 16) * kI8QScale;
+                const float hi = __uint_as_float(w[j] & 0xffff0000u) * kI8QScale;
+                q[st][2 * j] = static_cast<_Float16>(lo);
+                q[st][2 * j + 1] = static_cast<_Float16>(hi);
+            }
+        }
+    }
+};
+
+// int8 scores for the decode kernel, in units of kI8QScale and biased: the
+// caller subtracts kI8Bias times the query row's sum (query_row_sum below).
 template <int D>
-__device__ __forceinline__ f32x4 scores_i8_biased(const TileRegs<KV_INT8, D>& t, const QRegs<KV_INT8, D>& q) {
-    return scores_1b<KV_INT8, D, true>(t, q);
+__device__ __forceinline__ f32x4 scores_i8(const TileRegs<KV_INT8, D>& t, const QRegsI8<D>& q) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < D / 64; ++r) {
+        u32x4 x = t.k[r];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] ^= 0x80808080u;
+        const u32x4 lo = {i8x2_to_f16x2<false>(x[0]), i8x2_to_f16x2<true>(x[0]), i8x2_to_f16x2<false>(x[1]),
+                          i8x2_to_f16x2<true>(x[1])};
+        const u32x4 hi = {i8x2_to_f16x2<false>(x[2]), i8x2_to_f16x2<true>(x[2]), i8x2_to_f16x2<false>(x[3]),
+                          i8x2_to_f16x2<true>(x[3])};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, lo), q.q[2 * r], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, hi), q.q[2 * r + 1], acc, 0, 0, 0);
+    }
+    return acc;
 }
 
 // Biased scores: the caller subtracts kI4Bias times the query row's sum.
@@ -486,6 +529,16 @@ __device__ __forceinline__ f32x4 query_row_sum(const QRegs<KV_BF16, D>& q) {
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones), q.q[s], acc, 0, 0, 0);
+    return acc;
+}
+
+template <int D>
+__device__ __forceinline__ f32x4 query_row_sum(const QRegsI8<D>& q) {
+    const u32x4 ones = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ones), q.q[s], acc, 0, 0, 0);
     return acc;
 }
 

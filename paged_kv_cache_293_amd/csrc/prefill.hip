@@ -90,27 +90,40 @@ __device__ __forceinline__ int pf_v_chunk(int c) {
     else return c;
 }
 
-// Copy one pair (blocks id_a, id_b) of this KV head into an LDS stage: this
-// wave's share of the 1 KiB pieces, 16 bytes per lane, straight into LDS (the
-// lane's 16 bytes land at LDS offset lane * 16 of the piece; V tiles take
-// their chunks in the order pf_v_chunk gives).
+// Copy one pair (blocks A and B) of this KV head into an LDS stage: this
+// wave's share of the 1 KiB pieces, 16 bytes per lane, straight into LDS by
+// buffer_load ... lds (the lane's 16 bytes land at LDS offset lane * 16 of
+// the piece; V tiles take their chunks in the order pf_v_chunk gives).  A
+// piece lies in one block (tiles 0-1 of the pair are block A's K and V, 2-3
+// block B's; a piece spans two tiles only when tiles are 512 bytes, int4 at
+// head dim 64, and then both are one block's), so each load goes through
+// that block's buffer resource with a per-lane offset that is the same for
+// every pair: pf_piece_offset, computed once.
 template <int KVT, int D>
-__device__ __forceinline__ void pf_issue(const uint8_t* head_base, int64_t block_stride, int id_a, int id_b,
-                                         uint8_t* stage, int wave, int lane) {
+__device__ __forceinline__ int pf_piece_offset(int k, int wave, int lane) {
+    using Gm = PfGeom<KVT, D>;
+    const int at = (wave + kPfWaves * k) * 1024 + lane * 16;   // byte of the pair in LDS
+    const int tile = at / Gm::TILE;
+    const int c = (at - tile * Gm::TILE) / 16;
+    return (tile & 1) * Gm::TILE + ((tile & 1) ? pf_v_chunk<KVT>(c) : c) * 16;
+}
+
+template <int KVT, int D>
+__device__ __forceinline__ void pf_issue(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, uint8_t* stage,
+                                         const int (&voff)[PfGeom<KVT, D>::LOADS], int wave) {
     using Gm = PfGeom<KVT, D>;
 #pragma unroll
     for (int k = 0; k < Gm::LOADS; ++k) {
         const int gk = wave + kPfWaves * k;             // 1 KiB piece of the pair's 4 tiles
         if (Gm::PIECES % kPfWaves != 0 && gk >= Gm::PIECES) break;
-        const int at = gk * 1024;                       // byte of the pair in LDS
-        // this lane's 16 bytes: chunk c of tile 0 K_A, 1 V_A, 2 K_B, 3 V_B (a
-        // piece spans two tiles only when tiles are 512 bytes: int4, head dim 64)
-        const int tile = (at + lane * 16) / Gm::TILE;
-        const int c = (at + lane * 16 - tile * Gm::TILE) / 16;
-        const int chunk = (tile & 1) ? pf_v_chunk<KVT>(c) : c;
-        const int id = tile < 2 ? id_a : id_b;
-        const uint8_t* src = head_base + static_cast<int64_t>(id) * block_stride + (tile & 1) * Gm::TILE + chunk * 16;
-        __builtin_amdgcn_global_load_lds(src, stage + at, 16, 0, 0);
+        const bool in_a = gk * 1024 < 2 * Gm::TILE;
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(in_a ? ra : rb,
+                                                 (__attribute__((address_space(3))) void*)(stage + gk * 1024), 16,
+                                                 voff[k], 0, 0, 0);
+#else
+        (void)in_a; (void)ra; (void)rb; (void)stage; (void)voff;
+#endif
     }
 }
 
@@ -221,7 +234,7 @@ void attn_prefill_kernel(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t pf_smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lg = lane >> 4;
     const int col = lane & 15;
 
@@ -323,8 +336,15 @@ void attn_prefill_kernel(PrefillArgs a) {
         ia = crow[2 * q];
         ib = 2 * q + 1 < nblk ? crow[2 * q + 1] : ia;
     };
+    int voff[Gm::LOADS];
+#pragma unroll
+    for (int k = 0; k < Gm::LOADS; ++k) voff[k] = pf_piece_offset<KVT, D>(k, wave, lane);
+    auto block_rsrc = [&](int id) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(head_base) + static_cast<int64_t>(id) * block_stride,
+                                                 0, static_cast<int>(2 * Gm::TILE), 0x00020000);
+    };
     auto issue = [&](int q, int ia, int ib) {
-        pf_issue<KVT, D>(head_base, block_stride, ia, ib, pf_smem + (q % kPfStages) * Gm::PAIR, wave, lane);
+        pf_issue<KVT, D>(block_rsrc(ia), block_rsrc(ib), pf_smem + (q % kPfStages) * Gm::PAIR, voff, wave);
     };
 #pragma unroll
     for (int q = 0; q < kPfAhead; ++q) {
@@ -386,8 +406,7 @@ void attn_prefill_kernel(PrefillArgs a) {
             // accumulators are rescaled) only when a score exceeds it by more
             // than kLazyMax, so probabilities stay <= 2^kLazyMax.  O and its
             // row sum share the same max, so O / sum is unchanged.
-            float mx = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])),
-                             fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
+            float mx = smax(smax(smax(sa[0], sa[1]), smax(sa[2], sa[3])), smax(smax(sb[0], sb[1]), smax(sb[2], sb[3])));
             mx = max_over_rows(mx) * sscale;
             alpha[c] = 1.f;
             if (mx > m_run[c] + kLazyMax) {
