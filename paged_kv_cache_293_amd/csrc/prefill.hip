@@ -357,7 +357,12 @@ void attn_prefill_kernel(PrefillArgs a) {
     int next_a = 0, next_b = 0;   // ids of pair p + kPfAhead
     if (kPfAhead < npair) ids_of(kPfAhead, next_a, next_b);
 
-    for (int p = 0; p < npair; ++p) {
+    // One pair.  MASKED: the pair may hold positions some row of this wave
+    // may not see (causal mask, and positions past the sequence end, whose V
+    // entries are zeroed); the pairs before p_split hold none, and their
+    // steps carry no mask code.
+    auto step = [&](int p, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
         // This wave's pieces of pair p have landed (the next pairs may still
         // be in flight); the barrier makes every wave's pieces visible and
         // ensures pair p-1's stage is no longer read.
@@ -373,7 +378,7 @@ void attn_prefill_kernel(PrefillArgs a) {
 
         uint8_t* st = pf_smem + (p % kPfStages) * Gm::PAIR;
         const int t0 = 32 * p;
-        if (!CASCADE && KVT != KV_INT4 && t0 + 32 > n) {
+        if (MASKED && !CASCADE && KVT != KV_INT4 && t0 + 32 > n) {
             // only the last pair reaches past the sequence end; nothing is in
             // flight (every int4 nibble is a finite value: no zeroing needed)
             pf_zero_v_tail<KVT, D>(st, t0, n, tid);
@@ -382,7 +387,6 @@ void attn_prefill_kernel(PrefillArgs a) {
         TileRegs<KVT, D> ka, kb;
         pf_k_regs<KVT, D>(ka, st, lane);
         pf_k_regs<KVT, D>(kb, st + 2 * Gm::TILE, lane);
-        const bool need_mask = t0 + 32 > lim_lo;
         u32x4 pop[kPfNT];
         float alpha[kPfNT];
         bool rescale = false;
@@ -395,7 +399,7 @@ void attn_prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) { sa[i] -= qbias[c]; sb[i] -= qbias[c]; }
             }
-            if (need_mask) {
+            if constexpr (MASKED) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if (t0 + 4 * lg + i >= lim[c]) sa[i] = neg_inf();
@@ -414,7 +418,8 @@ void attn_prefill_kernel(PrefillArgs a) {
                 m_run[c] = mx;
                 rescale = true;
             }
-            const float muse = m_run[c] == neg_inf() ? 0.f : m_run[c];
+            // (every score of an unmasked pair is finite, so the max is too)
+            const float muse = MASKED && m_run[c] == neg_inf() ? 0.f : m_run[c];
             float pa[4], pb[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -450,7 +455,12 @@ void attn_prefill_kernel(PrefillArgs a) {
                 o[c][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, pop[c]), o[c][m],
                                                                   0, 0, 0);
         }
-    }
+    };
+    // Pair p needs the mask iff 32 p + 32 > lim_lo; the waves' splits differ,
+    // their barrier counts (one per pair) do not.
+    const int p_split = min(npair, lim_lo >= 32 ? (lim_lo - 32) / 32 + 1 : 0);
+    for (int p = 0; p < p_split; ++p) step(p, std::false_type{});
+    for (int p = p_split; p < npair; ++p) step(p, std::true_type{});
 
     // Normalise and store: lane holds dims 16m + 4lg .. +3 of row 16c + col.
 #pragma unroll
