@@ -291,6 +291,8 @@ def main():
     unique_bytes = int(int(w.info["blocks_used"]) * 16 * 2 * w.num_kv_heads * w.head_dim * ELEM_BYTES[w.kv_dtype])
     kernel_label = ("attn_partition_kernel (split-KV merge inside)" if info["max_parts"] <= 32
                     else "attn_partition_kernel + attn_merge_kernel")
+    prefix_blocks, prefix_chunks = table.shared_prefix()
+    shared_prefix = prefix_blocks > 0 and int(w.seq_lens.min()) - kq >= 16 * prefix_blocks
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
     if os.path.exists(tpath):
@@ -340,6 +342,29 @@ def main():
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
+    if shared_prefix:
+        # Two kernels per step: the shared-prefix pass (every query row
+        # against the prefix blocks, on the matrix cores) and the walk over
+        # each sequence's own blocks (HBM).  Their bound: the pass's flops at
+        # the bf16 MFMA peak plus the own blocks' bytes at the HBM peak; the
+        # step's time against that sum.  (Per-kernel durations come from the
+        # rocprofv3 trace of the same command.)
+        rows = w.batch * kq * w.num_q_heads
+        prefix_flops = 4 * rows * 16 * prefix_blocks * w.head_dim
+        own_bytes = unique_bytes - prefix_blocks * 16 * 2 * w.num_kv_heads * w.head_dim * ELEM_BYTES[w.kv_dtype]
+        t_mfma = prefix_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6
+        t_hbm = own_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
+        step_us = kernel_ms * 1e3
+        result["config"]["shared_prefix_blocks"] = prefix_blocks
+        result["config"]["prefix_chunks"] = prefix_chunks
+        result["roofline"] = {
+            "bound": "mfma+hbm",
+            "kernel": "attn_prefill_kernel (shared-prefix pass) then attn_partition_kernel (own blocks)",
+            "achieved": round(t_mfma + t_hbm, 2), "peak": round(step_us, 2),
+            "unit": "us: the two-kernel lower bound (achieved) and the step's time (peak)",
+            "frac": round((t_mfma + t_hbm) / step_us, 4), "traffic": traffic,
+            "parts": {"prefix_pass_flops": prefix_flops, "prefix_pass_us_at_mfma_peak": round(t_mfma, 2),
+                      "own_block_bytes": own_bytes, "own_blocks_us_at_hbm_peak": round(t_hbm, 2)}}
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)

@@ -54,7 +54,9 @@ constexpr int kFuseMaxParts = 32;
 // processes one) and the waves per SIMD it is built for, which is also its
 // resident work-groups per CU (a work-group is one wave on each SIMD).  At
 // d = 128 a deeper pipeline with two waves per SIMD streams faster than three
-// waves with one tile in flight each.
+// waves with one tile in flight each; int4 (2 KiB per block and KV head, the
+// most widening work per byte) runs three waves per SIMD with the deeper
+// pipeline too (measured on the Llama-3-8B decode batch: 39.2 -> 35.5 us).
 constexpr int decode_depth(int kv, int d) { return kv != 0 && d == 128 ? 2 : 1; }
 // Tile buffers a wave of the decode kernel rotates through (NBUF - 1 blocks
 // in flight while one is processed): 1 + decode_depth for one row tile,
@@ -75,7 +77,7 @@ constexpr int decode_buffers(int kv, int d, int nt) {
          : kv == 4 ? PKV_BUFS_I4
          : (kv == 2 || kv == 3) ? PKV_BUFS_1B : 3;
 }
-constexpr int decode_wgs_per_cu(int kv, int d) { return kv == 0 ? 1 : (d == 128 ? 2 : 3); }
+constexpr int decode_wgs_per_cu(int kv, int d) { return kv == 0 ? 1 : (d == 128 ? (kv == 4 ? 3 : 2) : 3); }
 constexpr int kAutoItemsPerWg = PKV_AUTO_ITEMS_PER_WG;
 constexpr int kAutoMinItemBlocks = PKV_AUTO_MIN_ITEM_BLOCKS;
 constexpr int kAutoMinBlocks = 8;

@@ -337,6 +337,11 @@ __device__ __forceinline__ unsigned i4_pair(unsigned lo, unsigned hi, int k) {
     return __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
 }
 
+// bf16 pair of bytes 2h and 2h + 1 of x (biased nibbles): bits 0x43 | u each.
+__device__ __forceinline__ unsigned i4_pair_same(unsigned x, int h) {
+    return __builtin_amdgcn_perm(0x43434343u, x, h ? 0x04030402u : 0x04010400u);
+}
+
 template <int D> struct TileRegs<KV_F32, D> {
     f32x4 k[D / 16];   // 4 f32: token lane%16, dims of chunk 4r + lane/16
     f32x4 v[D / 16];   // 4 f32: dim 16m + lane%16, tokens 4*(lane/16) .. +3
@@ -409,8 +414,23 @@ template <int D> struct QRegs1B {
 };
 template <int D> struct QRegs<KV_FP8, D> : QRegs1B<D> {};
 template <int D> struct QRegs<KV_INT8, D> : QRegs1B<D> {};
-// int4 K runs hold dims 32 s + 8 (lane / 16) + e per step s: the bf16 order.
-template <int D> struct QRegs<KV_INT4, D> : QRegs<KV_BF16, D> {};
+// int4 K runs hold dims 32 s + 8 (lane / 16) + e per step s; the score
+// operand takes them as even dims then odd dims (0 2 4 6 1 3 5 7 of each
+// eight, the order in which one byte permute per two codes widens them), so
+// the query's eight values of a step are loaded in that order.
+template <int D> struct QRegs<KV_INT4, D> : QRegs<KV_BF16, D> {
+    __device__ __forceinline__ void load(const uint16_t* row, bool valid, int lane) {
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+            const u32x4 w = valid ? *reinterpret_cast<const u32x4*>(row + (4 * s + (lane >> 4)) * 8)
+                                  : u32x4{0u, 0u, 0u, 0u};
+            // w = (q0 q1)(q2 q3)(q4 q5)(q6 q7) -> (q0 q2)(q4 q6)(q1 q3)(q5 q7)
+            const u32x4 p = {__builtin_amdgcn_perm(w[1], w[0], 0x05040100u), __builtin_amdgcn_perm(w[3], w[2], 0x05040100u),
+                             __builtin_amdgcn_perm(w[1], w[0], 0x07060302u), __builtin_amdgcn_perm(w[3], w[2], 0x07060302u)};
+            this->q[s] = __builtin_bit_cast(bf16x8, p);
+        }
+    }
+};
 
 template <int D> struct QRegs<KV_F32, D> {
     f32x4 q[D / 16];    // r: dims (4r + lane/16) * 4 .. +4, one MFMA per element
@@ -514,7 +534,9 @@ __device__ __forceinline__ f32x4 scores(const TileRegs<KV_INT4, D>& t, const QRe
     for (int s = 0; s < D / 32; ++s) {
         unsigned ev, od;
         i4_split(t.k[s], ev, od);
-        const u32x4 kb = {i4_pair(ev, od, 0), i4_pair(ev, od, 1), i4_pair(ev, od, 2), i4_pair(ev, od, 3)};
+        // dims 0 2 4 6 1 3 5 7 (the query's order): bf16 0x43 | u, one
+        // permute per pair against the constant high bytes
+        const u32x4 kb = {i4_pair_same(ev, 0), i4_pair_same(ev, 1), i4_pair_same(od, 0), i4_pair_same(od, 1)};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb), q.q[s], acc, 0, 0, 0);
     }
     return acc;
