@@ -104,7 +104,9 @@ typedef int32_t pkv_status;
  * of the attention kernel's 64 lanes reads one contiguous run; with
  * W = head_dim / 4 nibbles per run:
  *   K (o, i), i = 32 s + 8 g + e (e < 8, g < 4):   N = (g * 16 + o) * W + 8 s + e
- *   V (o, i), o = 4 g + t, i = 16 m + c (c < 16):  N = (g * 16 + c) * W + t * (head_dim / 16) + m
+ *   V (o, i), o = 4 g + t, i = 16 m + c (c < 16):  N = (g * 16 + c) * W + 8 (m / 2) + 2 t + (m % 2)
+ * (a V run's byte 4 j + t holds token 4 g + t at dims 16 (2 j) + c, low
+ * nibble, and 16 (2 j + 1) + c, high nibble).
  * Token position t of a sequence with block table row `bt` lives at block
  * bt[t / 16], offset t % 16; its flat slot is bt[t / 16] * 16 + t % 16.
  * For PKV_FP8_E4M3, PKV_INT8 and PKV_INT4 the stored code c of head h in layer l stands for the value

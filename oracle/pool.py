@@ -31,7 +31,7 @@ so the oracle reads the pool from the definition, not from library code):
   (nibble N is byte N // 2, the low half when N is even) so that no byte
   holds two tokens; with W = d // 4:
   K (token o, dim i = 32 s + 8 g + e):  N = (g * 16 + o) * W + 8 s + e,
-  V (token o = 4 g + t, dim i = 16 m + c):  N = (g * 16 + c) * W + t * (d // 16) + m.
+  V (token o = 4 g + t, dim i = 16 m + c):  N = (g * 16 + c) * W + 8 * (m // 2) + 2 * t + m % 2.
 
 Pins: the layout formula is checked against hand-computed offsets stored in
 ``tests/golden/pool_layout.txt``; the slot rule against the block-table
@@ -104,7 +104,7 @@ def v_nibble_in_tile(desc, token, dim):
     w = desc.head_dim // 4
     g, t = token // 4, token % 4
     m, c = dim // 16, dim % 16
-    return (g * BLOCK_SIZE + c) * w + t * (desc.head_dim // 16) + m
+    return (g * BLOCK_SIZE + c) * w + 8 * (m // 2) + 2 * t + m % 2
 
 
 def element_nibble_offset(desc, layer, block, head, kv, token, dim):

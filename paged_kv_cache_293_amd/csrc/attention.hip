@@ -139,26 +139,20 @@ __device__ __forceinline__ void accumulate_pv(const TileRegs<KV_INT4, D>& t, con
     for (int c = 0; c < NT; ++c) {
         pb[c] = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[c][0], p[c][1]), pack_bf16x2(p[c][2], p[c][3])});
     }
-    constexpr int M = D / 16;                    // nibbles per token in a lane's V run
-    constexpr int WPT = M / 8 > 0 ? M / 8 : 1;   // dwords per token (D = 128: 1; D = 64: half of one)
-    unsigned ev[4], od[4];                       // per token t: biased nibbles by parity
-    if constexpr (M == 8) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) i4_split(t.v[tt * WPT], ev[tt], od[tt]);
-    } else {
-        // D = 64: token t's 4 nibbles are the (t % 2) half of dword t / 2
+    for (int j = 0; j < D / 32; ++j) {
+        // V dword j: byte t holds token 4 (lane / 16) + t at dims 16 (2 j) +
+        // lane % 16 (low nibble) and 16 (2 j + 1) + lane % 16 (high nibble)
+        unsigned ev, od;
+        i4_split(t.v[j], ev, od);
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) i4_split(t.v[tt / 2] >> (16 * (tt % 2)), ev[tt], od[tt]);
-    }
+        for (int hh = 0; hh < 2; ++hh) {
+            const unsigned src = hh ? od : ev;
+            const s16x4 a = __builtin_bit_cast(s16x4, u32x2{i4_pair_same(src, 0), i4_pair_same(src, 1)});
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-        // tokens 4 (lane / 16) + t, dim 16 m + lane % 16: nibble m of token t
-        const unsigned* src = (m % 2) ? od : ev;
-        const u32x2 vb = {i4_pair(src[0], src[1], m / 2), i4_pair(src[2], src[3], m / 2)};
-        const s16x4 a = __builtin_bit_cast(s16x4, vb);
-#pragma unroll
-        for (int c = 0; c < NT; ++c)
-            o[c][m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb[c], o[c][m], 0, 0, 0);
+            for (int c = 0; c < NT; ++c)
+                o[c][2 * j + hh] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb[c], o[c][2 * j + hh], 0, 0, 0);
+        }
     }
 }
 
@@ -572,8 +566,8 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             const uint8_t* st = stage + (t - lo) * STOK;
             if constexpr (KVT == KV_INT4) {
                 // K: run (g, o) holds dims 32 s + 8 g + e at nibble 8 s + e;
-                // V: run (o / 4, c) holds dims 16 m + c of token o at nibble
-                // (o % 4) * (D / 16) + m.
+                // V: run (o / 4, c) holds dims 16 (2 j) + c and 16 (2 j + 1) + c
+                // of token o in byte 4 j + o % 4 (low, high nibble).
                 for (int w = tid; w < 4 + 16; w += 64 * kWaves) {
                     if (w < 4) {
                         unsigned wd[D / 32];
@@ -590,11 +584,10 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
                     } else {
                         const int c = w - 4;
                         uint8_t* run = tv + ((o / 4) * 16 + c) * (D / 8);
-                        unsigned x = 0;
 #pragma unroll
-                        for (int m = 0; m < D / 16; ++m) x |= (static_cast<unsigned>(st[D + 16 * m + c]) & 0xfu) << (4 * m);
-                        if constexpr (D == 128) reinterpret_cast<unsigned*>(run)[o % 4] = x;
-                        else reinterpret_cast<uint16_t*>(run)[o % 4] = static_cast<uint16_t>(x);
+                        for (int j = 0; j < D / 32; ++j)
+                            run[4 * j + o % 4] = static_cast<uint8_t>((st[D + 32 * j + c] & 0xfu) |
+                                                                      ((st[D + 32 * j + 16 + c] & 0xfu) << 4));
                     }
                 }
             } else {

@@ -81,8 +81,8 @@ __device__ __forceinline__ unsigned pack8_i4(const void* row, int64_t first, int
 }
 
 // int4 pools (layout in the library header): per token, K is four runs of
-// D / 4 nibbles (lane groups g), V sixteen partial runs of D / 16 nibbles
-// (columns c); every byte written belongs to this token alone.
+// D / 4 nibbles (lane groups g), V one byte in every fourth byte of sixteen
+// runs (columns c); every byte written belongs to this token alone.
 template <int IN, int D>
 __device__ __forceinline__ void write_token_i4(uint8_t* blk, int64_t tile_bytes, int off, const void* k_row,
                                                const void* v_row, int h0, int nh, const float* k_scale,
@@ -114,14 +114,13 @@ __device__ __forceinline__ void write_token_i4(uint8_t* blk, int64_t tile_bytes,
         const float inv = 1.0f / v_scale[h];
         uint8_t* run = blk + (static_cast<int64_t>(h) * 2 + 1) * tile_bytes + (g * 16 + c) * (W / 2);
         const int64_t src = static_cast<int64_t>(h) * D + c;
-        // dims 16 m + c at nibble t * (D / 16) + m
-        if constexpr (D == 128) {
-            reinterpret_cast<unsigned*>(run)[t] = pack8_i4<IN>(v_row, src, 16, inv);
-        } else {
-            unsigned w = 0;
+        // byte 4 j + t of the run: dims 16 (2 j) + c (low nibble) and
+        // 16 (2 j + 1) + c (high nibble) of this token
 #pragma unroll
-            for (int m = 0; m < 4; ++m) w |= quantize_i4(load_in<IN>(v_row, src + 16 * m), inv) << (4 * m);
-            reinterpret_cast<uint16_t*>(run)[t] = static_cast<uint16_t>(w);
+        for (int j = 0; j < D / 32; ++j) {
+            const unsigned lo = quantize_i4(load_in<IN>(v_row, src + 16 * (2 * j)), inv);
+            const unsigned hi = quantize_i4(load_in<IN>(v_row, src + 16 * (2 * j + 1)), inv);
+            run[4 * j + t] = static_cast<uint8_t>(lo | (hi << 4));
         }
     }
 }

@@ -246,13 +246,16 @@ template <int D> struct TileRegs<KV_INT8, D> : TileRegs1B<D> {};
 // int4 tiles: each lane reads its own run of D / 4 nibbles from the K and the
 // V tile (layout in the library header), so koff = lane * D / 8 and
 // voff = TILE + lane * D / 8 with TILE = 8 * D.  K nibble 8 s + e holds dim
-// 32 s + 8 (lane / 16) + e of token lane % 16; V nibble t * (D / 16) + m holds
-// dim 16 m + lane % 16 of token 4 (lane / 16) + t.
+// 32 s + 8 (lane / 16) + e of token lane % 16; V byte 4 j + t holds dims
+// 16 (2 j) + lane % 16 (low nibble) and 16 (2 j + 1) + lane % 16 (high
+// nibble) of token 4 (lane / 16) + t, so V dword j holds two dim tiles for
+// the lane's four tokens.
 //
 // Codes enter the matrix cores biased: flipping a nibble's top bit turns the
 // code c into u = c + 8 in [0, 15], and the bf16 bits 0x4300 | u are exactly
-// 128 + u = c + kI4Bias.  Two codes become one bf16 pair with a byte permute
-// and an OR.  The bias is taken out of the scores (kI4Bias * sum of the query
+// 128 + u = c + kI4Bias.  After the nibbles are split into bytes, two codes
+// become one bf16 pair with one byte permute against the constant high
+// bytes.  The bias is taken out of the scores (kI4Bias * sum of the query
 // row) and of the output (kI4Bias * the row's probability sum) by the caller.
 // Every nibble pattern is a finite value, so no V row needs zeroing.
 template <int D> struct TileRegs<KV_INT4, D> {
@@ -293,28 +296,15 @@ template <int D> struct TileRegs<KV_INT4, D> {
             }
         }
         if ((lane >> 4) == (o >> 2)) {
-            const int t = o & 3;
+            // byte o % 4 of every V dword
+            const unsigned sh = 8 * (o & 3);
+            const unsigned keep = ~(0xffu << sh);
             const int c = lane & 15;
-            if constexpr (D == 128) {
-                unsigned w = 0;
 #pragma unroll
-                for (int m = 0; m < 8; ++m) w |= (static_cast<unsigned>(st[D + 16 * m + c]) & 0xfu) << (4 * m);
-                // per-lane selects: with a uniform index the compiler would
-                // address v[] dynamically and move the tile to scratch
-                int tv = t;
-                asm volatile("" : "+v"(tv));
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = (j == tv) ? w : v[j];
-            } else {
-                unsigned w = 0;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) w |= (static_cast<unsigned>(st[D + 16 * m + c]) & 0xfu) << (4 * m);
-                const unsigned sh = 16 * (t & 1);
-                const unsigned keep = ~(0xffffu << sh);
-                int tv = t >> 1;
-                asm volatile("" : "+v"(tv));
-#pragma unroll
-                for (int j = 0; j < 2; ++j) v[j] = (j == tv) ? ((v[j] & keep) | (w << sh)) : v[j];
+            for (int j = 0; j < D / 32; ++j) {
+                const unsigned b = (static_cast<unsigned>(st[D + 32 * j + c]) & 0xfu) |
+                                   ((static_cast<unsigned>(st[D + 32 * j + 16 + c]) & 0xfu) << 4);
+                v[j] = (v[j] & keep) | (b << sh);
             }
         }
     }
@@ -328,13 +318,6 @@ __device__ __forceinline__ void i4_split(unsigned w, unsigned& even, unsigned& o
     const unsigned x = w ^ 0x88888888u;
     even = x & 0x0f0f0f0fu;
     odd = (x >> 4) & 0x0f0f0f0fu;
-}
-
-// bf16 pair (byte k of lo -> low half, byte k of hi -> high half), biased.
-__device__ __forceinline__ unsigned i4_pair(unsigned lo, unsigned hi, int k) {
-    // result bytes: [lo.k, 0, hi.k, 0]; selector 0x0c yields a zero byte
-    const unsigned sel = static_cast<unsigned>(k) | (0x0cu << 8) | ((4u + k) << 16) | (0x0cu << 24);
-    return __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
 }
 
 // bf16 pair of bytes 2h and 2h + 1 of x (biased nibbles): bits 0x43 | u each.

@@ -170,13 +170,14 @@ __device__ __forceinline__ u32x4 pf_v_op(const uint8_t* va, const uint8_t* vb, i
     }
 }
 
-// int4 V^T operand over a pair.  Lane (col, lg)'s run of a V tile holds
-// tokens 4lg .. 4lg+3 of dims 16m + col, m = 0 .. D/16 - 1 (layout in the
-// library header); its codes, biased by 8 (so code + kI4Bias as bf16), split
-// by the parity of m: ev[t] / od[t] hold token t's even / odd m in bytes.
+// int4 V^T operand over a pair.  Lane (col, lg)'s run of a V tile holds,
+// in byte 4j + t, token 4lg + t at dims 16 (2j) + col (low nibble) and
+// 16 (2j + 1) + col (high nibble) (layout in the library header); its codes,
+// biased by 8 (so code + kI4Bias as bf16), split into bytes: ev[b][j] holds
+// dim tile 2j, od[b][j] dim tile 2j + 1, tokens 0..3 of block b.
 template <int D>
 struct PfV4 {
-    unsigned ev[8], od[8];   // tokens 0..3 of block A, then of block B
+    unsigned ev[2][D / 32], od[2][D / 32];
     __device__ __forceinline__ void load(const uint8_t* va, const uint8_t* vb, int lane) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -184,19 +185,19 @@ struct PfV4 {
             if constexpr (D == 128) {
                 const u32x4 w = *reinterpret_cast<const u32x4*>(run);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) i4_split(w[t], ev[4 * b + t], od[4 * b + t]);
+                for (int j = 0; j < 4; ++j) i4_split(w[j], ev[b][j], od[b][j]);
             } else {
                 const u32x2 w = *reinterpret_cast<const u32x2*>(run);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) i4_split(w[t / 2] >> (16 * (t % 2)), ev[4 * b + t], od[4 * b + t]);
+                for (int j = 0; j < 2; ++j) i4_split(w[j], ev[b][j], od[b][j]);
             }
         }
     }
     // 8 biased bf16: dim 16m + col, tokens 0..3 of A then of B
     __device__ __forceinline__ u32x4 op(int m) const {
-        const unsigned* src = (m % 2) ? od : ev;
-        return u32x4{i4_pair(src[0], src[1], m / 2), i4_pair(src[2], src[3], m / 2), i4_pair(src[4], src[5], m / 2),
-                     i4_pair(src[6], src[7], m / 2)};
+        const unsigned a = (m % 2) ? od[0][m / 2] : ev[0][m / 2];
+        const unsigned b = (m % 2) ? od[1][m / 2] : ev[1][m / 2];
+        return u32x4{i4_pair_same(a, 0), i4_pair_same(a, 1), i4_pair_same(b, 0), i4_pair_same(b, 1)};
     }
 };
 

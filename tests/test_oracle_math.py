@@ -119,7 +119,7 @@ def test_int4_pool_layout_hand_offsets():
         got = opool.element_nibble_offset(desc, int(layer), int(block), int(head),
                                           0 if kv == "K" else 1, int(tok), int(dim))
         assert got == int(expected)
-    assert seen == 4
+    assert seen == 5
 
 
 @pytest.mark.parametrize("d", [64, 128])
