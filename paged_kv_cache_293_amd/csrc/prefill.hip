@@ -19,10 +19,13 @@
 // its state fits in 256 VGPRs, so two work-groups share a CU and their waves
 // interleave softmax (VALU) and matrix work on each SIMD.  The K/V of
 // the visible blocks stream through a three-stage LDS ring, two blocks (a
-// "pair") per stage, copied straight from the pool into LDS by
-// global_load_lds_dwordx4 (no register staging); each wave issues its share
-// of the pair two steps ahead, and one barrier per pair publishes it.  The
-// block ids are read with scalar loads, a pair ahead of their use.
+// "pair") per stage, copied straight from the pool into LDS by 16-byte
+// buffer loads with the LDS as destination (no register staging; one buffer
+// resource per block, loop-invariant lane offsets); each wave issues its
+// share of the pair two steps ahead, and one barrier per pair publishes it.
+// The block ids are read with scalar loads, a pair ahead of their use.  A
+// wave's pairs before the first position one of its rows may not see take a
+// step without the mask and tail code.
 //
 // Matrix cores.  Scores: S^T[token][row] = K[token][:] . Q^T[:][row] with
 // v_mfma_f32_16x16x32_bf16 per block (K is the A operand, one 16-byte LDS
