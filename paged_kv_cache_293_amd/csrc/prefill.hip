@@ -31,10 +31,13 @@
 // v_mfma_f32_16x16x32_bf16 per block (K is the A operand, one 16-byte LDS
 // read per lane, as in the decode kernel).  Output: O^T[dim][row] +=
 // V^T[dim][32 tokens] . P^T[32 tokens][row] with one v_mfma_f32_16x16x32_bf16
-// per 16 dims over the pair: lane group lg supplies tokens 4lg..4lg+3 of
-// each block of the pair (its 4 + 4 probabilities straight from the two score
-// tiles, and the matching 8-byte V^T reads), so the contraction runs at the
-// full-rate 32-deep instruction.  fp8 codes are converted to bf16 exactly
+// per 16 dims over the pair, so the contraction runs at the full-rate
+// 32-deep instruction; each lane's 8 probabilities come straight from the
+// two score tiles.  For bf16 the two score tiles each take half of both
+// blocks' tokens, so that a lane group's 8 probabilities are 8 consecutive
+// tokens of one block and its V^T operand is one 16-byte read (operand
+// order below); for one-byte codes tile 0 is block A and tile 1 block B,
+// and a lane group takes tokens 4lg..4lg+3 of each.  fp8 codes are converted to bf16 exactly
 // after the LDS read, and so are int8 codes; int4 codes are widened to bf16
 // biased by kI4Bias (as in the decode kernel: each lane reads its own run of
 // a tile), the bias taken out of the scores (kI4Bias times the query row's
@@ -78,25 +81,37 @@ template <int KVT, int D> struct PfGeom {
 // s_waitcnt immediate: vector-memory count <= N, no wait on the other counters.
 template <int N> constexpr int vmcnt_imm() { return (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14); }
 
-// LDS placement of the bf16 V^T tiles.  A V^T row (one dim, 16 tokens) is
-// 32 bytes, two 16-byte halves of 8 tokens; the PV operand read of a lane is
-// 8 bytes of row 16m + col, and the 32 lanes of one LDS cycle take rows
-// col = 0 .. 15, which 64 four-byte banks would map with rows col and col + 8
-// on the same banks.  Rows whose dim has bit 3 set therefore hold their two
-// halves swapped: row r's half h sits at half h ^ ((r >> 3) & 1).  As chunk
-// index (2r + h) in the tile, the 16-byte chunk stored at LDS chunk c is the
-// pool's chunk c ^ ((c >> 4) & 1).  One-byte codes (16-byte rows, 4-byte
-// reads) are read without conflicts as stored.
+// bf16 operand order over a pair.  The two score tiles of a pair do not
+// split it by block: in score tile T (0 or 1), MFMA row t = lane % 16 is
+// token 8 ((t & 7) >> 2) + 4T + (t & 3) of block t >> 3.  So lane group g
+// (lanes 16g .. 16g+15) of both score outputs holds tokens 8 (g & 1) .. +3
+// (tile 0) and +4 .. +7 (tile 1) of block g >> 1: 8 consecutive tokens of
+// one block, whose V^T entries are one 16-byte half of a V^T row.  The PV
+// operands are then one 16-byte LDS read each and the probabilities stay
+// where the score MFMAs leave them.  (One-byte codes keep tile 0 = block A,
+// tile 1 = block B, lane group g holding tokens 4g .. 4g+3 of each.)
+//
+// LDS placement of the bf16 K tiles.  A K tile is 16-byte chunks of 8
+// dims, 16 token rows per chunk group (256 bytes).  A score-operand read
+// takes, in the lanes t = 0 .. 15 of one lane group, token rows {0..3,
+// 8..11} (tile 0) or {4..7, 12..15} (tile 1) of one chunk group of block A
+// (t < 8) and the same rows of block B (t >= 8): with both tiles stored as
+// in the pool those 16 reads fall on 8 bank groups twice (measured on
+// gfx950 with the bank-conflict counter).  Block B's K tile therefore holds
+// its token rows o at o ^ 4: LDS chunk c of that tile is the pool's chunk
+// c ^ 4, and the 16 reads cover 16 distinct row slots (no conflicts,
+// measured).  V tiles, and every tile of one-byte codes, are stored as in
+// the pool (their reads do not conflict, measured).
 template <int KVT>
-__device__ __forceinline__ int pf_v_chunk(int c) {
-    if constexpr (KVT == KV_BF16) return c ^ ((c >> 4) & 1);
+__device__ __forceinline__ int pf_k_chunk(int c, int block_b) {
+    if constexpr (KVT == KV_BF16) return block_b ? c ^ 4 : c;
     else return c;
 }
 
 // Copy one pair (blocks A and B) of this KV head into an LDS stage: this
 // wave's share of the 1 KiB pieces, 16 bytes per lane, straight into LDS by
 // buffer_load ... lds (the lane's 16 bytes land at LDS offset lane * 16 of
-// the piece; V tiles take their chunks in the order pf_v_chunk gives).  A
+// the piece; K tiles take their chunks in the order pf_k_chunk gives).  A
 // piece lies in one block (tiles 0-1 of the pair are block A's K and V, 2-3
 // block B's; a piece spans two tiles only when tiles are 512 bytes, int4 at
 // head dim 64, and then both are one block's), so each load goes through
@@ -108,7 +123,7 @@ __device__ __forceinline__ int pf_piece_offset(int k, int wave, int lane) {
     const int at = (wave + kPfWaves * k) * 1024 + lane * 16;   // byte of the pair in LDS
     const int tile = at / Gm::TILE;
     const int c = (at - tile * Gm::TILE) / 16;
-    return (tile & 1) * Gm::TILE + ((tile & 1) ? pf_v_chunk<KVT>(c) : c) * 16;
+    return (tile & 1) * Gm::TILE + ((tile & 1) ? c : pf_k_chunk<KVT>(c, tile >> 1)) * 16;
 }
 
 template <int KVT, int D>
@@ -154,16 +169,37 @@ __device__ __forceinline__ void pf_k_regs(TileRegs<KVT, D>& t, const uint8_t* ti
     }
 }
 
-// V^T operand of dims 16m .. 16m+15 over the pair: this lane's dim 16m +
-// lane % 16, tokens 4lg .. 4lg+3 of block A then of block B, as 8 bf16.
+// bf16 score operand of tile T of the pair in an LDS stage (operand order
+// above): lane (t, lg) reads token row o of block t >> 3, dims 32s + 8lg ..
+// +7 for k-step s.
+template <int D>
+__device__ __forceinline__ void pf_k_regs_bf16(TileRegs<KV_BF16, D>& r, const uint8_t* stage, int T, int lane) {
+    using Gm = PfGeom<KV_BF16, D>;
+    const int t = lane & 15;
+    const int o = 8 * ((t & 7) >> 2) + 4 * T + (t & 3);
+    const int b = t >> 3;
+    const uint8_t* base = stage + b * 2 * Gm::TILE + (lane >> 4) * 256 + pf_k_chunk<KV_BF16>(o, b) * 16;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) r.k[s] = *reinterpret_cast<const u32x4*>(base + 1024 * s);
+}
+
+// Position in the pair of score value i of lane group lg in score tile T.
+template <int KVT>
+__device__ __forceinline__ int pf_token(int T, int lg, int i) {
+    if constexpr (KVT == KV_BF16) return 16 * (lg >> 1) + 8 * (lg & 1) + 4 * T + i;
+    else return 16 * T + 4 * lg + i;
+}
+
+// V^T operand of dims 16m .. 16m+15 over the pair, this lane's dim 16m +
+// lane % 16.  bf16: tokens 8 (lg & 1) .. +7 of block lg >> 1, one 16-byte
+// read; one-byte codes: tokens 4lg .. 4lg+3 of block A then of block B, as
+// 8 bf16.
 template <int KVT, int D>
 __device__ __forceinline__ u32x4 pf_v_op(const uint8_t* va, const uint8_t* vb, int m, int col, int lg) {
     if constexpr (KVT == KV_BF16) {
-        // tokens 4lg .. +3: half lg >> 1 (swapped in rows with dim bit 3), 8 bytes in
-        const int off = (16 * m + col) * 32 + (((lg >> 1) ^ ((col >> 3) & 1)) << 4) + (lg & 1) * 8;
-        const u32x2 x = *reinterpret_cast<const u32x2*>(va + off);
-        const u32x2 y = *reinterpret_cast<const u32x2*>(vb + off);
-        return u32x4{x[0], x[1], y[0], y[1]};
+        // half lg & 1 of the row
+        const int off = (16 * m + col) * 32 + ((lg & 1) << 4);
+        return *reinterpret_cast<const u32x4*>(((lg >> 1) ? vb : va) + off);
     } else {
         const int off = (16 * m + col) * 16 + lg * 4;
         const unsigned x = *reinterpret_cast<const unsigned*>(va + off);
@@ -217,11 +253,8 @@ __device__ __forceinline__ void pf_zero_v_tail(uint8_t* stage, int t0, int n, in
         const int dim = r - blk * D;
         const int cut = n - (t0 + 16 * blk);          // tokens of this block below n
         uint8_t* row = stage + (2 * blk + 1) * Gm::TILE + dim * 16 * Gm::EB;
-        for (int o = max(cut, 0); o < 16; ++o) {
-            // byte of token o in the row as placed in LDS (see pf_v_chunk)
-            const int at = Gm::EB == 2 ? ((((o >> 3) ^ ((dim >> 3) & 1)) << 4) + (o & 7) * 2) : o;
-            for (int b = 0; b < Gm::EB; ++b) row[at + b] = 0;
-        }
+        for (int o = max(cut, 0); o < 16; ++o)
+            for (int b = 0; b < Gm::EB; ++b) row[o * Gm::EB + b] = 0;
     }
 }
 
@@ -388,9 +421,14 @@ void attn_prefill_kernel(PrefillArgs a) {
             pf_zero_v_tail<KVT, D>(st, t0, n, tid);
             __syncthreads();
         }
-        TileRegs<KVT, D> ka, kb;
-        pf_k_regs<KVT, D>(ka, st, lane);
-        pf_k_regs<KVT, D>(kb, st + 2 * Gm::TILE, lane);
+        TileRegs<KVT, D> ka, kb;   // the two score tiles' K operands
+        if constexpr (KVT == KV_BF16) {
+            pf_k_regs_bf16<D>(ka, st, 0, lane);
+            pf_k_regs_bf16<D>(kb, st, 1, lane);
+        } else {
+            pf_k_regs<KVT, D>(ka, st, lane);
+            pf_k_regs<KVT, D>(kb, st + 2 * Gm::TILE, lane);
+        }
         u32x4 pop[kPfNT];
         float alpha[kPfNT];
         bool rescale = false;
@@ -406,8 +444,8 @@ void attn_prefill_kernel(PrefillArgs a) {
             if constexpr (MASKED) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    if (t0 + 4 * lg + i >= lim[c]) sa[i] = neg_inf();
-                    if (t0 + 16 + 4 * lg + i >= lim[c]) sb[i] = neg_inf();
+                    if (t0 + pf_token<KVT>(0, lg, i) >= lim[c]) sa[i] = neg_inf();
+                    if (t0 + pf_token<KVT>(1, lg, i) >= lim[c]) sb[i] = neg_inf();
                 }
             }
             // Running max in exp2 units, kept stale: it moves (and the
