@@ -277,11 +277,13 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     // int4 and int8: scores come out biased by the code bias times the sum of
     // the query row
     float qbias[NT];
+    float qbs[NT];   // the bias scaled (int4, int8: taken out of the scaled scores)
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
         if constexpr (KVT == KV_INT4) qbias[c] = kI4Bias * query_row_sum<D>(qr[c])[0];
         else if constexpr (KVT == KV_INT8) qbias[c] = kI8Bias * query_row_sum<D>(qr[c])[0];   // units of kI8QScale
         else qbias[c] = 0.f;
+        qbs[c] = qbias[c] * sscale;
     }
     const int mask_from = n - kq + 1;
 
@@ -337,13 +339,17 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             const int t1 = min(hi, blk * kBlock + kBlock);
             for (int t = t0; t < t1; ++t) tr.put_token(t - blk * kBlock, stage + (t - lo) * STOK, lane);
         }
+        // Scaled scores (int4, int8: still biased by qbs).  The scaling reads
+        // the score products' results in their own basic block, where the
+        // compiler pads the matrix-core result latency; a first read after the
+        // mask branch below was found unpadded on the branch-taken path.
         f32x4 s[NT];
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
             if constexpr (KVT == KV_INT8) s[c] = scores_i8<D>(tr, qr[c]);
             else s[c] = scores<D>(tr, qr[c]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[c][i] = (s[c][i] - qbias[c]) * sscale;
+            for (int i = 0; i < 4; ++i) s[c][i] *= sscale;
         }
         const int tok0 = blk * kBlock + 4 * lg;
         if (blk * kBlock + kBlock > mask_from) {
@@ -359,7 +365,8 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
         float alpha[NT];
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
-            const float mx = max_over_rows(smax(smax(s[c][0], s[c][1]), smax(s[c][2], s[c][3])));
+            float mx = max_over_rows(smax(smax(s[c][0], s[c][1]), smax(s[c][2], s[c][3])));
+            if constexpr (KVT == KV_INT4 || KVT == KV_INT8) mx -= qbs[c];   // (-inf: all masked)
             // The running max is a lagging reference: it moves only when a
             // score exceeds it by more than kLazyMax, so probabilities stay
             // <= 2^kLazyMax and the accumulators are rescaled on few blocks.
@@ -368,8 +375,9 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             const float mnew = grow ? mx : m_run[c];
             const float muse = (mnew == neg_inf()) ? 0.f : mnew;
             alpha[c] = grow ? fast_exp2(m_run[c] - muse) : 1.f;
+            const float off = (KVT == KV_INT4 || KVT == KV_INT8) ? qbs[c] + muse : muse;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p[c][i] = fast_exp2(s[c][i] - muse);
+            for (int i = 0; i < 4; ++i) p[c][i] = fast_exp2(s[c][i] - off);
             if constexpr (KVT == KV_F32) {
                 float psum = 0.f;
 #pragma unroll

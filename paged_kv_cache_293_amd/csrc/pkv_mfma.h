@@ -315,9 +315,11 @@ constexpr float kI4Bias = 136.f;
 // Biased nibbles of w split by parity: byte k of `even` holds u of nibble
 // 2k, byte k of `odd` that of nibble 2k + 1.
 __device__ __forceinline__ void i4_split(unsigned w, unsigned& even, unsigned& odd) {
-    const unsigned x = w ^ 0x88888888u;
-    even = x & 0x0f0f0f0fu;
-    odd = (x >> 4) & 0x0f0f0f0fu;
+    // (w ^ 0x88888888) & 0x0f0f0f0f and its shifted twin, each one
+    // three-operand bit operation (the shift goes first, so the two do not
+    // share an intermediate)
+    even = (w ^ 0x88888888u) & 0x0f0f0f0fu;
+    odd = ((w >> 4) ^ 0x08888888u) & 0x0f0f0f0fu;
 }
 
 // bf16 pair of bytes 2h and 2h + 1 of x (biased nibbles): bits 0x43 | u each.
@@ -372,8 +374,18 @@ template <int D> struct TileRegs<KV_F32, D> {
 // dims matching the K chunk each lane group holds.
 template <int KVT, int D> struct QRegs;
 
+// Sign flip of every 16-bit value in a 16-byte operand register.
+template <class V>
+__device__ __forceinline__ V flip16(const V& v) {
+    return __builtin_bit_cast(V, __builtin_bit_cast(u32x4, v) ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u});
+}
+
 template <int D> struct QRegs<KV_BF16, D> {
     bf16x8 q[D / 32];   // step s: dims (4s + lane/16) * 8 .. +8
+    __device__ __forceinline__ void negate() {
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) q[s] = flip16(q[s]);
+    }
     __device__ __forceinline__ void load(const uint16_t* row, bool valid, int lane) {
 #pragma unroll
         for (int s = 0; s < D / 32; ++s) {
@@ -386,6 +398,10 @@ template <int D> struct QRegs<KV_BF16, D> {
 
 template <int D> struct QRegs1B {
     bf16x8 q[D / 32];   // step 2r + hh: dims (4r + lane/16) * 16 + 8 hh .. +8
+    __device__ __forceinline__ void negate() {
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) q[s] = flip16(q[s]);
+    }
     __device__ __forceinline__ void load(const uint16_t* row, bool valid, int lane) {
 #pragma unroll
         for (int st = 0; st < D / 32; ++st) {
@@ -417,6 +433,10 @@ template <int D> struct QRegs<KV_INT4, D> : QRegs<KV_BF16, D> {
 
 template <int D> struct QRegs<KV_F32, D> {
     f32x4 q[D / 16];    // r: dims (4r + lane/16) * 4 .. +4, one MFMA per element
+    __device__ __forceinline__ void negate() {
+#pragma unroll
+        for (int r = 0; r < D / 16; ++r) q[r] = -q[r];
+    }
     __device__ __forceinline__ void load(const float* row, bool valid, int lane) {
 #pragma unroll
         for (int r = 0; r < D / 16; ++r)
@@ -473,6 +493,10 @@ __device__ __forceinline__ f32x4 scores(const TileRegs<KV_INT8, D>& t, const QRe
 constexpr float kI8QScale = 1.f / 256.f;
 template <int D> struct QRegsI8 {
     f16x8 q[D / 32];
+    __device__ __forceinline__ void negate() {
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) q[s] = flip16(q[s]);
+    }
     __device__ __forceinline__ void load(const uint16_t* row, bool valid, int lane) {
 #pragma unroll
         for (int st = 0; st < D / 32; ++st) {

@@ -322,6 +322,13 @@ void attn_prefill_kernel(PrefillArgs a) {
         sscale *= a.k_scale[a.layer * H + h];
         vscale = a.v_scale[a.layer * H + h];
     }
+    // Scores are scaled inside the exponent and a row's maximum scaled score
+    // comes from its maximum raw score, which needs a positive factor: a
+    // negative one moves its sign into the query, a zero one becomes the
+    // smallest normal float (scaled scores round to 0 against the offset,
+    // masked ones still give -inf).
+    const bool qneg = sscale < 0.f;
+    sscale = sscale == 0.f ? 1.17549435e-38f : fabsf(sscale);
 
     QRegs<KVT, D> qr[kPfNT];
     int lim[kPfNT];
@@ -334,12 +341,16 @@ void attn_prefill_kernel(PrefillArgs a) {
         const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) +
             ((static_cast<int64_t>(q0) + j) * a.num_q_heads + h * G + g) * D;
         qr[c].load(qrow, valid, lane);
+        if (qneg) qr[c].negate();
         lim[c] = CASCADE ? n : (valid ? first + j + 1 : 0);
     }
     // int4: kI4Bias times each query row's sum (the bias of its scores)
-    float qbias[kPfNT];
+    float qbias[kPfNT], qbs[kPfNT];   // qbs: the bias scaled
 #pragma unroll
-    for (int c = 0; c < kPfNT; ++c) qbias[c] = KVT == KV_INT4 ? kI4Bias * query_row_sum<D>(qr[c])[0] : 0.f;
+    for (int c = 0; c < kPfNT; ++c) {
+        qbias[c] = KVT == KV_INT4 ? kI4Bias * query_row_sum<D>(qr[c])[0] : 0.f;
+        qbs[c] = qbias[c] * sscale;
+    }
 
     // o: unnormalised output per (column tile, 16 dims); ol: the row sums of
     // the bf16 probabilities, accumulated by the matrix cores against a tile
@@ -434,13 +445,10 @@ void attn_prefill_kernel(PrefillArgs a) {
         bool rescale = false;
 #pragma unroll
         for (int c = 0; c < kPfNT; ++c) {
+            // raw scores (int4: biased by kI4Bias times the query row's sum,
+            // taken out in the exponent's offset and in the maximum)
             f32x4 sa = scores<D>(ka, qr[c]);
             f32x4 sb = scores<D>(kb, qr[c]);
-            if constexpr (KVT == KV_INT4) {
-                // int4 scores come out biased by kI4Bias times the query row's sum
-#pragma unroll
-                for (int i = 0; i < 4; ++i) { sa[i] -= qbias[c]; sb[i] -= qbias[c]; }
-            }
             if constexpr (MASKED) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -453,7 +461,7 @@ void attn_prefill_kernel(PrefillArgs a) {
             // than kLazyMax, so probabilities stay <= 2^kLazyMax.  O and its
             // row sum share the same max, so O / sum is unchanged.
             float mx = smax(smax(smax(sa[0], sa[1]), smax(sa[2], sa[3])), smax(smax(sb[0], sb[1]), smax(sb[2], sb[3])));
-            mx = max_over_rows(mx) * sscale;
+            mx = (max_over_rows(mx) - qbias[c]) * sscale;
             alpha[c] = 1.f;
             if (mx > m_run[c] + kLazyMax) {
                 alpha[c] = fast_exp2(m_run[c] - mx);
@@ -462,11 +470,12 @@ void attn_prefill_kernel(PrefillArgs a) {
             }
             // (every score of an unmasked pair is finite, so the max is too)
             const float muse = MASKED && m_run[c] == neg_inf() ? 0.f : m_run[c];
+            const float off = -(qbs[c] + muse);
             float pa[4], pb[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pa[i] = fast_exp2(__builtin_fmaf(sa[i], sscale, -muse));
-                pb[i] = fast_exp2(__builtin_fmaf(sb[i], sscale, -muse));
+                pa[i] = fast_exp2(__builtin_fmaf(sa[i], sscale, off));
+                pb[i] = fast_exp2(__builtin_fmaf(sb[i], sscale, off));
             }
             pop[c] = u32x4{pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3]), pack_bf16x2(pb[0], pb[1]),
                            pack_bf16x2(pb[2], pb[3])};
