@@ -358,9 +358,12 @@ void attn_prefill_kernel(PrefillArgs a) {
     f32x4 o[kPfNT][D / 16];
     f32x4 ol[kPfNT];
     float m_run[kPfNT];
+    float thr[kPfNT];   // raw score above which a column's reference must move
+    const float inv_sscale = 1.f / sscale;
 #pragma unroll
     for (int c = 0; c < kPfNT; ++c) {
         m_run[c] = neg_inf();
+        thr[c] = neg_inf();
         ol[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < D / 16; ++m) o[c][m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -441,8 +444,6 @@ void attn_prefill_kernel(PrefillArgs a) {
             pf_k_regs<KVT, D>(kb, st + 2 * Gm::TILE, lane);
         }
         u32x4 pop[kPfNT];
-        float alpha[kPfNT];
-        bool rescale = false;
 #pragma unroll
         for (int c = 0; c < kPfNT; ++c) {
             // raw scores (int4: biased by kI4Bias times the query row's sum,
@@ -459,14 +460,22 @@ void attn_prefill_kernel(PrefillArgs a) {
             // Running max in exp2 units, kept stale: it moves (and the
             // accumulators are rescaled) only when a score exceeds it by more
             // than kLazyMax, so probabilities stay <= 2^kLazyMax.  O and its
-            // row sum share the same max, so O / sum is unchanged.
-            float mx = smax(smax(smax(sa[0], sa[1]), smax(sa[2], sa[3])), smax(smax(sb[0], sb[1]), smax(sb[2], sb[3])));
-            mx = (max_over_rows(mx) - qbias[c]) * sscale;
-            alpha[c] = 1.f;
-            if (mx > m_run[c] + kLazyMax) {
-                alpha[c] = fast_exp2(m_run[c] - mx);
-                m_run[c] = mx;
-                rescale = true;
+            // row sum share the same max, so O / sum is unchanged.  Each lane
+            // compares its own 8 raw scores with the column's threshold
+            // (the reference plus kLazyMax, in raw units); only when some
+            // lane exceeds it does the wave reduce the columns' maxima across
+            // lanes and move the reference.
+            const float ml = smax(smax(smax(sa[0], sa[1]), smax(sa[2], sa[3])), smax(smax(sb[0], sb[1]), smax(sb[2], sb[3])));
+            if (__ballot(ml > thr[c])) {
+                const float mx = (max_over_rows(ml) - qbias[c]) * sscale;
+                if (mx > m_run[c] + kLazyMax) {
+                    const float alpha = fast_exp2(m_run[c] - mx);
+                    m_run[c] = mx;
+                    ol[c] *= alpha;
+#pragma unroll
+                    for (int m = 0; m < D / 16; ++m) o[c][m] *= alpha;
+                }
+                thr[c] = m_run[c] == neg_inf() ? neg_inf() : (m_run[c] + kLazyMax) * inv_sscale + qbias[c];
             }
             // (every score of an unmasked pair is finite, so the max is too)
             const float muse = MASKED && m_run[c] == neg_inf() ? 0.f : m_run[c];
@@ -479,14 +488,6 @@ void attn_prefill_kernel(PrefillArgs a) {
             }
             pop[c] = u32x4{pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3]), pack_bf16x2(pb[0], pb[1]),
                            pack_bf16x2(pb[2], pb[3])};
-        }
-        if (__ballot(rescale)) {
-#pragma unroll
-            for (int c = 0; c < kPfNT; ++c) {
-                ol[c] *= alpha[c];
-#pragma unroll
-                for (int m = 0; m < D / 16; ++m) o[c][m] *= alpha[c];
-            }
         }
 #pragma unroll
         for (int c = 0; c < kPfNT; ++c)
