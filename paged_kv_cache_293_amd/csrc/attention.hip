@@ -277,13 +277,13 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     // int4 and int8: scores come out biased by the code bias times the sum of
     // the query row
     float qbias[NT];
-    float qbs[NT];   // the bias scaled (int4, int8: taken out of the scaled scores)
+    float qbs[NT];   // the bias scaled (int4, int8: taken out of the scaled scores; otherwise 0)
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
         if constexpr (KVT == KV_INT4) qbias[c] = kI4Bias * query_row_sum<D>(qr[c])[0];
         else if constexpr (KVT == KV_INT8) qbias[c] = kI8Bias * query_row_sum<D>(qr[c])[0];   // units of kI8QScale
         else qbias[c] = 0.f;
-        qbs[c] = qbias[c] * sscale;
+        qbs[c] = (KVT == KV_INT4 || KVT == KV_INT8) ? qbias[c] * sscale : 0.f;
     }
     const int mask_from = n - kq + 1;
 
@@ -293,10 +293,12 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
     // (lacc: every element holds the row's sum of the values used).
     f32x4 o[NT][D / 16];
     float m_run[NT], l_run[NT];
+    float thr[NT];   // scaled (biased) score above which a column's reference must move
     f32x4 lacc[NT];
 #pragma unroll
     for (int c = 0; c < NT; ++c) {
         m_run[c] = neg_inf();
+        thr[c] = neg_inf();
         l_run[c] = 0.f;
         lacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -339,18 +341,19 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             const int t1 = min(hi, blk * kBlock + kBlock);
             for (int t = t0; t < t1; ++t) tr.put_token(t - blk * kBlock, stage + (t - lo) * STOK, lane);
         }
-        // Scaled scores (int4, int8: still biased by qbs).  The scaling reads
-        // the score products' results in their own basic block, where the
-        // compiler pads the matrix-core result latency; a first read after the
-        // mask branch below was found unpadded on the branch-taken path.
+        // Scaled scores (int4, int8: still biased by qbs).  The products'
+        // results pass through mfma_result_pad before any other use.
         f32x4 s[NT];
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
             if constexpr (KVT == KV_INT8) s[c] = scores_i8<D>(tr, qr[c]);
             else s[c] = scores<D>(tr, qr[c]);
+        }
+        mfma_result_pad<NT>(s);
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) s[c][i] *= sscale;
-        }
         const int tok0 = blk * kBlock + 4 * lg;
         if (blk * kBlock + kBlock > mask_from) {
 #pragma unroll
@@ -361,38 +364,39 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
         }
         if (blk * kBlock + kBlock > n) tr.zero_v_from(n - tok0);
         f32x4 p[NT];
-        bool rescale = false;
-        float alpha[NT];
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
-            float mx = max_over_rows(smax(smax(s[c][0], s[c][1]), smax(s[c][2], s[c][3])));
-            if constexpr (KVT == KV_INT4 || KVT == KV_INT8) mx -= qbs[c];   // (-inf: all masked)
             // The running max is a lagging reference: it moves only when a
             // score exceeds it by more than kLazyMax, so probabilities stay
             // <= 2^kLazyMax and the accumulators are rescaled on few blocks.
             // O and l share the reference, so O / l does not depend on it.
-            const bool grow = mx > m_run[c] + kLazyMax;   // a row's first finite score always grows it
-            const float mnew = grow ? mx : m_run[c];
-            const float muse = (mnew == neg_inf()) ? 0.f : mnew;
-            alpha[c] = grow ? fast_exp2(m_run[c] - muse) : 1.f;
-            const float off = (KVT == KV_INT4 || KVT == KV_INT8) ? qbs[c] + muse : muse;
+            // Each lane compares its own 4 scores with the column's threshold
+            // (reference + kLazyMax, in the scores' biased units); only when
+            // some lane passes it does the wave reduce the column maxima
+            // across lanes and move the reference (a row's first finite
+            // score always does).
+            const float ml = smax(smax(s[c][0], s[c][1]), smax(s[c][2], s[c][3]));
+            if (__ballot(ml > thr[c])) {
+                const float mx = max_over_rows(ml) - qbs[c];
+                if (mx > m_run[c] + kLazyMax) {
+                    const float alpha = fast_exp2(m_run[c] - mx);
+                    m_run[c] = mx;
+                    lacc[c] *= alpha;
+                    l_run[c] *= alpha;
+#pragma unroll
+                    for (int m = 0; m < D / 16; ++m) o[c][m] *= alpha;
+                }
+                thr[c] = m_run[c] + kLazyMax + qbs[c];
+            }
+            const float muse = m_run[c] == neg_inf() ? 0.f : m_run[c];
+            const float off = qbs[c] + muse;
 #pragma unroll
             for (int i = 0; i < 4; ++i) p[c][i] = fast_exp2(s[c][i] - off);
             if constexpr (KVT == KV_F32) {
                 float psum = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) psum += p[c][i];
-                l_run[c] = l_run[c] * alpha[c] + psum;
-            }
-            m_run[c] = mnew;
-            rescale |= grow;
-        }
-        if (__ballot(rescale)) {
-#pragma unroll
-            for (int c = 0; c < NT; ++c) {
-                lacc[c] *= alpha[c];
-#pragma unroll
-                for (int m = 0; m < D / 16; ++m) o[c][m] *= alpha[c];
+                l_run[c] += psum;
             }
         }
         if constexpr (KVT == KV_INT8) {
