@@ -1,0 +1,123 @@
+"""CPU: matrix-core result reads in the built gfx950 code.
+
+A vector (VALU) instruction may read a register written by a matrix-core
+(MFMA) instruction only after some wait states.  The compiler pads such
+reads inside a basic block; a read placed just past a branch was found
+unpadded on the branch-taken path, and the kernel then read stale score
+values.  The kernels pad their score tiles explicitly (mfma_result_pad).
+
+This test disassembles the gfx950 code object of the built library (the
+library built here, with the ROCm tools of this image) and follows every
+path from each MFMA instruction (fall-through and branch targets, up to 16
+instructions), counting wait states (s_nop N counts N + 1, any other
+instruction 1).  A VALU read of the MFMA's destination with fewer than 8
+wait states fails the test; 8 is the padding the compiler itself emits in
+front of such a read in one basic block.
+"""
+
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "paged_kv_cache_293_amd", "lib", "libpagedkv.so")
+LLVM = "/opt/rocm/llvm/bin"
+REQUIRED_WAIT_STATES = 8
+PATH_LENGTH = 16
+
+
+def _disassemble(tmp):
+    fatbin = os.path.join(tmp, "fatbin")
+    code = os.path.join(tmp, "gfx950.co")
+    subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fatbin}", LIB], check=True)
+    subprocess.run([os.path.join(LLVM, "clang-offload-bundler"), "--type=o",
+                    "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--input={fatbin}", f"--output={code}",
+                    "--unbundle"], check=True)
+    out = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", code], check=True,
+                         capture_output=True, text=True)
+    return out.stdout.splitlines()
+
+
+def _instructions(lines):
+    ins, index, syms = [], {}, {}
+    func = None
+    pat = re.compile(r"\s+(\S+)\s*(.*?)\s*//\s*([0-9A-Fa-f]+):[^<]*(?:<(\S+?)(?:\+0x([0-9a-f]+))?>)?")
+    for line in lines:
+        m = re.match(r"^([0-9a-f]+) <(\S+)>:", line)
+        if m:
+            syms[m.group(2)] = int(m.group(1), 16)
+            func = m.group(2)
+            continue
+        m = pat.match(line)
+        if not m:
+            continue
+        target = None
+        if m.group(4) in syms:
+            target = syms[m.group(4)] + (int(m.group(5), 16) if m.group(5) else 0)
+        index[int(m.group(3), 16)] = len(ins)
+        ins.append((m.group(1), m.group(2), target, func))
+    return ins, index
+
+
+def _vgprs(token):
+    token = token.strip().split(" ")[0] if token.strip() else ""
+    m = re.match(r"v\[(\d+):(\d+)\]$", token)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", token)
+    return {int(m.group(1))} if m else set()
+
+
+def _early_reads(ins, index):
+    found = []
+
+    def walk(i, dst, waits, depth, source):
+        steps = 0
+        while i < len(ins) and steps < PATH_LENGTH:
+            op, args, target, func = ins[i]
+            if op == "s_nop":
+                waits += int(args.split()[0], 0) + 1
+                i += 1
+                steps += 1
+                continue
+            if op.startswith("v_") and not op.startswith("v_mfma"):
+                read = set()
+                for tok in args.split(",")[1:]:
+                    read |= _vgprs(tok)
+                if read & dst:
+                    if waits < REQUIRED_WAIT_STATES:
+                        found.append((func, source, f"{op} {args}", waits))
+                    return
+            if op == "s_endpgm":
+                return
+            if op.startswith("s_cbranch") and target in index and depth < 3:
+                walk(index[target], dst, waits + 1, depth + 1, source)
+            if op == "s_branch":
+                if target in index and depth < 3:
+                    walk(index[target], dst, waits + 1, depth + 1, source)
+                return
+            waits += 1
+            i += 1
+            steps += 1
+
+    for i, (op, args, _, _) in enumerate(ins):
+        if op.startswith("v_mfma"):
+            walk(i + 1, _vgprs(args.split(",")[0]), 0, 0, f"{op} {args}")
+    return found
+
+
+def test_matrix_core_results_are_padded():
+    if not os.path.exists(LIB):
+        pytest.skip("library not built")
+    tools = [shutil.which("objcopy"), os.path.join(LLVM, "clang-offload-bundler"), os.path.join(LLVM, "llvm-objdump")]
+    if not all(t and os.path.exists(t) for t in tools):
+        pytest.skip("ROCm binary tools not available")
+    with tempfile.TemporaryDirectory() as tmp:
+        ins, index = _instructions(_disassemble(tmp))
+    assert sum(1 for op, _, _, _ in ins if op.startswith("v_mfma")) > 1000, "no matrix-core code found"
+    early = _early_reads(ins, index)
+    assert not early, f"{len(early)} MFMA results read with too few wait states, e.g. {early[:3]}"
