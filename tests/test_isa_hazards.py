@@ -33,7 +33,9 @@ PATH_LENGTH = 16
 def _disassemble(tmp):
     fatbin = os.path.join(tmp, "fatbin")
     code = os.path.join(tmp, "gfx950.co")
-    subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fatbin}", LIB], check=True)
+    # (an explicit output file: without one objcopy rewrites its input in place)
+    subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fatbin}", LIB, os.path.join(tmp, "copy.so")],
+                   check=True)
     subprocess.run([os.path.join(LLVM, "clang-offload-bundler"), "--type=o",
                     "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--input={fatbin}", f"--output={code}",
                     "--unbundle"], check=True)
