@@ -18,11 +18,11 @@
 // 16-row column tiles, with their queries resident in registers; the rest of
 // its state fits in 256 VGPRs, so two work-groups share a CU and their waves
 // interleave softmax (VALU) and matrix work on each SIMD.  The K/V of
-// the visible blocks stream through a three-stage LDS ring, two blocks (a
+// the visible blocks stream through a four-stage LDS ring, two blocks (a
 // "pair") per stage, copied straight from the pool into LDS by 16-byte
 // buffer loads with the LDS as destination (no register staging; one buffer
 // resource per block, loop-invariant lane offsets); each wave issues its
-// share of the pair two steps ahead, and one barrier per pair publishes it.
+// share of the pair three steps ahead, and one barrier per pair publishes it.
 // The block ids are read with scalar loads, a pair ahead of their use.  A
 // wave's pairs before the first position one of its rows may not see take a
 // step without the mask and tail code.
@@ -59,7 +59,7 @@ namespace {
 constexpr int kPfWaves = 4;
 constexpr int kPfNT = kPrefillRows / (16 * kPfWaves);   // column tiles per wave (3)
 #ifndef PKV_PREFILL_STAGES
-#define PKV_PREFILL_STAGES 3
+#define PKV_PREFILL_STAGES 4
 #endif
 constexpr int kPfStages = PKV_PREFILL_STAGES;           // LDS ring of block pairs
 constexpr int kPfAhead = kPfStages - 1;                 // pairs in flight ahead of the one computed
