@@ -332,11 +332,13 @@ int32_t max_prefix_blocks(const pkv_pool* pool, const int32_t* seq_lens, int32_t
     return m >= pkv::kCascadeMinBlocks ? m : 0;
 }
 
-// A shared-prefix plan: one unit per sequence over its own blocks (after
-// the prefix), prefix_chunks leading partials per sequence.
+// A shared-prefix plan: each sequence's own blocks (after the prefix) cut
+// as the balanced plan cuts whole sequences (one unit when the batch fills
+// the device, near-equal parts when few long sequences do not), with
+// prefix_chunks leading partials per sequence.
 bool build_cascade_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads,
                         int32_t wgs_per_cu, int32_t prefix_blocks, int32_t prefix_chunks, Plan* C) {
-    return build_plan(seq_lens, num_seqs, max_blocks, 0, num_kv_heads, wgs_per_cu, C, prefix_blocks, prefix_chunks);
+    return build_plan(seq_lens, num_seqs, max_blocks, -1, num_kv_heads, wgs_per_cu, C, prefix_blocks, prefix_chunks);
 }
 
 // Prefix chunks: at most kCascadeMaxChunks, each of at least
@@ -421,9 +423,9 @@ size_t block_table_device_bytes(const pkv_pool* pool, const int32_t* host_seq_le
         if (!build_plan(host_seq_lens, num_seqs, max_blocks_per_seq, partition_tokens, pool->desc.num_kv_heads, wpc,
                         &P))
             return 0;
-        // Room for a shared-prefix plan if the tables turn out to share one:
-        // the plan with the smallest prefix is the largest (one unit per
-        // sequence, ids for its longest own run).
+        // Room for a shared-prefix plan if the tables turn out to share one,
+        // sized for the smallest prefix (the most own blocks); an upload whose
+        // actual prefix plan would not fit keeps the plain plan.
         Plan C;
         const bool maybe = partition_tokens == -1 && max_prefix_blocks(pool, host_seq_lens, num_seqs) > 0 &&
                            build_cascade_plan(host_seq_lens, num_seqs, max_blocks_per_seq, pool->desc.num_kv_heads,
@@ -486,7 +488,11 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
         if (prefix) prefix_chunking(prefix, &chunk_blocks, &chunks);
         if (prefix && !build_cascade_plan(host_seq_lens, num_seqs, max_blocks_per_seq, hkv, wpc, prefix, chunks, &C))
             return PKV_ERR_INVALID;
-        const TableLayout L = table_layout(num_seqs, max_blocks_per_seq, hkv, P, prefix ? &C : nullptr);
+        TableLayout L = table_layout(num_seqs, max_blocks_per_seq, hkv, P, prefix ? &C : nullptr);
+        if (prefix && dev_buffer_bytes < L.total) {
+            prefix = 0;
+            L = table_layout(num_seqs, max_blocks_per_seq, hkv, P, nullptr);
+        }
         if (dev_buffer_bytes < L.total) return PKV_ERR_WORKSPACE;
 
         pkv_table* t = new pkv_table;

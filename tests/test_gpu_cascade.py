@@ -6,6 +6,7 @@ sequence's own blocks in one partition merged with the prefix partials.
 Covered: which tables get a prefix (its length, the chunk count, the
 refusals: fixed partitions, fewer than 4 sequences, a float32 pool, a prefix
 under 8 blocks), parity with the oracle over every dtype, both head dims,
+long private parts cut into several units per sequence,
 decode and verify rows, prefix chunks of even and odd block counts and the
 shortest sequence ending right where the rows still see the whole prefix; a
 call whose rows reach into the prefix (the plan then is not used) on the same
@@ -137,3 +138,19 @@ def test_shared_prefix_reduced_verify_config():
     b = s.run()
     assert torch.equal(a, b)
     assert_close(out_values(a), ref, w.kv_dtype, "c5s shared prefix")
+
+
+@pytest.mark.parametrize("kv,k", [("bf16", 1), ("fp8", 5), ("int4", 3)])
+def test_shared_prefix_with_long_own_parts(kv, k):
+    """Few sequences with long private parts: the plan cuts each sequence's
+    own blocks into several units (as the balanced plan cuts whole
+    sequences), merged with the prefix partials by the split merge."""
+    log(f"shared prefix, long own parts, {kv} k={k}")
+    rng = np.random.Generator(np.random.PCG64(29304 + k))
+    lens = 16 * 12 + np.array([3000, 4100, 2500, 3700]) + k
+    w = workloads.build(f"prefix-long-{kv}", 29304 + k, rng, lens, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                        kv_dtype=kv, k_rows=k, shared_prefix_tokens=16 * 12, materialize=True, partition_tokens=-1)
+    s = Setup(w, partition_tokens=-1)
+    assert s.table.shared_prefix() == (12, 1)
+    got = s.run()
+    assert_close(out_values(got), s.oracle(), kv, "long own parts")
