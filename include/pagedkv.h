@@ -165,7 +165,7 @@ pkv_status kv_pool_destroy(pkv_pool* pool);
 /*
  * Device bytes block_table_upload needs for this batch: the tables, the
  * lengths and the split-KV plan (which depends on the lengths, the pool's KV
- * head count and, for partition_tokens = -1, the device's CU count).  Same
+ * head count and, for partition_tokens = -1 or -2, the device's CU count).  Same
  * arguments as block_table_upload.  0 for invalid arguments.
  */
 size_t block_table_device_bytes(const pkv_pool* pool, const int32_t* host_seq_lens, int32_t num_seqs,
@@ -192,7 +192,7 @@ size_t block_table_device_bytes(const pkv_pool* pool, const int32_t* host_seq_le
  *                     attended independently and their partial results
  *                     merged (inside the attention kernel for up to 32
  *                     partitions, by a second kernel beyond that).
- *                     With -1 the upload also looks for a shared prefix (page
+ *                     With -1 or -2 the upload also looks for a shared prefix (page
  *                     "KV cache & continuous batching", section "4. Prefix
  *                     caching / prompt caching": requests with a common
  *                     prefix reuse its cached K/V; page "LLM Serving - KV
@@ -207,9 +207,14 @@ size_t block_table_device_bytes(const pkv_pool* pool, const int32_t* host_seq_le
  *                     attends to the prefix once for all sequences' query
  *                     rows (a dense pass over the shared blocks, in up to 4
  *                     chunks, each giving a partial result per row) and
- *                     walks only each sequence's own blocks, one partition
- *                     per sequence merged with the prefix partials: the
- *                     same softmax, split at the prefix end.
+ *                     walks only each sequence's own blocks, merged with
+ *                     the prefix partials: the
+ *                     same softmax, split at the prefix end.  With -1 the
+ *                     prefix plan is kept only when a rough cost model
+ *                     (the prefix pass's chunk walk against every
+ *                     sequence reading the prefix) favours it; -2 keeps it
+ *                     whenever a prefix is found.  Each sequence's own
+ *                     blocks are cut as the balanced plan cuts sequences.
  *   dev_buffer        device buffer of >= block_table_device_bytes(...) bytes;
  *                     it must stay valid and unmodified while the table is in use.
  * The host arrays are copied into the handle before returning; the copy to
@@ -239,7 +244,7 @@ pkv_status block_table_info(const pkv_table* table, int32_t* num_units, int32_t*
                             int32_t* max_seq_len, int32_t* min_seq_len, int32_t* max_parts);
 
 /*
- * The table's shared prefix (see block_table_upload, partition_tokens = -1):
+ * The table's shared prefix (see block_table_upload, partition_tokens = -1, -2):
  * its length in blocks and the chunks the prefix pass cuts it into; both 0
  * when the table has none.  Either output pointer may be NULL.
  */

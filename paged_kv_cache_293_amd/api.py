@@ -135,7 +135,9 @@ def block_table_upload(pool, block_tables, seq_lens, partition_tokens=-1, device
     """Validate and upload host block tables ([B][max_blocks] int32) and lengths ([B]).
 
     partition_tokens: a multiple of 16 for fixed split-KV partitions, 0 for
-    none, -1 (default) for the balanced plan.
+    none, -1 (default) for the balanced plan (with the shared-prefix plan
+    when the tables share a prefix and a cost estimate favours it), -2 for
+    the balanced plan with the shared-prefix plan whenever a prefix is found.
     """
     bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
     sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))

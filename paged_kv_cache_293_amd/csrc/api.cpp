@@ -321,6 +321,10 @@ TableLayout table_layout(int32_t num_seqs, int32_t max_blocks, int32_t num_kv_he
 
 pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
+// partition_tokens value: the balanced plan, and the shared-prefix plan
+// whenever the tables share a prefix (no cost estimate).
+constexpr int32_t kForcePrefixPlan = -2;
+
 // The largest shared prefix (in blocks) the lengths allow: every sequence
 // keeps at least one position past it.  0 when no shared-prefix plan can
 // arise (too few sequences, too short, or a float32 pool, which the prefix
@@ -349,6 +353,21 @@ void prefix_chunking(int32_t prefix_blocks, int32_t* chunk_blocks, int32_t* chun
     const int32_t per = (prefix_blocks + 2 * want - 1) / (2 * want) * 2;
     *chunk_blocks = per;
     *chunks = (prefix_blocks + per - 1) / per;
+}
+
+// Whether attending a shared prefix once for all rows should beat reading
+// it once per sequence, by a rough model of MI355X: a prefix-pass
+// work-group walks one chunk at about 2 us per block pair after about 5 us
+// of start-up (the pass's work-groups run side by side), while the plain
+// walk reads every sequence's reference to the prefix tiles at about
+// 6 TB/s.  (The model gives 37 against 90 us for 128 verify sequences
+// over a 2,048-token fp8 prefix, prefix plan; 69 against 11 us for four
+// bf16 sequences behind a 4,096-token prefix, plain plan.)
+bool prefix_plan_pays(const pkv_pool* pool, int32_t num_seqs, int32_t prefix_blocks, int32_t chunk_blocks) {
+    const double pass_us = 5.0 + 2.0 * (chunk_blocks / 2.0);
+    const double plain_us = static_cast<double>(num_seqs) * prefix_blocks * pool->desc.num_kv_heads * 2.0 *
+                            static_cast<double>(pool->tile_bytes) / 6.0e6;
+    return pass_us < plain_us;
 }
 
 }  // namespace
@@ -418,6 +437,8 @@ size_t block_table_device_bytes(const pkv_pool* pool, const int32_t* host_seq_le
                                 int32_t max_blocks_per_seq, int32_t partition_tokens) {
     try {
         if (!pool || !host_seq_lens) return 0;
+        const bool balanced = partition_tokens == -1 || partition_tokens == kForcePrefixPlan;
+        if (partition_tokens == kForcePrefixPlan) partition_tokens = -1;
         Plan P;
         const int32_t wpc = pkv::decode_wgs_per_cu(pool->desc.kv_dtype, pool->desc.head_dim);
         if (!build_plan(host_seq_lens, num_seqs, max_blocks_per_seq, partition_tokens, pool->desc.num_kv_heads, wpc,
@@ -427,7 +448,7 @@ size_t block_table_device_bytes(const pkv_pool* pool, const int32_t* host_seq_le
         // sized for the smallest prefix (the most own blocks); an upload whose
         // actual prefix plan would not fit keeps the plain plan.
         Plan C;
-        const bool maybe = partition_tokens == -1 && max_prefix_blocks(pool, host_seq_lens, num_seqs) > 0 &&
+        const bool maybe = balanced && max_prefix_blocks(pool, host_seq_lens, num_seqs) > 0 &&
                            build_cascade_plan(host_seq_lens, num_seqs, max_blocks_per_seq, pool->desc.num_kv_heads,
                                               wpc, pkv::kCascadeMinBlocks, 1, &C);
         return table_layout(num_seqs, max_blocks_per_seq, pool->desc.num_kv_heads, P, maybe ? &C : nullptr).total;
@@ -446,8 +467,10 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
         if (!pool || !host_block_table || !host_seq_lens || !dev_buffer) return PKV_ERR_INVALID;
         if (reinterpret_cast<uintptr_t>(dev_buffer) % kAlign) return PKV_ERR_INVALID;
         if (num_seqs < 1 || max_blocks_per_seq < 1) return PKV_ERR_INVALID;
-        if (partition_tokens < -1 || (partition_tokens > 0 && partition_tokens % PKV_BLOCK_SIZE))
+        if (partition_tokens < kForcePrefixPlan || (partition_tokens > 0 && partition_tokens % PKV_BLOCK_SIZE))
             return PKV_ERR_INVALID;
+        const bool force_prefix = partition_tokens == kForcePrefixPlan;
+        if (force_prefix) partition_tokens = -1;
         const int32_t nb_pool = pool->desc.num_blocks;
         const int32_t hkv = pool->desc.num_kv_heads;
         const int64_t cap = static_cast<int64_t>(max_blocks_per_seq) * PKV_BLOCK_SIZE;
@@ -486,6 +509,7 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
         Plan C;
         int32_t chunk_blocks = 0, chunks = 0;
         if (prefix) prefix_chunking(prefix, &chunk_blocks, &chunks);
+        if (prefix && !force_prefix && !prefix_plan_pays(pool, num_seqs, prefix, chunk_blocks)) prefix = 0;
         if (prefix && !build_cascade_plan(host_seq_lens, num_seqs, max_blocks_per_seq, hkv, wpc, prefix, chunks, &C))
             return PKV_ERR_INVALID;
         TableLayout L = table_layout(num_seqs, max_blocks_per_seq, hkv, P, prefix ? &C : nullptr);

@@ -1,7 +1,9 @@
-"""GPU: the shared-prefix plan.  A balanced upload (partition_tokens = -1)
-whose tables all start with the same physical blocks attends to that prefix
-once for every sequence's query rows (the prefix pass) and walks each
-sequence's own blocks in one partition merged with the prefix partials.
+"""GPU: the shared-prefix plan.  A balanced upload (partition_tokens = -1
+when a cost estimate favours it, -2 always) whose tables all start with the
+same physical blocks attends to that prefix once for every sequence's query
+rows (the prefix pass) and walks each sequence's own blocks, merged with the
+prefix partials.  The parity tests force the plan (-2) on batches small
+enough for the oracle.
 
 Covered: which tables get a prefix (its length, the chunk count, the
 refusals: fixed partitions, fewer than 4 sequences, a float32 pool, a prefix
@@ -33,7 +35,7 @@ def _prefix_workload(kv, d, Hq, Hkv, k, prefix_blocks, B, seed, exact_min=True):
     lens = 16 * prefix_blocks + suffix
     return workloads.build(f"prefix-{kv}", seed, rng, lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
                            kv_dtype=kv, k_rows=k, shared_prefix_tokens=16 * prefix_blocks,
-                           materialize=True, partition_tokens=-1)
+                           materialize=True, partition_tokens=-2)
 
 
 def _chunks(prefix_blocks):
@@ -58,7 +60,7 @@ CASES = [
 def test_shared_prefix_parity(kv, d, Hq, Hkv, k, pb, B):
     log(f"shared prefix {kv} d{d} {Hq}/{Hkv} k={k} prefix {pb} blocks, batch {B}")
     w = _prefix_workload(kv, d, Hq, Hkv, k, pb, B, seed=2930 + pb)
-    s = Setup(w, partition_tokens=-1)
+    s = Setup(w, partition_tokens=-2)
     assert s.table.shared_prefix() == (pb, _chunks(pb))
     got = s.run()
     ref = s.oracle()
@@ -80,7 +82,7 @@ def test_rows_reaching_into_the_prefix_use_the_plain_plan():
     w.seq_lens[2] = 16 * 20 + 2
     # the builder wrote sequence 2's positions for its original length; its
     # table row covers the shorter length as well
-    s = Setup(w, partition_tokens=-1)
+    s = Setup(w, partition_tokens=-2)
     assert s.table.shared_prefix() == (20, 1)
     got = s.run()
     assert_close(out_values(got), s.oracle(), "bf16", "verify reaching into the prefix")
@@ -97,32 +99,34 @@ def test_which_tables_get_a_prefix():
     import paged_kv_cache_293_amd as pk
     log("shared prefix detection")
     w = _prefix_workload("bf16", 64, 8, 2, 1, 20, 5, seed=29302)
-    s = Setup(w, partition_tokens=-1)
+    s = Setup(w, partition_tokens=-2)
     assert s.table.shared_prefix() == (20, 1)
-    # fixed partitions and whole sequences keep no prefix
+    # fixed partitions and whole sequences keep no prefix; the cost estimate
+    # (-1) turns down a prefix this small for five short sequences
     assert s.upload(128).shared_prefix() == (0, 0)
     assert s.upload(0).shared_prefix() == (0, 0)
+    assert s.upload(-1).shared_prefix() == (0, 0)
     # one row naming another block at block 12 shortens the prefix to 12 blocks
     free = np.setdiff1d(np.arange(w.num_blocks), w.block_tables[w.block_tables >= 0])
     bt = w.block_tables.copy()
     bt[3, 12] = free[0]
-    t = pk.block_table_upload(s.pool, bt, w.seq_lens, -1)
+    t = pk.block_table_upload(s.pool, bt, w.seq_lens, -2)
     assert t.shared_prefix() == (12, 1)
     # ... at block 7: under the 8-block minimum
     bt = w.block_tables.copy()
     bt[4, 7] = free[1]
-    assert pk.block_table_upload(s.pool, bt, w.seq_lens, -1).shared_prefix() == (0, 0)
+    assert pk.block_table_upload(s.pool, bt, w.seq_lens, -2).shared_prefix() == (0, 0)
     # three sequences are too few
-    assert pk.block_table_upload(s.pool, w.block_tables[:3], w.seq_lens[:3], -1).shared_prefix() == (0, 0)
+    assert pk.block_table_upload(s.pool, w.block_tables[:3], w.seq_lens[:3], -2).shared_prefix() == (0, 0)
     # a float32 pool takes no prefix pass
     f32 = pk.kv_pool_create(1, w.num_blocks, 2, 64, "f32")
-    assert pk.block_table_upload(f32, w.block_tables, w.seq_lens, -1).shared_prefix() == (0, 0)
+    assert pk.block_table_upload(f32, w.block_tables, w.seq_lens, -2).shared_prefix() == (0, 0)
     # the prefix stops one position short of the shortest sequence's end
     lens = w.seq_lens.copy()
     lens[1] = 16 * 10 + 1
-    assert pk.block_table_upload(s.pool, w.block_tables, lens, -1).shared_prefix() == (10, 1)
+    assert pk.block_table_upload(s.pool, w.block_tables, lens, -2).shared_prefix() == (10, 1)
     lens[1] = 16 * 10
-    assert pk.block_table_upload(s.pool, w.block_tables, lens, -1).shared_prefix() == (9, 1)
+    assert pk.block_table_upload(s.pool, w.block_tables, lens, -2).shared_prefix() == (9, 1)
 
 
 def test_shared_prefix_reduced_verify_config():
@@ -131,7 +135,7 @@ def test_shared_prefix_reduced_verify_config():
     at zero)."""
     log("shared prefix c5s")
     w = workloads.make("c5s")
-    s = Setup(w, partition_tokens=-1)
+    s = Setup(w, partition_tokens=-2)
     assert s.table.shared_prefix() == (16, 1)
     ref = s.oracle()
     a = s.run()
@@ -149,8 +153,8 @@ def test_shared_prefix_with_long_own_parts(kv, k):
     rng = np.random.Generator(np.random.PCG64(29304 + k))
     lens = 16 * 12 + np.array([3000, 4100, 2500, 3700]) + k
     w = workloads.build(f"prefix-long-{kv}", 29304 + k, rng, lens, num_q_heads=32, num_kv_heads=8, head_dim=128,
-                        kv_dtype=kv, k_rows=k, shared_prefix_tokens=16 * 12, materialize=True, partition_tokens=-1)
-    s = Setup(w, partition_tokens=-1)
+                        kv_dtype=kv, k_rows=k, shared_prefix_tokens=16 * 12, materialize=True, partition_tokens=-2)
+    s = Setup(w, partition_tokens=-2)
     assert s.table.shared_prefix() == (12, 1)
     got = s.run()
     assert_close(out_values(got), s.oracle(), kv, "long own parts")

@@ -56,3 +56,7 @@ def test_full_size_every_sequence(name, P):
     assert e_unit == err
     if name == "c4" and P == 512:
         assert table.info()["max_parts"] == 256   # 131072 / 512: the separate merge kernel runs
+    if name == "c5":
+        # the balanced upload keeps the shared-prefix plan (its cost estimate
+        # favours it at 128 sequences); fixed partitions do not
+        assert table.shared_prefix() == ((128, 4) if P == -1 else (0, 0))

@@ -68,8 +68,8 @@ def test_shared_prefix_scale_sign():
     lens = 16 * 20 + rng.integers(5, 60, size=5, endpoint=True)
     w = workloads.build("prefix-scale", 7130, rng, lens, num_q_heads=8, num_kv_heads=2, head_dim=64,
                         kv_dtype="fp8", k_rows=5, shared_prefix_tokens=16 * 20, materialize=True,
-                        partition_tokens=-1)
-    s = Setup(w, partition_tokens=-1)
+                        partition_tokens=-2)
+    s = Setup(w, partition_tokens=-2)
     assert s.table.shared_prefix()[0] == 20
     for f in FACTORS:
         scale = f * w.scale
