@@ -356,17 +356,20 @@ void prefix_chunking(int32_t prefix_blocks, int32_t* chunk_blocks, int32_t* chun
 }
 
 // Whether attending a shared prefix once for all rows should beat reading
-// it once per sequence, by a rough model of MI355X: a prefix-pass
-// work-group walks one chunk at about 2 us per block pair after about 5 us
-// of start-up (the pass's work-groups run side by side), while the plain
-// walk reads every sequence's reference to the prefix tiles at about
-// 6 TB/s.  (The model gives 37 against 90 us for 128 verify sequences
-// over a 2,048-token fp8 prefix, prefix plan; 69 against 11 us for four
-// bf16 sequences behind a 4,096-token prefix, plain plan.)
+// it once per sequence, by a rough model fitted on MI355X: a prefix-pass
+// work-group walks one chunk at about 1.5 us per block pair after about
+// 5 us of start-up (the pass's work-groups run side by side), while the
+// plain walk reads every sequence's reference to the prefix tiles at about
+// 12 TB/s (the repeated reads of shared tiles hit the L2 and the Infinity
+// Cache).  Measured, prefix plan against plain plan: 128 fp8 verify
+// sequences over a 2,048-token prefix 88 against 101 us, 64 bf16 decode
+// sequences 44 against 49 us (model: prefix plan); 32 bf16 sequences 36.5
+// against 34.9 us, 4 sequences behind a 4,096-token prefix 43 against
+// 19 us (model: plain plan).
 bool prefix_plan_pays(const pkv_pool* pool, int32_t num_seqs, int32_t prefix_blocks, int32_t chunk_blocks) {
-    const double pass_us = 5.0 + 2.0 * (chunk_blocks / 2.0);
+    const double pass_us = 5.0 + 1.5 * (chunk_blocks / 2.0);
     const double plain_us = static_cast<double>(num_seqs) * prefix_blocks * pool->desc.num_kv_heads * 2.0 *
-                            static_cast<double>(pool->tile_bytes) / 6.0e6;
+                            static_cast<double>(pool->tile_bytes) / 12.0e6;
     return pass_us < plain_us;
 }
 
