@@ -443,20 +443,74 @@ void attn_prefill_kernel(PrefillArgs a) {
             pf_k_regs<KVT, D>(ka, st, lane);
             pf_k_regs<KVT, D>(kb, st + 2 * Gm::TILE, lane);
         }
+        // Software pipeline over the wave's column tiles: the score MFMAs of
+        // tile c + 1 are issued in the same basic block as tile c's softmax,
+        // and the V products of the earlier tiles in the same block as the
+        // last tile's, so the matrix cores work while the VALU computes the
+        // probabilities.  The probabilities are taken against the current
+        // running max before the lazy-max check; the rare case that moves the
+        // max computes them again.
+        f32x4 sa[kPfNT], sb[kPfNT];
         u32x4 pop[kPfNT];
-#pragma unroll
-        for (int c = 0; c < kPfNT; ++c) {
+        u32x4 vop[D / 16];
+        auto qk = [&](int c) {
             // raw scores (int4: biased by kI4Bias times the query row's sum,
             // taken out in the exponent's offset and in the maximum)
-            f32x4 sa = scores<D>(ka, qr[c]);
-            f32x4 sb = scores<D>(kb, qr[c]);
+            sa[c] = scores<D>(ka, qr[c]);
+            sb[c] = scores<D>(kb, qr[c]);
+        };
+        auto probs = [&](int c) {
+            // (every score of an unmasked pair is finite, so the max is too)
+            const float muse = MASKED && m_run[c] == neg_inf() ? 0.f : m_run[c];
+            const float off = -(qbs[c] + muse);
+            float pa[4], pb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pa[i] = fast_exp2(__builtin_fmaf(sa[c][i], sscale, off));
+                pb[i] = fast_exp2(__builtin_fmaf(sb[c][i], sscale, off));
+            }
+            pop[c] = u32x4{pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3]), pack_bf16x2(pb[0], pb[1]),
+                           pack_bf16x2(pb[2], pb[3])};
+        };
+        auto pv = [&](int c) {
+            ol[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, pop[c]), ol[c], 0, 0, 0);
+#pragma unroll
+            for (int m = 0; m < D / 16; ++m)
+                o[c][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[m]),
+                                                                  __builtin_bit_cast(bf16x8, pop[c]), o[c][m], 0, 0, 0);
+        };
+        qk(0);
+#pragma unroll
+        for (int c = 0; c < kPfNT; ++c) {
+            if (c + 1 < kPfNT) {
+                qk(c + 1);
+            } else {
+                // V^T operands of the pair (the K operands are dead by now),
+                // then the products of every earlier tile
+                const uint8_t* va = st + Gm::TILE;
+                const uint8_t* vb = st + 3 * Gm::TILE;
+                PfV4<D> v4;
+                if constexpr (KVT == KV_INT4) v4.load(va, vb, lane);
+#pragma unroll
+                for (int m = 0; m < D / 16; ++m) {
+                    if constexpr (KVT == KV_INT4) vop[m] = v4.op(m);
+                    else vop[m] = pf_v_op<KVT, D>(va, vb, m, col, lg);
+                }
+#pragma unroll
+                for (int e = 0; e < kPfNT - 1; ++e) pv(e);
+            }
             if constexpr (MASKED) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    if (t0 + pf_token<KVT>(0, lg, i) >= lim[c]) sa[i] = neg_inf();
-                    if (t0 + pf_token<KVT>(1, lg, i) >= lim[c]) sb[i] = neg_inf();
+                    if (t0 + pf_token<KVT>(0, lg, i) >= lim[c]) sa[c][i] = neg_inf();
+                    if (t0 + pf_token<KVT>(1, lg, i) >= lim[c]) sb[c][i] = neg_inf();
                 }
             }
+            // (grouped in threes: four three-input maxima)
+            const float m1 = smax(smax(sa[c][0], sa[c][1]), sa[c][2]);
+            const float m2 = smax(smax(sa[c][3], sb[c][0]), sb[c][1]);
+            const float ml = smax(smax(smax(sb[c][2], sb[c][3]), m1), m2);
+            probs(c);
             // Running max in exp2 units, kept stale: it moves (and the
             // accumulators are rescaled) only when a score exceeds it by more
             // than kLazyMax, so probabilities stay <= 2^kLazyMax.  O and its
@@ -465,7 +519,6 @@ void attn_prefill_kernel(PrefillArgs a) {
             // (the reference plus kLazyMax, in raw units); only when some
             // lane exceeds it does the wave reduce the columns' maxima across
             // lanes and move the reference.
-            const float ml = smax(smax(smax(sa[0], sa[1]), smax(sa[2], sa[3])), smax(smax(sb[0], sb[1]), smax(sb[2], sb[3])));
             if (__ballot(ml > thr[c])) {
                 const float mx = (max_over_rows(ml) - qbias[c]) * sscale;
                 if (mx > m_run[c] + kLazyMax) {
@@ -476,37 +529,10 @@ void attn_prefill_kernel(PrefillArgs a) {
                     for (int m = 0; m < D / 16; ++m) o[c][m] *= alpha;
                 }
                 thr[c] = m_run[c] == neg_inf() ? neg_inf() : (m_run[c] + kLazyMax) * inv_sscale + qbias[c];
+                probs(c);
             }
-            // (every score of an unmasked pair is finite, so the max is too)
-            const float muse = MASKED && m_run[c] == neg_inf() ? 0.f : m_run[c];
-            const float off = -(qbs[c] + muse);
-            float pa[4], pb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pa[i] = fast_exp2(__builtin_fmaf(sa[i], sscale, off));
-                pb[i] = fast_exp2(__builtin_fmaf(sb[i], sscale, off));
-            }
-            pop[c] = u32x4{pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3]), pack_bf16x2(pb[0], pb[1]),
-                           pack_bf16x2(pb[2], pb[3])};
         }
-#pragma unroll
-        for (int c = 0; c < kPfNT; ++c)
-            ol[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, pop[c]), ol[c], 0, 0, 0);
-        const uint8_t* va = st + Gm::TILE;
-        const uint8_t* vb = st + 3 * Gm::TILE;
-        PfV4<D> v4;
-        if constexpr (KVT == KV_INT4) v4.load(va, vb, lane);
-#pragma unroll
-        for (int m = 0; m < D / 16; ++m) {
-            u32x4 vop;
-            if constexpr (KVT == KV_INT4) vop = v4.op(m);
-            else vop = pf_v_op<KVT, D>(va, vb, m, col, lg);
-            const bf16x8 av = __builtin_bit_cast(bf16x8, vop);
-#pragma unroll
-            for (int c = 0; c < kPfNT; ++c)
-                o[c][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, pop[c]), o[c][m],
-                                                                  0, 0, 0);
-        }
+        pv(kPfNT - 1);
     };
     // Pair p needs the mask iff 32 p + 32 > lim_lo; the waves' splits differ,
     // their barrier counts (one per pair) do not.
