@@ -293,13 +293,7 @@ def main():
                     else "attn_partition_kernel + attn_merge_kernel")
     prefix_blocks, prefix_chunks = table.shared_prefix()
     shared_prefix = prefix_blocks > 0 and int(w.seq_lens.min()) - kq >= 16 * prefix_blocks
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
-    if os.path.exists(tpath):
-        with open(tpath) as f:
-            tr = json.load(f)
-        if tr.get("kernel_source_digest") == _kernel_digest():
-            traffic = tr.get("hbm_bytes_per_launch")
+    traffic = _recorded_traffic(args.workload)
 
     result = {
         "metric": METRIC,
@@ -366,13 +360,8 @@ def main():
             "parts": {"prefix_pass_flops": prefix_flops, "prefix_pass_us_at_mfma_peak": round(t_mfma, 2),
                       "own_block_bytes": own_bytes, "own_blocks_us_at_hbm_peak": round(t_hbm, 2)}}
     if args.calibrate_copy > 0:
-        n = args.calibrate_copy << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        result["calibrate_copy_bytes"] = n
+        _calibration_copies(args.calibrate_copy << 20, dev)
+        result["calibrate_copy_bytes"] = args.calibrate_copy << 20
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
         image = pools[0].storage.cpu().numpy()
@@ -475,8 +464,11 @@ def run_prefill(args):
                      "achieved": round(flops / (attn_avg * 1e-3) / 1e12, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / (attn_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": _recorded_traffic("pf")},
     }
+    if args.calibrate_copy > 0:
+        _calibration_copies(args.calibrate_copy << 20, dev)
+        result["calibrate_copy_bytes"] = args.calibrate_copy << 20
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = prefill_cpu_baseline(w, pools[0].storage.cpu().numpy(), args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -565,6 +557,29 @@ def run_speculative(args):
                                   "sample": f"float64 numpy oracle on the first {done} of {w.batch} sequences, "
                                             f"{dt:.1f} s, one thread"}
     print(json.dumps(result), flush=True)
+
+
+def _calibration_copies(n, dev):
+    """Three device-to-device copies of n bytes: a profiler's FETCH_SIZE and
+    WRITE_SIZE for them give the counters' scale against known bytes."""
+    import torch
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _recorded_traffic(workload):
+    """HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE record in
+    profiles/traffic_<workload>.json, or None when there is none or it was
+    taken on other kernel sources than these."""
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(tpath):
+        return None
+    with open(tpath) as f:
+        tr = json.load(f)
+    return tr.get("hbm_bytes_per_launch") if tr.get("kernel_source_digest") == _kernel_digest() else None
 
 
 def _kernel_digest():

@@ -341,19 +341,21 @@ __device__ __forceinline__ void attend_item(const AttnArgs& a, const int unit, c
             const int t1 = min(hi, blk * kBlock + kBlock);
             for (int t = t0; t < t1; ++t) tr.put_token(t - blk * kBlock, stage + (t - lo) * STOK, lane);
         }
-        // Scaled scores (int4, int8: still biased by qbs).  The products'
-        // results pass through mfma_result_pad before any other use.
+        // Scaled scores (int4, int8: still biased by qbs).  The scaling is
+        // the products' only reader and is pinned to their basic block (see
+        // pin_after_mfma_reads).
         f32x4 s[NT];
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
             if constexpr (KVT == KV_INT8) s[c] = scores_i8<D>(tr, qr[c]);
             else s[c] = scores<D>(tr, qr[c]);
         }
-        mfma_result_pad<NT>(s);
 #pragma unroll
-        for (int c = 0; c < NT; ++c)
+        for (int c = 0; c < NT; ++c) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) s[c][i] *= sscale;
+            pin_after_mfma_reads(s[c]);
+        }
         const int tok0 = blk * kBlock + 4 * lg;
         if (blk * kBlock + kBlock > mask_from) {
 #pragma unroll

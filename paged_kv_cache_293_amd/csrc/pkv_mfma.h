@@ -37,17 +37,13 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 
 // A vector instruction may read a matrix-core result only some cycles after
 // the product issues (the wait states grow with the product's passes).  The
-// compiler pads such reads within a basic block, but a read placed just past
-// a branch was found unpadded on the branch-taken path (garbage scores in
-// the decode kernel).  Score tiles therefore pass through this explicit pad,
-// 12 wait states, before any other use.
-template <int NT>
-__device__ __forceinline__ void mfma_result_pad(f32x4 (&s)[NT]) {
-    static_assert(NT == 1 || NT == 2 || NT == 4, "one, two or four score tiles");
-    if constexpr (NT == 1) asm volatile("s_nop 7\n\ts_nop 3" : "+v"(s[0]));
-    else if constexpr (NT == 2) asm volatile("s_nop 7\n\ts_nop 3" : "+v"(s[0]), "+v"(s[1]));
-    else asm volatile("s_nop 7\n\ts_nop 3" : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3]));
-}
+// compiler pads such reads within a basic block, but a read it moved past a
+// branch was found unpadded on the branch-taken path (garbage scores in the
+// decode kernel).  The decode kernel therefore reads its score tiles in one
+// place, the scaling right after the products, and this empty statement,
+// which takes the scaled values as its operands, keeps that scaling in the
+// products' basic block: the compiler cannot move the reads past it.
+__device__ __forceinline__ void pin_after_mfma_reads(f32x4& s) { asm volatile("" : "+v"(s)); }
 
 // Maximum of scores (finite, or -inf where masked): the IEEE maximum, which
 // passes NaN through and so needs no quieting of its operands (fmaxf costs

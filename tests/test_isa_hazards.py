@@ -4,7 +4,8 @@ A vector (VALU) instruction may read a register written by a matrix-core
 (MFMA) instruction only after some wait states.  The compiler pads such
 reads inside a basic block; a read placed just past a branch was found
 unpadded on the branch-taken path, and the kernel then read stale score
-values.  The kernels pad their score tiles explicitly (mfma_result_pad).
+values.  The decode kernel pins the scaling of its score tiles, their only
+reader, to the products' basic block (pin_after_mfma_reads).
 
 This test disassembles the gfx950 code object of the built library (the
 library built here, with the ROCm tools of this image) and follows every
