@@ -1,9 +1,8 @@
 """GPU: the sign and the zero of the softmax scale factor.
 
-The kernels scale scores inside the exponent and take a row's largest scaled
-score from its largest raw score, which holds only for a positive factor; a
-negative factor has its sign moved into the query, a zero factor is replaced
-by the smallest normal float.  Checked against the float64 oracle (which
+The decode kernel scales its scores before taking their maximum; the prefill
+kernel holds the query multiplied by the factor, so a factor of either sign,
+or zero, reaches its scores directly.  Checked against the float64 oracle (which
 applies the factor as given): a zero factor (every visible position weighs
 the same: the mean of the visible V rows), negative factors, and a positive
 one for contrast, for decode and verify rows (causal masks inside the last
