@@ -406,10 +406,7 @@ pkv_status paged_attention_append(const pkv_pool* pool, int32_t layer, const pkv
  *   h = g / (num_q_heads / num_kv_heads).
  * It is the computation of paged_attention_verify with C rows, for any C:
  * the kernel keeps each work-group's 192 query rows resident and streams the
- * visible K/V blocks through LDS, bound by the matrix cores.  It holds the
- * queries multiplied by scale (and by the pool's per-head K scale) and
- * rounded to bfloat16, one rounding of relative size 2^-9 per query element
- * beyond the decode and verify calls, which scale the float32 scores.
+ * visible K/V blocks through LDS, bound by the matrix cores.
  *   dev_q    [num_seqs][C][num_q_heads][head_dim] bfloat16.
  *   dev_out  [num_seqs][C][num_q_heads][head_dim], out_dtype PKV_BF16 or PKV_F32.
  *   Pools: PKV_BF16, PKV_FP8_E4M3, PKV_INT8 or PKV_INT4 (PKV_F32 pools:

@@ -384,21 +384,17 @@ template <int D> struct TileRegs<KV_F32, D> {
 // dims matching the K chunk each lane group holds.
 template <int KVT, int D> struct QRegs;
 
-// bf16 values times k, rounded to bf16 (nearest even).
-__device__ __forceinline__ bf16x8 scale_bf16x8(const bf16x8& v, float k) {
-    const u32x4 w = __builtin_bit_cast(u32x4, v);
-    u32x4 r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        r[j] = pack_bf16x2(__uint_as_float(w[j] << 16) * k, __uint_as_float(w[j] & 0xffff0000u) * k);
-    return __builtin_bit_cast(bf16x8, r);
+// Sign flip of every 16-bit value in a 16-byte operand register.
+template <class V>
+__device__ __forceinline__ V flip16(const V& v) {
+    return __builtin_bit_cast(V, __builtin_bit_cast(u32x4, v) ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u});
 }
 
 template <int D> struct QRegs<KV_BF16, D> {
     bf16x8 q[D / 32];   // step s: dims (4s + lane/16) * 8 .. +8
-    __device__ __forceinline__ void scale(float k) {
+    __device__ __forceinline__ void negate() {
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) q[s] = scale_bf16x8(q[s], k);
+        for (int s = 0; s < D / 32; ++s) q[s] = flip16(q[s]);
     }
     __device__ __forceinline__ void load(const uint16_t* row, bool valid, int lane) {
 #pragma unroll
@@ -412,9 +408,9 @@ template <int D> struct QRegs<KV_BF16, D> {
 
 template <int D> struct QRegs1B {
     bf16x8 q[D / 32];   // step 2r + hh: dims (4r + lane/16) * 16 + 8 hh .. +8
-    __device__ __forceinline__ void scale(float k) {
+    __device__ __forceinline__ void negate() {
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) q[s] = scale_bf16x8(q[s], k);
+        for (int s = 0; s < D / 32; ++s) q[s] = flip16(q[s]);
     }
     __device__ __forceinline__ void load(const uint16_t* row, bool valid, int lane) {
 #pragma unroll
@@ -447,6 +443,10 @@ template <int D> struct QRegs<KV_INT4, D> : QRegs<KV_BF16, D> {
 
 template <int D> struct QRegs<KV_F32, D> {
     f32x4 q[D / 16];    // r: dims (4r + lane/16) * 4 .. +4, one MFMA per element
+    __device__ __forceinline__ void negate() {
+#pragma unroll
+        for (int r = 0; r < D / 16; ++r) q[r] = -q[r];
+    }
     __device__ __forceinline__ void load(const float* row, bool valid, int lane) {
 #pragma unroll
         for (int r = 0; r < D / 16; ++r)
@@ -455,12 +455,10 @@ template <int D> struct QRegs<KV_F32, D> {
     }
 };
 
-// S^T tile (tokens x rows) of one block for one column tile, added to acc
-// (the scores functions take the accumulator's initial value: zero, or a
-// column's offset broadcast over its four entries).
+// S^T tile (tokens x rows) of one block for one column tile.
 template <int D>
-__device__ __forceinline__ f32x4 scores(const TileRegs<KV_BF16, D>& t, const QRegs<KV_BF16, D>& q,
-                                        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}) {
+__device__ __forceinline__ f32x4 scores(const TileRegs<KV_BF16, D>& t, const QRegs<KV_BF16, D>& q) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[s]), q.q[s], acc, 0, 0, 0);
@@ -468,7 +466,8 @@ __device__ __forceinline__ f32x4 scores(const TileRegs<KV_BF16, D>& t, const QRe
 }
 
 template <int KVT, int D>
-__device__ __forceinline__ f32x4 scores_1b(const TileRegs<KVT, D>& t, const QRegs<KVT, D>& q, f32x4 acc) {
+__device__ __forceinline__ f32x4 scores_1b(const TileRegs<KVT, D>& t, const QRegs<KVT, D>& q) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < D / 64; ++r) {
         const u32x4 w = t.k[r];
@@ -487,15 +486,13 @@ __device__ __forceinline__ f32x4 scores_1b(const TileRegs<KVT, D>& t, const QReg
 }
 
 template <int D>
-__device__ __forceinline__ f32x4 scores(const TileRegs<KV_FP8, D>& t, const QRegs<KV_FP8, D>& q,
-                                        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}) {
-    return scores_1b<KV_FP8, D>(t, q, acc);
+__device__ __forceinline__ f32x4 scores(const TileRegs<KV_FP8, D>& t, const QRegs<KV_FP8, D>& q) {
+    return scores_1b<KV_FP8, D>(t, q);
 }
 
 template <int D>
-__device__ __forceinline__ f32x4 scores(const TileRegs<KV_INT8, D>& t, const QRegs<KV_INT8, D>& q,
-                                        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}) {
-    return scores_1b<KV_INT8, D>(t, q, acc);
+__device__ __forceinline__ f32x4 scores(const TileRegs<KV_INT8, D>& t, const QRegs<KV_INT8, D>& q) {
+    return scores_1b<KV_INT8, D>(t, q);
 }
 
 // Decode-kernel int8 query operand: the bf16 query times 2^-8 as fp16 (in
@@ -506,6 +503,10 @@ __device__ __forceinline__ f32x4 scores(const TileRegs<KV_INT8, D>& t, const QRe
 constexpr float kI8QScale = 1.f / 256.f;
 template <int D> struct QRegsI8 {
     f16x8 q[D / 32];
+    __device__ __forceinline__ void negate() {
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) q[s] = flip16(q[s]);
+    }
     __device__ __forceinline__ void load(const uint16_t* row, bool valid, int lane) {
 #pragma unroll
         for (int st = 0; st < D / 32; ++st) {
@@ -544,8 +545,8 @@ __device__ __forceinline__ f32x4 scores_i8(const TileRegs<KV_INT8, D>& t, const 
 
 // Biased scores: the caller subtracts kI4Bias times the query row's sum.
 template <int D>
-__device__ __forceinline__ f32x4 scores(const TileRegs<KV_INT4, D>& t, const QRegs<KV_INT4, D>& q,
-                                        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}) {
+__device__ __forceinline__ f32x4 scores(const TileRegs<KV_INT4, D>& t, const QRegs<KV_INT4, D>& q) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
         unsigned ev, od;

@@ -322,11 +322,13 @@ void attn_prefill_kernel(PrefillArgs a) {
         sscale *= a.k_scale[a.layer * H + h];
         vscale = a.v_scale[a.layer * H + h];
     }
-    // The queries are held scaled (times the score factor, in exp2 units,
-    // rounded to bf16), so the score MFMAs produce scaled scores; each
-    // column's offset enters as the MFMA accumulator's initial value, and a
-    // probability is one exp2 of an MFMA result.  A factor of any sign or
-    // zero needs no special case.
+    // Scores are scaled inside the exponent and a row's maximum scaled score
+    // comes from its maximum raw score, which needs a positive factor: a
+    // negative one moves its sign into the query, a zero one becomes the
+    // smallest normal float (scaled scores round to 0 against the offset,
+    // masked ones still give -inf).
+    const bool qneg = sscale < 0.f;
+    sscale = sscale == 0.f ? 1.17549435e-38f : fabsf(sscale);
 
     QRegs<KVT, D> qr[kPfNT];
     int lim[kPfNT];
@@ -339,32 +341,29 @@ void attn_prefill_kernel(PrefillArgs a) {
         const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) +
             ((static_cast<int64_t>(q0) + j) * a.num_q_heads + h * G + g) * D;
         qr[c].load(qrow, valid, lane);
-        qr[c].scale(sscale);
+        if (qneg) qr[c].negate();
         lim[c] = CASCADE ? n : (valid ? first + j + 1 : 0);
     }
-    // int4: kI4Bias times each (scaled) query row's sum, the bias of its
-    // scores
-    float qbs[kPfNT];
+    // int4: kI4Bias times each query row's sum (the bias of its scores)
+    float qbias[kPfNT], qbs[kPfNT];   // qbs: the bias scaled
 #pragma unroll
-    for (int c = 0; c < kPfNT; ++c) qbs[c] = KVT == KV_INT4 ? kI4Bias * query_row_sum<D>(qr[c])[0] : 0.f;
+    for (int c = 0; c < kPfNT; ++c) {
+        qbias[c] = KVT == KV_INT4 ? kI4Bias * query_row_sum<D>(qr[c])[0] : 0.f;
+        qbs[c] = qbias[c] * sscale;
+    }
 
     // o: unnormalised output per (column tile, 16 dims); ol: the row sums of
     // the bf16 probabilities, accumulated by the matrix cores against a tile
     // of ones (every entry of a column holds that row's sum).
-    // m_run: a column's reference (running max, kept stale; -inf until its
-    // first visible score); the scores come out of the MFMAs relative to it
-    // (to 0 while it is -inf): coff = -(qbs + reference), broadcast over
-    // the four entries of the accumulator's initial value.
     f32x4 o[kPfNT][D / 16];
     f32x4 ol[kPfNT];
     float m_run[kPfNT];
-    float thr[kPfNT];   // relative score above which a column's reference must move
-    float coff[kPfNT];
+    float thr[kPfNT];   // raw score above which a column's reference must move
+    const float inv_sscale = 1.f / sscale;
 #pragma unroll
     for (int c = 0; c < kPfNT; ++c) {
         m_run[c] = neg_inf();
         thr[c] = neg_inf();
-        coff[c] = -qbs[c];
         ol[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < D / 16; ++m) o[c][m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -455,18 +454,20 @@ void attn_prefill_kernel(PrefillArgs a) {
         u32x4 pop[kPfNT];
         u32x4 vop[D / 16];
         auto qk = [&](int c) {
-            // scaled scores relative to the column's reference (int4: the
-            // bias, kI4Bias times the query row's sum, cancelled by coff)
-            const f32x4 ci = {coff[c], coff[c], coff[c], coff[c]};
-            sa[c] = scores<D>(ka, qr[c], ci);
-            sb[c] = scores<D>(kb, qr[c], ci);
+            // raw scores (int4: biased by kI4Bias times the query row's sum,
+            // taken out in the exponent's offset and in the maximum)
+            sa[c] = scores<D>(ka, qr[c]);
+            sb[c] = scores<D>(kb, qr[c]);
         };
         auto probs = [&](int c) {
+            // (every score of an unmasked pair is finite, so the max is too)
+            const float muse = MASKED && m_run[c] == neg_inf() ? 0.f : m_run[c];
+            const float off = -(qbs[c] + muse);
             float pa[4], pb[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pa[i] = fast_exp2(sa[c][i]);
-                pb[i] = fast_exp2(sb[c][i]);
+                pa[i] = fast_exp2(__builtin_fmaf(sa[c][i], sscale, off));
+                pb[i] = fast_exp2(__builtin_fmaf(sb[c][i], sscale, off));
             }
             pop[c] = u32x4{pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3]), pack_bf16x2(pb[0], pb[1]),
                            pack_bf16x2(pb[2], pb[3])};
@@ -514,26 +515,20 @@ void attn_prefill_kernel(PrefillArgs a) {
             // accumulators are rescaled) only when a score exceeds it by more
             // than kLazyMax, so probabilities stay <= 2^kLazyMax.  O and its
             // row sum share the same max, so O / sum is unchanged.  Each lane
-            // compares its own 8 relative scores with the column's threshold
-            // (kLazyMax, -inf before the first visible score); only when some
+            // compares its own 8 raw scores with the column's threshold
+            // (the reference plus kLazyMax, in raw units); only when some
             // lane exceeds it does the wave reduce the columns' maxima across
-            // lanes, move the reference, shift the tile's scores to it and
-            // take the probabilities again.
+            // lanes and move the reference.
             if (__ballot(ml > thr[c])) {
-                const float base = m_run[c] == neg_inf() ? 0.f : m_run[c];
-                const float mx = max_over_rows(ml) + base;
+                const float mx = (max_over_rows(ml) - qbias[c]) * sscale;
                 if (mx > m_run[c] + kLazyMax) {
                     const float alpha = fast_exp2(m_run[c] - mx);
                     m_run[c] = mx;
                     ol[c] *= alpha;
 #pragma unroll
                     for (int m = 0; m < D / 16; ++m) o[c][m] *= alpha;
-                    const float d = mx - base;
-                    sa[c] -= d;
-                    sb[c] -= d;
-                    coff[c] = -(qbs[c] + mx);
                 }
-                thr[c] = m_run[c] == neg_inf() ? neg_inf() : kLazyMax;
+                thr[c] = m_run[c] == neg_inf() ? neg_inf() : (m_run[c] + kLazyMax) * inv_sscale + qbias[c];
                 probs(c);
             }
         }

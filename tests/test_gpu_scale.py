@@ -1,8 +1,9 @@
 """GPU: the sign and the zero of the softmax scale factor.
 
-The decode kernel scales its scores before taking their maximum; the prefill
-kernel holds the query multiplied by the factor, so a factor of either sign,
-or zero, reaches its scores directly.  Checked against the float64 oracle (which
+The kernels scale scores inside the exponent and take a row's largest scaled
+score from its largest raw score, which holds only for a positive factor; a
+negative factor has its sign moved into the query, a zero factor is replaced
+by the smallest normal float.  Checked against the float64 oracle (which
 applies the factor as given): a zero factor (every visible position weighs
 the same: the mean of the visible V rows), negative factors, and a positive
 one for contrast, for decode and verify rows (causal masks inside the last
@@ -76,3 +77,30 @@ def test_shared_prefix_scale_sign():
         got = out_values(s.run(scale=scale))
         assert np.isfinite(got).all()
         assert_close(got, s.oracle(scale=scale), "fp8", f"shared prefix scale {scale:+.4f}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8", "int4"])
+def test_prefill_large_scale_factors(kv):
+    """Peaky softmax: 2, 4 and 8 times 1/sqrt(d).  The scale is applied to
+    float32 scores, so the error does not grow with the scores' size (a
+    query rounded to bf16 after scaling gave 2e-2 at 4x and 4e-2 at 8x)."""
+    w = workloads.custom(7125, [60, 97, 300], num_q_heads=8, num_kv_heads=2, head_dim=128, kv_dtype=kv,
+                         k_rows=60, partition_tokens=0)
+    s = Setup(w)
+    for f in [2.0, 4.0, 8.0]:
+        scale = f * w.scale
+        got = out_values(s.run_prefill(scale=scale, out_dtype="f32"))
+        err = assert_close(got, s.oracle_prefill(scale=scale), kv, f"prefill {kv} scale x{f}")
+        log(f"prefill {kv} x{f}: max abs err {err:.3e}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int4"])
+def test_verify_large_scale_factors(kv):
+    w = workloads.custom(7126, [37, 200, 517], num_q_heads=8, num_kv_heads=2, head_dim=128, kv_dtype=kv,
+                         k_rows=5, partition_tokens=64)
+    s = Setup(w)
+    for f in [4.0, 8.0]:
+        scale = f * w.scale
+        got = out_values(s.run(scale=scale))
+        err = assert_close(got, s.oracle(scale=scale), kv, f"verify {kv} scale x{f}")
+        log(f"verify {kv} x{f}: max abs err {err:.3e}")
