@@ -16,8 +16,12 @@
 // tile of 192 query rows); rows are ordered (token, head of the group), so
 // the G heads of one token sit side by side.  Each wave owns 48 rows as three
 // 16-row column tiles, with their queries resident in registers; the rest of
-// its state fits in 256 VGPRs, so two work-groups share a CU and their waves
-// interleave softmax (VALU) and matrix work on each SIMD.  The K/V of
+// its state fits in 256 VGPRs, so two work-groups share a CU and each SIMD
+// has a second wave to issue while one waits (on gfx950 a SIMD's fp32 VALU
+// and matrix instructions do not run side by side, so softmax time adds to
+// matrix time; within a pair the next column tile's score MFMAs share a
+// basic block with the current tile's softmax, so neither waits on the
+// other's branch).  The K/V of
 // the visible blocks stream through a four-stage LDS ring, two blocks (a
 // "pair") per stage, copied straight from the pool into LDS by 16-byte
 // buffer loads with the LDS as destination (no register staging; one buffer
