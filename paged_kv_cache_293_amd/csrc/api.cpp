@@ -128,7 +128,8 @@ int device_cu_count() {
 }
 
 // Blocks per unit for the balanced plan: the smallest unit size whose plan has
-// at most wgs_per_cu work-groups per CU over all KV heads, kept within
+// at most wgs_per_cu work-groups per CU over all KV heads (plan_wgs_per_cu),
+// kept within
 // [kAutoMinBlocks, kAutoMaxBlocks].
 int32_t auto_unit_blocks(const std::vector<int32_t>& nblk, int32_t num_kv_heads, int32_t wgs_per_cu) {
     const int64_t slots = static_cast<int64_t>(device_cu_count()) * wgs_per_cu;
@@ -203,13 +204,17 @@ std::vector<int32_t> place_on_cus(size_t num_units, int32_t num_kv_heads, int32_
 // balanced, every sequence cut into near-equal parts of about
 // auto_unit_blocks() blocks (no part under 2 * kAutoMinItemBlocks when the
 // batch alone fills the device).  Units are ordered longest first, or placed
-// by place_on_cus() when the grid has a work-group per item.
+// by place_on_cus() when the grid has a work-group per item.  wgs_per_cu: the
+// work-groups per CU the balanced units are sized for (plan_wgs_per_cu);
+// resident_per_cu: those the kernel keeps resident (decode_wgs_per_cu), which
+// decide whether every item has its own work-group.
 // Shared-prefix plans: the units cover blocks skip .. of every sequence (the
 // first `skip` blocks are attended by the prefix pass), and every sequence
 // carries `lead` more partial results (the prefix chunks', in its first
 // slots), merged with its own.
 bool build_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, int32_t partition_tokens,
-                int32_t num_kv_heads, int32_t wgs_per_cu, Plan* P, int32_t skip = 0, int32_t lead = 0) {
+                int32_t num_kv_heads, int32_t wgs_per_cu, int32_t resident_per_cu, Plan* P, int32_t skip = 0,
+                int32_t lead = 0) {
     if (num_seqs < 1 || max_blocks < 1) return false;
     if (partition_tokens < -1 || (partition_tokens > 0 && partition_tokens % PKV_BLOCK_SIZE)) return false;
     std::vector<int32_t> nblk(num_seqs);
@@ -264,7 +269,7 @@ bool build_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, i
     }
     std::stable_sort(us.begin(), us.end(), [](const U& x, const U& y) { return x.nb > y.nb; });
     const std::vector<int32_t> order =
-        place_on_cus(us.size(), num_kv_heads, wgs_per_cu, [&](size_t i) { return us[i].nb; });
+        place_on_cus(us.size(), num_kv_heads, resident_per_cu, [&](size_t i) { return us[i].nb; });
     {
         std::vector<U> placed(us.size());
         for (size_t pos = 0; pos < us.size(); ++pos) placed[pos] = us[order[pos]];
@@ -341,8 +346,10 @@ int32_t max_prefix_blocks(const pkv_pool* pool, const int32_t* seq_lens, int32_t
 // the device, near-equal parts when few long sequences do not), with
 // prefix_chunks leading partials per sequence.
 bool build_cascade_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks, int32_t num_kv_heads,
-                        int32_t wgs_per_cu, int32_t prefix_blocks, int32_t prefix_chunks, Plan* C) {
-    return build_plan(seq_lens, num_seqs, max_blocks, -1, num_kv_heads, wgs_per_cu, C, prefix_blocks, prefix_chunks);
+                        int32_t wgs_per_cu, int32_t resident_per_cu, int32_t prefix_blocks, int32_t prefix_chunks,
+                        Plan* C) {
+    return build_plan(seq_lens, num_seqs, max_blocks, -1, num_kv_heads, wgs_per_cu, resident_per_cu, C, prefix_blocks,
+                      prefix_chunks);
 }
 
 // Prefix chunks: at most kCascadeMaxChunks, each of at least
@@ -443,9 +450,10 @@ size_t block_table_device_bytes(const pkv_pool* pool, const int32_t* host_seq_le
         const bool balanced = partition_tokens == -1 || partition_tokens == kForcePrefixPlan;
         if (partition_tokens == kForcePrefixPlan) partition_tokens = -1;
         Plan P;
-        const int32_t wpc = pkv::decode_wgs_per_cu(pool->desc.kv_dtype, pool->desc.head_dim);
+        const int32_t wpc = pkv::plan_wgs_per_cu(pool->desc.kv_dtype, pool->desc.head_dim);
+        const int32_t rpc = pkv::decode_wgs_per_cu(pool->desc.kv_dtype, pool->desc.head_dim);
         if (!build_plan(host_seq_lens, num_seqs, max_blocks_per_seq, partition_tokens, pool->desc.num_kv_heads, wpc,
-                        &P))
+                        rpc, &P))
             return 0;
         // Room for a shared-prefix plan if the tables turn out to share one,
         // sized for the smallest prefix (the most own blocks); an upload whose
@@ -453,7 +461,7 @@ size_t block_table_device_bytes(const pkv_pool* pool, const int32_t* host_seq_le
         Plan C;
         const bool maybe = balanced && max_prefix_blocks(pool, host_seq_lens, num_seqs) > 0 &&
                            build_cascade_plan(host_seq_lens, num_seqs, max_blocks_per_seq, pool->desc.num_kv_heads,
-                                              wpc, pkv::kCascadeMinBlocks, 1, &C);
+                                              wpc, rpc, pkv::kCascadeMinBlocks, 1, &C);
         return table_layout(num_seqs, max_blocks_per_seq, pool->desc.num_kv_heads, P, maybe ? &C : nullptr).total;
     } catch (...) {
         return 0;
@@ -492,8 +500,9 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
             }
         }
         Plan P;
-        const int32_t wpc = pkv::decode_wgs_per_cu(pool->desc.kv_dtype, pool->desc.head_dim);
-        if (!build_plan(host_seq_lens, num_seqs, max_blocks_per_seq, partition_tokens, hkv, wpc, &P))
+        const int32_t wpc = pkv::plan_wgs_per_cu(pool->desc.kv_dtype, pool->desc.head_dim);
+        const int32_t rpc = pkv::decode_wgs_per_cu(pool->desc.kv_dtype, pool->desc.head_dim);
+        if (!build_plan(host_seq_lens, num_seqs, max_blocks_per_seq, partition_tokens, hkv, wpc, rpc, &P))
             return PKV_ERR_INVALID;
         // Shared prefix (balanced plans only: fixed partitions are kept as
         // asked): the longest run of leading physical blocks that every
@@ -513,7 +522,8 @@ pkv_status block_table_upload(const pkv_pool* pool, const int32_t* host_block_ta
         int32_t chunk_blocks = 0, chunks = 0;
         if (prefix) prefix_chunking(prefix, &chunk_blocks, &chunks);
         if (prefix && !force_prefix && !prefix_plan_pays(pool, num_seqs, prefix, chunk_blocks)) prefix = 0;
-        if (prefix && !build_cascade_plan(host_seq_lens, num_seqs, max_blocks_per_seq, hkv, wpc, prefix, chunks, &C))
+        if (prefix && !build_cascade_plan(host_seq_lens, num_seqs, max_blocks_per_seq, hkv, wpc, rpc, prefix, chunks,
+                                          &C))
             return PKV_ERR_INVALID;
         TableLayout L = table_layout(num_seqs, max_blocks_per_seq, hkv, P, prefix ? &C : nullptr);
         if (prefix && dev_buffer_bytes < L.total) {

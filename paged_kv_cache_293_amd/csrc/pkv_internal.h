@@ -78,6 +78,12 @@ constexpr int decode_buffers(int kv, int d, int nt) {
          : (kv == 2 || kv == 3) ? PKV_BUFS_1B : 3;
 }
 constexpr int decode_wgs_per_cu(int kv, int d) { return kv == 0 ? 1 : (d == 128 ? (kv == 4 ? 3 : 2) : 3); }
+// Work-groups per CU the balanced plan sizes its units for.  The int4
+// instance runs three per CU to hide latency, but cutting sequences to give
+// that third work-group an item costs more (partials and merges) than it
+// balances: on the Llama-3-8B decode batch, whole sequences (64 units) ran
+// 31.4-32.1 us against 33.4-34.5 us for 96 units, four runs each.
+constexpr int plan_wgs_per_cu(int kv, int d) { return kv == 4 && d == 128 ? 2 : decode_wgs_per_cu(kv, d); }
 constexpr int kAutoItemsPerWg = PKV_AUTO_ITEMS_PER_WG;
 constexpr int kAutoMinItemBlocks = PKV_AUTO_MIN_ITEM_BLOCKS;
 constexpr int kAutoMinBlocks = 8;
