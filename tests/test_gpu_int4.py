@@ -150,4 +150,17 @@ def test_int4_prefill(Hq, Hkv, d, C, lens):
     log(f"  max abs err {err:.3e}")
 
 
+@pytest.mark.parametrize("k,Hq,Hkv,d,part", [(5, 8, 1, 128, 0), (2, 4, 4, 64, -1), (4, 64, 8, 128, -1)])
+def test_int4_verify_mqa_mha(k, Hq, Hkv, d, part):
+    """int4 verify rows for MQA, MHA and G = 8 (64-row tiles), unsplit and
+    under the balanced plan."""
+    log(f"int4 verify k={k} {Hq}/{Hkv} d{d} partitions {part}")
+    lens = [k, k + 1, 16, 40, 300, 2000]
+    w = workloads.custom(4700 + k + d, lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, kv_dtype="int4",
+                         k_rows=k, partition_tokens=part)
+    s = Setup(w, partition_tokens=part)
+    err = assert_close(out_values(s.run()), s.oracle(), "int4", f"int4 verify k={k} {Hq}/{Hkv}")
+    log(f"  max abs err {err:.3e}")
+
+
 # The full-size c2i4 workload is checked on every sequence in test_gpu_fullsize.py.

@@ -120,3 +120,16 @@ def test_int8_prefill_and_fused_append():
 
 
 # The full-size c2i8 workload is checked on every sequence in test_gpu_fullsize.py.
+
+
+@pytest.mark.parametrize("k,Hq,Hkv,d,part", [(3, 16, 2, 64, 32), (9, 32, 8, 128, 32), (5, 8, 1, 128, 0), (2, 4, 4, 64, -1)])
+def test_int8_verify_rows(k, Hq, Hkv, d, part):
+    """Verify rows (causal among the k rows) over int8 pools: GQA, MQA and
+    MHA, split and unsplit sequences, both head dims."""
+    log(f"int8 verify k={k} {Hq}/{Hkv} d{d} partitions {part}")
+    lens = [k, k + 1, 16, 40, 300]
+    w = workloads.custom(4600 + k + d, lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, kv_dtype="int8",
+                         k_rows=k, partition_tokens=part)
+    s = Setup(w, partition_tokens=part)
+    err = assert_close(out_values(s.run()), s.oracle(), "int8", f"int8 verify k={k}")
+    log(f"  max abs err {err:.3e}")
